@@ -1,0 +1,398 @@
+/*
+ * qsa_oracle.c -- FP64 CPU reference for route-set grouped-query attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this file's library. It shares no
+ * code, header, table or helper with the HIP library it checks.
+ *
+ * What it computes is the plain definition of the method, written out with
+ * loops, in double precision:
+ *
+ *  - Route set. For query row (b, i) the set R(b, i) holds every route value r
+ *    with 0 <= r < Skv, tested on the full integer width; duplicates count once
+ *    and everything else is padding. ("nemo_automodel ... flex_qsa" page,
+ *    `_routes_to_membership`; "... fa4_qsa" page, `_preprocess` and
+ *    `fa4_sparse_gqa_attention`.)
+ *  - Membership and tiles. memb[b, i, j] = 1 iff j is in R(b, i); 128 x 128
+ *    tiles are absent (no member), full (all 128*128 cells members) or partial;
+ *    per tile row and per tile column, the partial and the full tile indices in
+ *    ascending order. ("fa4_qsa" page, `_block_kinds`, `_compact_blocks`;
+ *    "flex_qsa" page, `_dense_blocks_to_ordered`.)
+ *  - Forward. For every query head h of KV group g = h / (Hq / Hkv):
+ *    s_j = scale * <q, k_j> over j in R, lse = log sum_j exp(s_j),
+ *    o = sum_j exp(s_j - lse) v_j; an empty R gives o = 0 and lse = -inf.
+ *    ("Query Sparse Attention (QSA)" page of cuDNN Frontend, sections
+ *    "Tensors" and "Selection and components".)
+ *  - Backward. The equations of that section: P = exp(S - lse) on the allowed
+ *    keys and 0 elsewhere, delta = sum(dO * O), dP = dO V^T,
+ *    dS = P (dP - delta), dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO, with
+ *    dK and dV summed over the query heads that share a KV head.
+ *
+ * Inputs are double arrays (bf16 values are widened exactly by the caller).
+ * Layouts: q, dO [B, Sq, Hq, D]; k, v [B, Skv, Hkv, D]; routes [B, Sq, W]
+ * (int32 or int64); lse [B, Hq, Sq] when written for all rows.
+ *
+ * Every function has a "parity pin" in the CPU test suite: dense masked-softmax
+ * brute force, closed forms, central finite differences and invariants.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+typedef struct {
+    int64_t B, Sq, Skv, Hq, Hkv, D, W;
+    int32_t route_is_i64;
+    int32_t pad_;
+    double scale;
+    const void *routes;
+    const double *q, *k, *v, *dout;
+} orc_problem;
+
+static int64_t route_value(const orc_problem *P, int64_t flat)
+{
+    if (P->route_is_i64) return ((const int64_t *)P->routes)[flat];
+    return (int64_t)((const int32_t *)P->routes)[flat];
+}
+
+static int cmp_i64(const void *a, const void *b)
+{
+    int64_t x = *(const int64_t *)a, y = *(const int64_t *)b;
+    return (x > y) - (x < y);
+}
+
+/* R(b, i) in ascending order; returns |R|. `keys` must hold W entries. */
+static int64_t route_set_raw(const void *routes, int is_i64, int64_t W, int64_t Skv,
+                             int64_t row, int64_t *keys)
+{
+    int64_t n = 0;
+    for (int64_t w = 0; w < W; ++w) {
+        int64_t r = is_i64 ? ((const int64_t *)routes)[row * W + w]
+                           : (int64_t)((const int32_t *)routes)[row * W + w];
+        if (r >= 0 && r < Skv) keys[n++] = r;
+    }
+    qsort(keys, (size_t)n, sizeof(int64_t), cmp_i64);
+    int64_t m = 0;
+    for (int64_t t = 0; t < n; ++t)
+        if (m == 0 || keys[t] != keys[m - 1]) keys[m++] = keys[t];
+    return m;
+}
+
+int64_t orc_route_set(const void *routes, int32_t is_i64, int64_t W, int64_t Skv, int64_t row,
+                      int64_t *keys)
+{
+    return route_set_raw(routes, is_i64, W, Skv, row, keys);
+}
+
+/* memb[b, i, j] for j < Skv, zero in the padding columns up to `stride`. */
+void orc_membership(const void *routes, int32_t is_i64, int64_t B, int64_t Sq, int64_t W,
+                    int64_t Skv, int64_t stride, uint8_t *memb, uint8_t *has_routes)
+{
+    memset(memb, 0, (size_t)(B * Sq * stride));
+    for (int64_t row = 0; row < B * Sq; ++row) {
+        int any = 0;
+        for (int64_t w = 0; w < W; ++w) {
+            int64_t r = is_i64 ? ((const int64_t *)routes)[row * W + w]
+                               : (int64_t)((const int32_t *)routes)[row * W + w];
+            if (r >= 0 && r < Skv) {
+                memb[row * stride + r] = 1;
+                any = 1;
+            }
+        }
+        has_routes[row] = (uint8_t)any;
+    }
+}
+
+/*
+ * Tile kinds and lists. cnt = members of the tile (rows and columns clipped to
+ * the table); kind 0 if cnt == 0, 2 if cnt == tq * tk, else 1. Lists hold the
+ * matching tile indices in ascending order, then -1.
+ */
+void orc_tiles(const uint8_t *memb, int64_t B, int64_t Sq, int64_t Skv, int64_t stride,
+               int64_t tq, int64_t tk, int32_t *kinds, int32_t *fwd_p_cnt, int32_t *fwd_p_idx,
+               int32_t *fwd_f_cnt, int32_t *fwd_f_idx, int32_t *rev_p_cnt, int32_t *rev_p_idx,
+               int32_t *rev_f_cnt, int32_t *rev_f_idx)
+{
+    int64_t nqt = (Sq + tq - 1) / tq, nkt = (Skv + tk - 1) / tk;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t r = 0; r < nqt; ++r)
+            for (int64_t t = 0; t < nkt; ++t) {
+                int64_t cnt = 0;
+                for (int64_t i = r * tq; i < (r + 1) * tq && i < Sq; ++i)
+                    for (int64_t j = t * tk; j < (t + 1) * tk && j < Skv; ++j)
+                        cnt += memb[(b * Sq + i) * stride + j];
+                kinds[(b * nqt + r) * nkt + t] = cnt == 0 ? 0 : (cnt == tq * tk ? 2 : 1);
+            }
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t r = 0; r < nqt; ++r) {
+            int32_t np_ = 0, nf = 0;
+            int32_t *pi = fwd_p_idx + (b * nqt + r) * nkt, *fi = fwd_f_idx + (b * nqt + r) * nkt;
+            for (int64_t t = 0; t < nkt; ++t) {
+                int32_t kd = kinds[(b * nqt + r) * nkt + t];
+                if (kd == 1) pi[np_++] = (int32_t)t;
+                if (kd == 2) fi[nf++] = (int32_t)t;
+            }
+            for (int64_t t = np_; t < nkt; ++t) pi[t] = -1;
+            for (int64_t t = nf; t < nkt; ++t) fi[t] = -1;
+            fwd_p_cnt[b * nqt + r] = np_;
+            fwd_f_cnt[b * nqt + r] = nf;
+        }
+        for (int64_t t = 0; t < nkt; ++t) {
+            int32_t np_ = 0, nf = 0;
+            int32_t *pi = rev_p_idx + (b * nkt + t) * nqt, *fi = rev_f_idx + (b * nkt + t) * nqt;
+            for (int64_t r = 0; r < nqt; ++r) {
+                int32_t kd = kinds[(b * nqt + r) * nkt + t];
+                if (kd == 1) pi[np_++] = (int32_t)r;
+                if (kd == 2) fi[nf++] = (int32_t)r;
+            }
+            for (int64_t r = np_; r < nqt; ++r) pi[r] = -1;
+            for (int64_t r = nf; r < nqt; ++r) fi[r] = -1;
+            rev_p_cnt[b * nkt + t] = np_;
+            rev_f_cnt[b * nkt + t] = nf;
+        }
+    }
+}
+
+static double dot(const double *a, const double *b, int64_t n)
+{
+    double s = 0.0;
+    for (int64_t d = 0; d < n; ++d) s += a[d] * b[d];
+    return s;
+}
+
+/*
+ * Forward of one query row for all heads. s must hold |R| doubles.
+ * out [Hq, D], lse [Hq].
+ */
+static void forward_row(const orc_problem *P, int64_t b, int64_t i, const int64_t *keys,
+                        int64_t n, double *s, double *out, double *lse)
+{
+    const int64_t D = P->D, Hq = P->Hq, Hkv = P->Hkv, G = Hq / Hkv;
+    for (int64_t h = 0; h < Hq; ++h) {
+        const int64_t g = h / G;
+        double *o = out + h * D;
+        for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+        if (n == 0) {
+            lse[h] = -INFINITY;
+            continue;
+        }
+        const double *qh = P->q + ((b * P->Sq + i) * Hq + h) * D;
+        double m = -INFINITY;
+        for (int64_t t = 0; t < n; ++t) {
+            const double *kj = P->k + ((b * P->Skv + keys[t]) * Hkv + g) * D;
+            s[t] = P->scale * dot(qh, kj, D);
+            if (s[t] > m) m = s[t];
+        }
+        double l = 0.0;
+        for (int64_t t = 0; t < n; ++t) l += exp(s[t] - m);
+        lse[h] = m + log(l);
+        for (int64_t t = 0; t < n; ++t) {
+            const double p = exp(s[t] - lse[h]);
+            const double *vj = P->v + ((b * P->Skv + keys[t]) * Hkv + g) * D;
+            for (int64_t d = 0; d < D; ++d) o[d] += p * vj[d];
+        }
+    }
+}
+
+/* Forward for the listed flat rows (b * Sq + i): out [nrows, Hq, D], lse [nrows, Hq]. */
+void orc_forward(const orc_problem *P, int64_t nrows, const int64_t *rows, double *out,
+                 double *lse)
+{
+#pragma omp parallel
+    {
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)(P->W > 0 ? P->W : 1));
+        double *s = (double *)malloc(sizeof(double) * (size_t)(P->W > 0 ? P->W : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < nrows; ++t) {
+            const int64_t row = rows[t], b = row / P->Sq, i = row % P->Sq;
+            const int64_t n = route_set_raw(P->routes, P->route_is_i64, P->W, P->Skv, row, keys);
+            forward_row(P, b, i, keys, n, s, out + t * P->Hq * P->D, lse + t * P->Hq);
+        }
+        free(keys);
+        free(s);
+    }
+}
+
+/*
+ * Backward terms of one row: with the row's own O and lse, for each key of R
+ * and each head, p = exp(s - lse), dp = <dO, v>, ds = p (dp - delta).
+ * Accumulates dq [Hq, D] (zeroed here). When dk/dv are given ([nsel, Hkv, D]),
+ * also adds the row's contributions to the selected keys sel[0..nsel) of batch b.
+ */
+static void backward_row(const orc_problem *P, int64_t b, int64_t i, const int64_t *keys,
+                         int64_t n, double *s, double *o, double *lse, double *dq,
+                         int64_t nsel, const int64_t *sel, double *dk, double *dv)
+{
+    const int64_t D = P->D, Hq = P->Hq, Hkv = P->Hkv, G = Hq / Hkv;
+    forward_row(P, b, i, keys, n, s, o, lse);
+    for (int64_t x = 0; x < Hq * D; ++x) dq[x] = 0.0;
+    if (n == 0) return;
+    for (int64_t h = 0; h < Hq; ++h) {
+        const int64_t g = h / G;
+        const double *qh = P->q + ((b * P->Sq + i) * Hq + h) * D;
+        const double *doh = P->dout + ((b * P->Sq + i) * Hq + h) * D;
+        const double delta = dot(doh, o + h * D, D);
+        for (int64_t t = 0; t < n; ++t) {
+            const int64_t j = keys[t];
+            const double *kj = P->k + ((b * P->Skv + j) * Hkv + g) * D;
+            const double *vj = P->v + ((b * P->Skv + j) * Hkv + g) * D;
+            const double p = exp(P->scale * dot(qh, kj, D) - lse[h]);
+            const double dp = dot(doh, vj, D);
+            const double ds = p * (dp - delta);
+            for (int64_t d = 0; d < D; ++d) dq[h * D + d] += P->scale * ds * kj[d];
+            for (int64_t u = 0; u < nsel; ++u) {
+                if (sel[u] != b * P->Skv + j) continue;
+                for (int64_t d = 0; d < D; ++d) {
+                    dk[(u * Hkv + g) * D + d] += P->scale * ds * qh[d];
+                    dv[(u * Hkv + g) * D + d] += p * doh[d];
+                }
+            }
+        }
+    }
+}
+
+/* dq for the listed flat rows: dq [nrows, Hq, D]. */
+void orc_backward_dq(const orc_problem *P, int64_t nrows, const int64_t *rows, double *dq)
+{
+#pragma omp parallel
+    {
+        const int64_t W1 = P->W > 0 ? P->W : 1;
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)W1);
+        double *s = (double *)malloc(sizeof(double) * (size_t)W1);
+        double *o = (double *)malloc(sizeof(double) * (size_t)(P->Hq * P->D));
+        double *lse = (double *)malloc(sizeof(double) * (size_t)P->Hq);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < nrows; ++t) {
+            const int64_t row = rows[t], b = row / P->Sq, i = row % P->Sq;
+            const int64_t n = route_set_raw(P->routes, P->route_is_i64, P->W, P->Skv, row, keys);
+            backward_row(P, b, i, keys, n, s, o, lse, dq + t * P->Hq * P->D, 0, NULL, NULL,
+                         NULL);
+        }
+        free(keys);
+        free(s);
+        free(o);
+        free(lse);
+    }
+}
+
+/*
+ * dk, dv for the listed flat keys (b * Skv + j): dk, dv [nkeys, Hkv, D].
+ * Every query row of the keys' batches contributes when its route set holds
+ * the key. Rows are split over threads; each thread sums its rows in ascending
+ * order and the per-thread sums are added in thread order.
+ */
+void orc_backward_dkdv(const orc_problem *P, int64_t nkeys, const int64_t *keys_sel, double *dk,
+                       double *dv)
+{
+    const int64_t per = nkeys * P->Hkv * P->D;
+    memset(dk, 0, sizeof(double) * (size_t)per);
+    memset(dv, 0, sizeof(double) * (size_t)per);
+    int nthreads = 1;
+#ifdef _OPENMP
+    nthreads = omp_get_max_threads();
+#endif
+    double *acc_k = (double *)calloc((size_t)(per * nthreads), sizeof(double));
+    double *acc_v = (double *)calloc((size_t)(per * nthreads), sizeof(double));
+    const int64_t nrows = P->B * P->Sq;
+#pragma omp parallel num_threads(nthreads)
+    {
+        int tid = 0;
+#ifdef _OPENMP
+        tid = omp_get_thread_num();
+#endif
+        const int64_t W1 = P->W > 0 ? P->W : 1;
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)W1);
+        double *s = (double *)malloc(sizeof(double) * (size_t)W1);
+        double *o = (double *)malloc(sizeof(double) * (size_t)(P->Hq * P->D));
+        double *lse = (double *)malloc(sizeof(double) * (size_t)P->Hq);
+        double *dq = (double *)malloc(sizeof(double) * (size_t)(P->Hq * P->D));
+#pragma omp for schedule(static)
+        for (int64_t row = 0; row < nrows; ++row) {
+            const int64_t b = row / P->Sq, i = row % P->Sq;
+            const int64_t n = route_set_raw(P->routes, P->route_is_i64, P->W, P->Skv, row, keys);
+            int hit = 0;
+            for (int64_t u = 0; u < nkeys && !hit; ++u)
+                for (int64_t t = 0; t < n; ++t)
+                    if (keys_sel[u] == b * P->Skv + keys[t]) {
+                        hit = 1;
+                        break;
+                    }
+            if (!hit) continue;
+            backward_row(P, b, i, keys, n, s, o, lse, dq, nkeys, keys_sel, acc_k + tid * per,
+                         acc_v + tid * per);
+        }
+        free(keys);
+        free(s);
+        free(o);
+        free(lse);
+        free(dq);
+    }
+    for (int t = 0; t < nthreads; ++t)
+        for (int64_t x = 0; x < per; ++x) {
+            dk[x] += acc_k[t * per + x];
+            dv[x] += acc_v[t * per + x];
+        }
+    free(acc_k);
+    free(acc_v);
+}
+
+/*
+ * Whole backward restricted to a set of query rows: dq of those rows and their
+ * contributions to every dk, dv ([B, Skv, Hkv, D], zeroed here). With all rows
+ * listed this is the full backward. Rows are visited in list order, one thread.
+ */
+void orc_backward_rows(const orc_problem *P, int64_t nrows, const int64_t *rows, double *dq,
+                       double *dk, double *dv)
+{
+    const int64_t D = P->D, Hq = P->Hq, Hkv = P->Hkv, G = Hq / Hkv;
+    const int64_t W1 = P->W > 0 ? P->W : 1;
+    memset(dk, 0, sizeof(double) * (size_t)(P->B * P->Skv * Hkv * D));
+    memset(dv, 0, sizeof(double) * (size_t)(P->B * P->Skv * Hkv * D));
+    int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)W1);
+    double *s = (double *)malloc(sizeof(double) * (size_t)W1);
+    double *o = (double *)malloc(sizeof(double) * (size_t)(Hq * D));
+    double *lse = (double *)malloc(sizeof(double) * (size_t)Hq);
+    for (int64_t t = 0; t < nrows; ++t) {
+        const int64_t row = rows[t], b = row / P->Sq, i = row % P->Sq;
+        const int64_t n = route_set_raw(P->routes, P->route_is_i64, P->W, P->Skv, row, keys);
+        double *dqr = dq + t * Hq * D;
+        forward_row(P, b, i, keys, n, s, o, lse);
+        for (int64_t x = 0; x < Hq * D; ++x) dqr[x] = 0.0;
+        for (int64_t h = 0; h < Hq && n > 0; ++h) {
+            const int64_t g = h / G;
+            const double *qh = P->q + ((b * P->Sq + i) * Hq + h) * D;
+            const double *doh = P->dout + ((b * P->Sq + i) * Hq + h) * D;
+            const double delta = dot(doh, o + h * D, D);
+            for (int64_t u = 0; u < n; ++u) {
+                const int64_t j = keys[u];
+                const double *kj = P->k + ((b * P->Skv + j) * Hkv + g) * D;
+                const double *vj = P->v + ((b * P->Skv + j) * Hkv + g) * D;
+                const double p = exp(P->scale * dot(qh, kj, D) - lse[h]);
+                const double ds = p * (dot(doh, vj, D) - delta);
+                double *dkj = dk + ((b * P->Skv + j) * Hkv + g) * D;
+                double *dvj = dv + ((b * P->Skv + j) * Hkv + g) * D;
+                for (int64_t d = 0; d < D; ++d) {
+                    dqr[h * D + d] += P->scale * ds * kj[d];
+                    dkj[d] += P->scale * ds * qh[d];
+                    dvj[d] += p * doh[d];
+                }
+            }
+        }
+    }
+    free(keys);
+    free(s);
+    free(o);
+    free(lse);
+}
+
+int32_t orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return (int32_t)omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

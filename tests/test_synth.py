@@ -1,0 +1,96 @@
+"""The seeded workload generators produce the route structure they promise (CPU only)."""
+import numpy as np
+import pytest
+
+from token_indexed_sparse_amd import synth
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, 1.0 + 2**-9, -2.5, np.inf, 1e-40], np.float32)
+    b = synth.bf16_bits(x)
+    back = synth.bf16_to_f32(b)
+    assert back.tolist()[:5] == [1.0, 1.0, 1.0 + 4 * 2**-8, 1.0, -2.5]
+    assert np.isinf(back[5])
+    assert np.isnan(synth.bf16_to_f32(synth.bf16_bits(np.array([np.nan], np.float32))))[0]
+
+
+def _check_row(row, n_max, doc_start, pos):
+    c = (pos - doc_start) // 4
+    own = row[4 * n_max:]
+    want_own = list(range(doc_start + 4 * c, pos + 1))
+    assert own[: len(want_own)].tolist() == want_own
+    assert (own[len(want_own):] == -1).all()
+    body = row[: 4 * n_max].reshape(n_max, 4)
+    used = body[body[:, 0] >= 0]
+    assert (body[body[:, 0] < 0] == -1).all()
+    blocks = (used[:, 0] - doc_start) // 4
+    assert ((used - used[:, :1]) == np.arange(4)).all()
+    assert ((used[:, 0] - doc_start) % 4 == 0).all()
+    assert (np.diff(blocks) > 0).all() and (blocks < c).all() and (blocks >= 0).all()
+    return blocks, c
+
+
+def test_tiny_workload_structure_and_determinism():
+    wl = synth.WORKLOADS[1]
+    a = synth.make_inputs(wl)
+    b = synth.make_inputs(wl)
+    assert a.routes.shape == (1, 256, 36) and a.routes.dtype == np.int32
+    assert np.array_equal(a.routes, b.routes) and np.array_equal(a.q, b.q)
+    assert a.q.shape == (1, 256, 12, 256) and a.k.shape == (1, 256, 1, 256)
+    for p in range(256):
+        blocks, c = _check_row(a.routes[0, p], 8, 0, p)
+        assert len(blocks) == min(8, c)
+
+
+def test_docs_workload_structure():
+    wl = synth.WORKLOADS[2]
+    rng = np.random.default_rng(wl.seed)
+    routes, info = synth.make_routes(wl, rng)
+    starts = info["doc_starts"]
+    assert routes.shape == (1, 8192, 260) and len(starts) == 4 and starts[0] == 0
+    for p in range(0, 8192, 7):
+        s = int(starts[np.searchsorted(starts, p, side="right") - 1])
+        blocks, c = _check_row(routes[0, p], 64, s, p)
+        assert len(blocks) == min(64, c)
+
+
+def test_padded_workload_structure():
+    wl = synth.WORKLOADS[3]
+    rng = np.random.default_rng(wl.seed)
+    routes, info = synth.make_routes(wl, rng)
+    L = info["lengths"]
+    assert routes.shape == (4, 4096, 260)
+    assert ((L >= 1024) & (L <= 4096)).all()
+    for b in range(4):
+        assert (routes[b, L[b]:] == -1).all()
+        for p in range(0, int(L[b]), 13):
+            blocks, c = _check_row(routes[b, p], 64, 0, p)
+            assert len(blocks) == min(64, c)
+
+
+@pytest.mark.slow
+def test_long_and_shard_workload_structure():
+    wl = synth.WORKLOADS[4]
+    routes, _ = synth.make_routes(wl, np.random.default_rng(wl.seed))
+    assert routes.shape == (1, 32768, 2052)
+    for p in list(range(0, 32768, 997)) + [2047, 2048, 32767]:
+        blocks, c = _check_row(routes[0, p], 512, 0, p)
+        assert len(blocks) == min(c, 512)
+        recent = np.arange(max(0, c - 256), c)
+        assert np.isin(recent, blocks).all()
+    wl = synth.WORKLOADS[5]
+    routes, _ = synth.make_routes(wl, np.random.default_rng(wl.seed))
+    assert routes.shape == (1, 4096, 1028)
+    for i in range(0, 4096, 331):
+        blocks, c = _check_row(routes[0, i], 256, 0, 28672 + i)
+        assert len(blocks) == 256
+
+
+def test_random_case_has_padding_duplicates_and_invalid():
+    c = synth.random_case(0, 2, 50, 40, 12, 1, 16, route_dtype=np.int64)
+    r = c.routes
+    assert (r == -1).any() and (r >= 40).any() and (r < -1).any() and (r > 2**32).any()
+    dups = sum(len(x[(x >= 0) & (x < 40)]) - len(np.unique(x[(x >= 0) & (x < 40)]))
+               for x in r.reshape(-1, 16))
+    assert dups > 0
+    assert ((r == -1).all(-1)).sum() >= 2
