@@ -52,12 +52,6 @@ typedef struct {
     const double *q, *k, *v, *dout;
 } orc_problem;
 
-static int64_t route_value(const orc_problem *P, int64_t flat)
-{
-    if (P->route_is_i64) return ((const int64_t *)P->routes)[flat];
-    return (int64_t)((const int32_t *)P->routes)[flat];
-}
-
 static int cmp_i64(const void *a, const void *b)
 {
     int64_t x = *(const int64_t *)a, y = *(const int64_t *)b;
@@ -219,7 +213,7 @@ void orc_forward(const orc_problem *P, int64_t nrows, const int64_t *rows, doubl
 /*
  * Backward terms of one row: with the row's own O and lse, for each key of R
  * and each head, p = exp(s - lse), dp = <dO, v>, ds = p (dp - delta).
- * Accumulates dq [Hq, D] (zeroed here). When dk/dv are given ([nsel, Hkv, D]),
+ * Accumulates dq [Hq, D] (zeroed here) unless dq is NULL. When dk/dv are given ([nsel, Hkv, D]),
  * also adds the row's contributions to the selected keys sel[0..nsel) of batch b.
  */
 static void backward_row(const orc_problem *P, int64_t b, int64_t i, const int64_t *keys,
@@ -228,7 +222,8 @@ static void backward_row(const orc_problem *P, int64_t b, int64_t i, const int64
 {
     const int64_t D = P->D, Hq = P->Hq, Hkv = P->Hkv, G = Hq / Hkv;
     forward_row(P, b, i, keys, n, s, o, lse);
-    for (int64_t x = 0; x < Hq * D; ++x) dq[x] = 0.0;
+    if (dq)
+        for (int64_t x = 0; x < Hq * D; ++x) dq[x] = 0.0;
     if (n == 0) return;
     for (int64_t h = 0; h < Hq; ++h) {
         const int64_t g = h / G;
@@ -242,7 +237,8 @@ static void backward_row(const orc_problem *P, int64_t b, int64_t i, const int64
             const double p = exp(P->scale * dot(qh, kj, D) - lse[h]);
             const double dp = dot(doh, vj, D);
             const double ds = p * (dp - delta);
-            for (int64_t d = 0; d < D; ++d) dq[h * D + d] += P->scale * ds * kj[d];
+            if (dq)
+                for (int64_t d = 0; d < D; ++d) dq[h * D + d] += P->scale * ds * kj[d];
             for (int64_t u = 0; u < nsel; ++u) {
                 if (sel[u] != b * P->Skv + j) continue;
                 for (int64_t d = 0; d < D; ++d) {
@@ -308,7 +304,6 @@ void orc_backward_dkdv(const orc_problem *P, int64_t nkeys, const int64_t *keys_
         double *s = (double *)malloc(sizeof(double) * (size_t)W1);
         double *o = (double *)malloc(sizeof(double) * (size_t)(P->Hq * P->D));
         double *lse = (double *)malloc(sizeof(double) * (size_t)P->Hq);
-        double *dq = (double *)malloc(sizeof(double) * (size_t)(P->Hq * P->D));
 #pragma omp for schedule(static)
         for (int64_t row = 0; row < nrows; ++row) {
             const int64_t b = row / P->Sq, i = row % P->Sq;
@@ -321,14 +316,13 @@ void orc_backward_dkdv(const orc_problem *P, int64_t nkeys, const int64_t *keys_
                         break;
                     }
             if (!hit) continue;
-            backward_row(P, b, i, keys, n, s, o, lse, dq, nkeys, keys_sel, acc_k + tid * per,
+            backward_row(P, b, i, keys, n, s, o, lse, NULL, nkeys, keys_sel, acc_k + tid * per,
                          acc_v + tid * per);
         }
         free(keys);
         free(s);
         free(o);
         free(lse);
-        free(dq);
     }
     for (int t = 0; t < nthreads; ++t)
         for (int64_t x = 0; x < per; ++x) {

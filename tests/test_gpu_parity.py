@@ -1,0 +1,244 @@
+"""HIP path vs the FP64 oracle on the same seeded inputs (needs an MI355X).
+
+Integer tables (membership, tile kinds, tile lists, per-row key lists) must
+match bit-exactly. Floating outputs must satisfy |x - ref| <= tol + tol*|ref|
+elementwise, with tol = 1e-3 for out_fp32 and lse and 2e-2 for the bf16
+tensors out, dq, dk, dv; -inf LSE must match exactly. Small cases compare every
+element; the full-size workloads compare sampled rows and keys that the oracle
+computes one by one, plus properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import (TOL_BF16, TOL_FP32, GpuRun, bf16_bits_of, check_close,
+                      check_preprocess_exact, log, to_np)
+from token_indexed_sparse_amd import qsa, synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    qsa.library()  # fails loudly if the HIP library is missing
+
+
+def _full_compare(inp, scale, run=None):
+    run = run or GpuRun(inp, scale)
+    P = oracle.Problem(inp.q, inp.k, inp.v, inp.routes, scale, inp.grad_out)
+    o_ref, l_ref = P.forward_full()
+    check_close("out_fp32", to_np(run.out32), o_ref, TOL_FP32)
+    check_close("lse", to_np(run.lse), l_ref, TOL_FP32)
+    check_close("out", to_np(run.out), o_ref, TOL_BF16)
+    dq_ref, dk_ref, dv_ref = P.backward_full()
+    check_close("dq", to_np(run.dq), dq_ref, TOL_BF16)
+    check_close("dk", to_np(run.dk), dk_ref, TOL_BF16)
+    check_close("dv", to_np(run.dv), dv_ref, TOL_BF16)
+    # out is the bf16 rounding of the same kernel's out_fp32
+    from token_indexed_sparse_amd.synth import bf16_bits
+    assert np.array_equal(bf16_bits_of(run.out), bf16_bits(to_np(run.out32).astype(np.float32)))
+    return run
+
+
+# Small cases: several tiles, ragged tails, padding, duplicates, invalid IDs.
+SMALL = [
+    dict(seed=31, B=1, Sq=300, Skv=333, Hq=12, Hkv=1, W=40),
+    dict(seed=32, B=2, Sq=129, Skv=260, Hq=24, Hkv=2, W=70),
+    dict(seed=33, B=1, Sq=64, Skv=1000, Hq=12, Hkv=1, W=300),
+    dict(seed=34, B=3, Sq=17, Skv=5, Hq=12, Hkv=1, W=3),
+    dict(seed=35, B=1, Sq=200, Skv=200, Hq=12, Hkv=1, W=200, causal=True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"seed{c['seed']}")
+def test_small_cases_full_parity(case):
+    log(f"case {case}")
+    inp = synth.random_case(**case)
+    run = GpuRun(inp, 0.0625)
+    check_preprocess_exact(inp.routes, case["Skv"], run.routes)
+    _full_compare(inp, 0.0625, run)
+
+
+def test_int64_routes_huge_values_match_int32():
+    inp = synth.random_case(41, 1, 150, 140, 12, 1, 30, route_dtype=np.int64)
+    log("int64 routes with values beyond 2^31")
+    run = GpuRun(inp, 0.1)
+    check_preprocess_exact(inp.routes, 140, run.routes)
+    _full_compare(inp, 0.1, run)
+    r32 = np.where((inp.routes >= 0) & (inp.routes < 140), inp.routes, -1).astype(np.int32)
+    run32 = GpuRun(inp, 0.1, routes=r32)
+    for a, b in ((run.out32, run32.out32), (run.lse, run32.lse), (run.dq, run32.dq),
+                 (run.dk, run32.dk), (run.dv, run32.dv)):
+        assert torch.equal(a, b)
+
+
+def test_tiny_workload_full_parity():
+    wl = synth.WORKLOADS[1]
+    log(f"workload {wl.name}")
+    inp = synth.make_inputs(wl)
+    run = GpuRun(inp, wl.scale)
+    check_preprocess_exact(inp.routes, wl.Skv, run.routes)
+    _full_compare(inp, wl.scale, run)
+
+
+def _sample_rows(wl, inp, rng, n=48):
+    rows = set(range(3)) | set(range(wl.Sq - 3, wl.Sq))
+    rows |= set(int(x) for x in rng.choice(wl.Sq, n, replace=False))
+    for s in inp.info.get("doc_starts", []):
+        rows |= {int(s), min(int(s) + 5, wl.Sq - 1)}
+    flat = []
+    for b in range(wl.B):
+        extra = set()
+        if "lengths" in inp.info:
+            L = int(inp.info["lengths"][b])
+            extra = {L - 1, min(L, wl.Sq - 1), min(L + 1, wl.Sq - 1)}
+        flat += [b * wl.Sq + r for r in sorted(rows | extra)]
+    return np.array(sorted(set(flat)), np.int64)
+
+
+SAMPLED_KEYS = {
+    2: [0, 1, 2000, 4095, 6000, 8191],
+    3: [0, 77, 1030, 4095, 4096 + 5, 4096 * 2 + 3000, 4096 * 3 + 4095],
+    4: [16000, 16002, 31000, 32767],
+    5: [0, 5000, 20001, 28700, 32767],
+}
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4, 5])
+def test_full_size_workload_parity(idx):
+    wl = synth.WORKLOADS[idx]
+    log(f"workload {wl.name}: generating")
+    inp = synth.make_inputs(wl)
+    run = GpuRun(inp, wl.scale)
+    log("  preprocess check")
+    check_preprocess_exact(inp.routes, wl.Skv, run.routes)
+    P = oracle.Problem(inp.q, inp.k, inp.v, inp.routes, wl.scale, inp.grad_out)
+    rng = np.random.default_rng(100 + idx)
+    rows = _sample_rows(wl, inp, rng)
+    o_ref, l_ref = P.forward(rows)
+    out32 = to_np(run.out32).reshape(-1, wl.Hq, wl.D)[rows]
+    lse = to_np(run.lse).transpose(0, 2, 1).reshape(-1, wl.Hq)[rows]
+    check_close(f"out_fp32[{len(rows)} rows]", out32, o_ref, TOL_FP32)
+    check_close("lse[rows]", lse, l_ref, TOL_FP32)
+    check_close("out[rows]", to_np(run.out).reshape(-1, wl.Hq, wl.D)[rows], o_ref, TOL_BF16)
+    dq_ref = P.backward_dq(rows)
+    check_close("dq[rows]", to_np(run.dq).reshape(-1, wl.Hq, wl.D)[rows], dq_ref, TOL_BF16)
+    keys = np.array(SAMPLED_KEYS[idx], np.int64)
+    log(f"  oracle dk/dv for keys {keys.tolist()}")
+    dk_ref, dv_ref = P.backward_dkdv(keys)
+    check_close("dk[keys]", to_np(run.dk).reshape(-1, wl.Hkv, wl.D)[keys], dk_ref, TOL_BF16)
+    check_close("dv[keys]", to_np(run.dv).reshape(-1, wl.Hkv, wl.D)[keys], dv_ref, TOL_BF16)
+    # properties at full size: empty rows are exactly zero with -inf lse
+    has = (inp.routes >= 0).any(-1)
+    empty = ~has
+    if empty.any():
+        o = to_np(run.out32)[empty]
+        assert (o == 0).all() and not np.signbit(o).any()
+        assert (to_np(run.dq)[empty] == 0).all()
+        assert np.isneginf(to_np(run.lse).transpose(0, 2, 1)[empty]).all()
+    assert np.isfinite(to_np(run.out32)).all() and np.isfinite(to_np(run.dk)).all()
+
+
+def test_route_order_duplicates_invalid_ids_bitwise():
+    inp = synth.random_case(51, 1, 260, 300, 12, 1, 48)
+    base = GpuRun(inp, 0.0625)
+    rng = np.random.default_rng(9)
+    perm = np.take_along_axis(inp.routes,
+                              rng.permuted(np.tile(np.arange(48), (1, 260, 1)), axis=2), 2)
+    dup = inp.routes.copy()
+    bad = inp.routes.copy()
+    for i in range(260):
+        row = dup[0, i]
+        valid = row[(row >= 0) & (row < 300)]
+        if len(valid):
+            row[row == -1] = valid[-1]
+    bad[bad == -1] = 300
+    bad[0, ::2][bad[0, ::2] == 300] = -77
+    for name, r in (("permuted", perm), ("duplicated", dup), ("invalid", bad)):
+        other = GpuRun(inp, 0.0625, routes=r)
+        for a, b in ((base.out, other.out), (base.out32, other.out32), (base.lse, other.lse),
+                     (base.dq, other.dq), (base.dk, other.dk), (base.dv, other.dv)):
+            assert torch.equal(a, b), name
+        log(f"  {name}: bitwise identical")
+
+
+def test_run_to_run_bitwise_determinism():
+    wl = synth.WORKLOADS[2]
+    inp = synth.make_inputs(wl)
+    a = GpuRun(inp, wl.scale)
+    b = GpuRun(inp, wl.scale)
+    for x, y in ((a.out32, b.out32), (a.lse, b.lse), (a.dq, b.dq), (a.dk, b.dk), (a.dv, b.dv)):
+        assert torch.equal(x, y)
+
+
+def test_nan_in_unselected_kv_does_not_leak():
+    inp = synth.random_case(61, 1, 100, 120, 12, 1, 20)
+    r = inp.routes.copy()
+    r[(r >= 100) & (r < 120)] = -1                   # keys 100.. selected by nobody
+    base = GpuRun(inp, 0.0625, routes=r)
+    k = inp.k.copy()
+    v = inp.v.copy()
+    k[0, 100:] = 0x7FC0                              # NaN
+    v[0, 105:] = 0x7F80                              # +inf
+    q = inp.q.copy()
+    empty = np.nonzero(~((r >= 0) & (r < 120)).any(-1)[0])[0]
+    q[0, empty] = 0x7FC0                             # Q of padding rows is irrelevant
+    nan_inp = synth.Inputs(inp.wl, r, q, k, v, inp.grad_out, {})
+    other = GpuRun(nan_inp, 0.0625)
+    for a, b in ((base.out32, other.out32), (base.lse, other.lse), (base.dq, other.dq),
+                 (base.dv, other.dv)):
+        assert torch.equal(a, b)
+    assert torch.equal(base.dk[:, :100], other.dk[:, :100])
+    assert (other.dk[:, 100:] == 0).all() and (other.dv[:, 100:] == 0).all()
+
+
+def test_membership_offsets_beyond_int32():
+    # B * Sq * stride > 2^31: the tail rows must still see their own routes.
+    Sq = Skv = 46400
+    W = 4
+    rng = np.random.default_rng(3)
+    routes = np.full((1, Sq, W), -1, np.int32)
+    tail = np.arange(Sq - 300, Sq)
+    routes[0, tail, 0] = tail
+    routes[0, tail, 1] = rng.integers(0, Skv, size=len(tail))
+    routes[0, tail, 2] = np.maximum(tail - 1, 0)
+    log("membership beyond 2^31 bytes")
+    P = qsa.preprocess(torch.from_numpy(routes).cuda(), Skv, with_row_keys=True)
+    stride = P["memb"].shape[2]
+    assert Sq * stride > 2**31
+    memb_tail = P["memb"][0, Sq - 300:].cpu().numpy()
+    rk = P["row_keys"][0, Sq - 300:].cpu().numpy()
+    for n, i in enumerate(tail):
+        want = oracle.route_set(routes, Skv, int(i))
+        got = np.nonzero(memb_tail[n])[0]
+        assert np.array_equal(got, want), int(i)
+        assert np.array_equal(rk[n, :len(want)], want)
+    del P
+    torch.cuda.empty_cache()
+    # forward on the same routes (small head count, D=256): tail rows vs oracle
+    q = synth.bf16_bits(rng.standard_normal((1, Sq, 12, 256), dtype=np.float32))
+    kv = synth.bf16_bits(rng.standard_normal((1, Skv, 1, 256), dtype=np.float32))
+    inp = synth.Inputs(None, routes, q, kv, kv, None, {})
+    run = GpuRun(inp, 0.0625, backward=False)
+    Pr = oracle.Problem(q, kv, kv, routes, 0.0625)
+    rows = tail[-40:]
+    o_ref, l_ref = Pr.forward(rows)
+    check_close("out_fp32[tail]", to_np(run.out32[0, rows]), o_ref, TOL_FP32)
+
+
+def test_errors_through_binding():
+    q = torch.zeros((1, 8, 12, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 8, 1, 128), dtype=torch.bfloat16, device="cuda")
+    r = torch.zeros((1, 8, 4), dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        qsa.forward(q, k, k, r, 0.1)
+    q = torch.zeros((1, 8, 12, 256), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 8, 1, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        qsa.forward(q, k, k, r, float("inf"))
+    with pytest.raises(TypeError):
+        qsa.forward(q, k, k, r.float(), 0.1)
+    with pytest.raises(TypeError):
+        qsa.forward(q.float(), k, k, r, 0.1)

@@ -1,0 +1,192 @@
+// Route preprocessing on the device: membership table, per-row sorted key
+// lists, 128 x 128 tile kinds and the forward / reverse tile lists.
+//
+// Definitions: "nemo_automodel ... flex_qsa" page (`_routes_to_membership`,
+// `_block_mask_from_membership`, `_dense_blocks_to_ordered`) and "... fa4_qsa"
+// page (`_preprocess`, `_block_kinds`, `_compact_blocks`). Everything stays on
+// the device; the host never reads a count.
+//
+// gfx950 design: one workgroup per query row scatters the row's routes into an
+// on-chip bitmap (one bit per key, LDS atomics dedupe for free), then writes
+// the byte row of the table with 16-byte coalesced stores in a single pass
+// (the table is never cleared and re-scattered in HBM), compacts the bitmap
+// into the ascending key list with a workgroup prefix sum, and adds the row's
+// per-tile popcounts into the tile counters with integer atomics (the result
+// does not depend on their order). One wave per tile row / tile column then
+// classifies and compacts with ballots.
+#include "common.h"
+
+namespace qsa {
+
+namespace {
+
+constexpr int kPrepThreads = 256;
+
+__global__ void k_fill_i32(int32_t *__restrict__ p, int64_t n, int32_t value)
+{
+    for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < n;
+         x += (int64_t)gridDim.x * blockDim.x)
+        p[x] = value;
+}
+
+template <typename RouteT>
+__global__ __launch_bounds__(kPrepThreads) void k_prep_rows(Problem p)
+{
+    extern __shared__ uint32_t lds[];
+    const int64_t row = blockIdx.x;  // flat b * Sq + i
+    const int64_t b = row / p.Sq, i = row - b * p.Sq;
+    const int tid = threadIdx.x;
+    const int64_t nwords = p.stride >> 5;
+    uint32_t *bm = lds;
+    uint32_t *scan = lds + nwords;  // kPrepThreads + 1 entries
+
+    for (int64_t w = tid; w < nwords; w += kPrepThreads) bm[w] = 0u;
+    __syncthreads();
+
+    const RouteT *routes = static_cast<const RouteT *>(p.routes) + row * p.W;
+    for (int64_t s = tid; s < p.W; s += kPrepThreads) {
+        const int64_t r = (int64_t)routes[s];  // range test on the full width
+        if (r >= 0 && r < p.Skv) atomicOr(&bm[r >> 5], 1u << (r & 31));
+    }
+    __syncthreads();
+
+    // Byte row of the membership table, 16 bytes per store.
+    if (p.memb) {
+        uint4 *dst = reinterpret_cast<uint4 *>(p.memb + row * p.stride);
+        for (int64_t c = tid; c < (p.stride >> 4); c += kPrepThreads) {
+            const uint32_t bits = (bm[c >> 1] >> ((c & 1) * 16)) & 0xffffu;
+            uint32_t wv[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const uint32_t nib = (bits >> (4 * x)) & 0xfu;
+                wv[x] = (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
+            }
+            dst[c] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
+    }
+
+    // Ascending key list: each thread owns a contiguous run of words.
+    const int64_t per = (nwords + kPrepThreads - 1) / kPrepThreads;
+    const int64_t w0 = tid * per, w1 = (w0 + per < nwords) ? w0 + per : nwords;
+    int cnt = 0;
+    for (int64_t w = w0; w < w1; ++w) cnt += __popc(bm[w]);
+    scan[tid] = cnt;
+    __syncthreads();
+    for (int off = 1; off < kPrepThreads; off <<= 1) {
+        const int add = tid >= off ? scan[tid - off] : 0;
+        __syncthreads();
+        scan[tid] += add;
+        __syncthreads();
+    }
+    const int total = scan[kPrepThreads - 1];
+    int pos = scan[tid] - cnt;
+    int32_t *keys = p.row_keys + row * p.W;
+    for (int64_t w = w0; w < w1; ++w) {
+        uint32_t bits = bm[w];
+        while (bits) {
+            const int bit = __ffs(bits) - 1;
+            bits &= bits - 1;
+            keys[pos++] = (int32_t)(w * 32 + bit);
+        }
+    }
+    for (int64_t s = total + tid; s < p.W; s += kPrepThreads) keys[s] = -1;
+    if (tid == 0) {
+        p.row_cnt[row] = total;
+        if (p.has_routes) p.has_routes[row] = total > 0 ? 1 : 0;
+    }
+
+    // Tile counts: tile t covers words 4t .. 4t+3.
+    int32_t *tc = p.tile_cnt + (b * p.nQT + (i >> 7)) * p.nKT;
+    for (int64_t t = tid; t < p.nKT; t += kPrepThreads) {
+        const int c = __popc(bm[4 * t]) + __popc(bm[4 * t + 1]) + __popc(bm[4 * t + 2]) +
+                      __popc(bm[4 * t + 3]);
+        if (c) atomicAdd(&tc[t], c);
+    }
+}
+
+__device__ __forceinline__ int32_t tile_kind(int32_t cnt)
+{
+    return cnt == 0 ? 0 : (cnt == kTile * kTile ? 2 : 1);
+}
+
+// One wave per (b, tile row): kinds and the forward lists.
+__global__ __launch_bounds__(64) void k_lists_fwd(Problem p)
+{
+    const int64_t br = blockIdx.x;  // b * nQT + r
+    const int lane = threadIdx.x;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int32_t *tc = p.tile_cnt + br * p.nKT;
+    int32_t *kd = p.kinds + br * p.nKT;
+    int32_t *pi = p.fwd_p_idx + br * p.nKT;
+    int32_t *fi = p.fwd_f_idx + br * p.nKT;
+    int np_ = 0, nf = 0;
+    for (int64_t t0 = 0; t0 < p.nKT; t0 += 64) {
+        const int64_t t = t0 + lane;
+        const bool in = t < p.nKT;
+        const int32_t kind = in ? tile_kind(tc[t]) : 0;
+        if (in) kd[t] = kind;
+        const uint64_t mp = __ballot(in && kind == 1);
+        const uint64_t mf = __ballot(in && kind == 2);
+        if (kind == 1 && in) pi[np_ + __popcll(mp & below)] = (int32_t)t;
+        if (kind == 2 && in) fi[nf + __popcll(mf & below)] = (int32_t)t;
+        np_ += __popcll(mp);
+        nf += __popcll(mf);
+    }
+    for (int64_t t = np_ + lane; t < p.nKT; t += 64) pi[t] = -1;
+    for (int64_t t = nf + lane; t < p.nKT; t += 64) fi[t] = -1;
+    if (lane == 0) {
+        p.fwd_p_cnt[br] = np_;
+        p.fwd_f_cnt[br] = nf;
+    }
+}
+
+// One wave per (b, tile column): the reverse lists.
+__global__ __launch_bounds__(64) void k_lists_rev(Problem p)
+{
+    const int64_t bt = blockIdx.x;  // b * nKT + t
+    const int64_t b = bt / p.nKT, t = bt - b * p.nKT;
+    const int lane = threadIdx.x;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int32_t *pi = p.rev_p_idx + bt * p.nQT;
+    int32_t *fi = p.rev_f_idx + bt * p.nQT;
+    int np_ = 0, nf = 0;
+    for (int64_t r0 = 0; r0 < p.nQT; r0 += 64) {
+        const int64_t r = r0 + lane;
+        const bool in = r < p.nQT;
+        const int32_t kind = in ? tile_kind(p.tile_cnt[(b * p.nQT + r) * p.nKT + t]) : 0;
+        const uint64_t mp = __ballot(in && kind == 1);
+        const uint64_t mf = __ballot(in && kind == 2);
+        if (kind == 1 && in) pi[np_ + __popcll(mp & below)] = (int32_t)r;
+        if (kind == 2 && in) fi[nf + __popcll(mf & below)] = (int32_t)r;
+        np_ += __popcll(mp);
+        nf += __popcll(mf);
+    }
+    for (int64_t r = np_ + lane; r < p.nQT; r += 64) pi[r] = -1;
+    for (int64_t r = nf + lane; r < p.nQT; r += 64) fi[r] = -1;
+    if (lane == 0) {
+        p.rev_p_cnt[bt] = np_;
+        p.rev_f_cnt[bt] = nf;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_preprocess(const Problem &p, hipStream_t s)
+{
+    const int64_t ntiles = p.B * p.nQT * p.nKT;
+    int blocks = (int)((ntiles + 255) / 256);
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(k_fill_i32, dim3(blocks), dim3(256), 0, s, p.tile_cnt, ntiles, 0);
+    const size_t lds = (size_t)(p.stride / 32) * 4 + (kPrepThreads + 1) * 4;
+    if (p.route_is_i64)
+        hipLaunchKernelGGL(k_prep_rows<int64_t>, dim3((unsigned)(p.B * p.Sq)), dim3(kPrepThreads),
+                           lds, s, p);
+    else
+        hipLaunchKernelGGL(k_prep_rows<int32_t>, dim3((unsigned)(p.B * p.Sq)), dim3(kPrepThreads),
+                           lds, s, p);
+    hipLaunchKernelGGL(k_lists_fwd, dim3((unsigned)(p.B * p.nQT)), dim3(64), 0, s, p);
+    hipLaunchKernelGGL(k_lists_rev, dim3((unsigned)(p.B * p.nKT)), dim3(64), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace qsa
