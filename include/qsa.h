@@ -145,6 +145,27 @@ qsa_status qsa_preprocess(const qsa_dims *dims, const void *routes, uint8_t *mem
                           int32_t *rev_f_idx, int32_t *row_keys, int32_t *row_cnt,
                           void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Benchmark variants: identical work, plus event records between the launch
+ * stages so a caller can time each kernel on the stream it runs on. `events`
+ * holds n_events >= stages + 1 hipEvent_t handles created by the caller;
+ * events[0] is recorded before the first launch and events[s + 1] after
+ * stage s. Forward stages: 0 route preprocessing, 1 attention. Backward
+ * stages: 0 route preprocessing, 1 delta, 2 dQ, 3 dK/dV. events == NULL
+ * behaves exactly like the plain call; too few events gives QSA_ERR_NULL.
+ */
+#define QSA_FORWARD_STAGES 2
+#define QSA_BACKWARD_STAGES 4
+qsa_status qsa_forward_timed(const qsa_dims *dims, const void *q, const void *k, const void *v,
+                             const void *routes, float scale, void *out, float *out_fp32,
+                             float *lse, void *workspace, size_t workspace_bytes, void *stream,
+                             void *const *events, int32_t n_events);
+qsa_status qsa_backward_timed(const qsa_dims *dims, const void *grad_out, const void *q,
+                              const void *k, const void *v, const float *out_fp32,
+                              const float *lse, const void *routes, float scale, void *dq,
+                              void *dk, void *dv, void *workspace, size_t workspace_bytes,
+                              void *stream, void *const *events, int32_t n_events);
+
 /* Static description of a status code. */
 const char *qsa_status_string(qsa_status status);
 

@@ -152,6 +152,12 @@ qsa_status check_scale(float scale)
 
 size_t route_align(const qsa_dims *d) { return d->route_is_i64 ? 8 : 4; }
 
+hipError_t mark(void *const *events, int at, hipStream_t s)
+{
+    if (!events) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(events[at]), s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -171,9 +177,10 @@ size_t qsa_preprocess_workspace_bytes(const qsa_dims *dims)
     return check_dims(dims) == QSA_OK ? layout(dims, 2).total : 0;
 }
 
-qsa_status qsa_forward(const qsa_dims *dims, const void *q, const void *k, const void *v,
-                       const void *routes, float scale, void *out, float *out_fp32, float *lse,
-                       void *workspace, size_t workspace_bytes, void *stream)
+qsa_status qsa_forward_timed(const qsa_dims *dims, const void *q, const void *k, const void *v,
+                             const void *routes, float scale, void *out, float *out_fp32,
+                             float *lse, void *workspace, size_t workspace_bytes, void *stream,
+                             void *const *events, int32_t n_events)
 {
     qsa_status st = check_dims(dims);
     if (st != QSA_OK) return st;
@@ -197,15 +204,28 @@ qsa_status qsa_forward(const qsa_dims *dims, const void *q, const void *k, const
     p.out_fp32 = out_fp32;
     p.lse = lse;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (events && n_events < QSA_FORWARD_STAGES + 1) return QSA_ERR_NULL;
+    if (mark(events, 0, s) != hipSuccess) return QSA_ERR_DEVICE;
     if (launch_preprocess(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 1, s) != hipSuccess) return QSA_ERR_DEVICE;
     if (launch_forward(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 2, s) != hipSuccess) return QSA_ERR_DEVICE;
     return QSA_OK;
 }
 
-qsa_status qsa_backward(const qsa_dims *dims, const void *grad_out, const void *q, const void *k,
-                        const void *v, const float *out_fp32, const float *lse,
-                        const void *routes, float scale, void *dq, void *dk, void *dv,
-                        void *workspace, size_t workspace_bytes, void *stream)
+qsa_status qsa_forward(const qsa_dims *dims, const void *q, const void *k, const void *v,
+                       const void *routes, float scale, void *out, float *out_fp32, float *lse,
+                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    return qsa_forward_timed(dims, q, k, v, routes, scale, out, out_fp32, lse, workspace,
+                             workspace_bytes, stream, nullptr, 0);
+}
+
+qsa_status qsa_backward_timed(const qsa_dims *dims, const void *grad_out, const void *q,
+                              const void *k, const void *v, const float *out_fp32,
+                              const float *lse, const void *routes, float scale, void *dq,
+                              void *dk, void *dv, void *workspace, size_t workspace_bytes,
+                              void *stream, void *const *events, int32_t n_events)
 {
     qsa_status st = check_dims(dims);
     if (st != QSA_OK) return st;
@@ -234,9 +254,26 @@ qsa_status qsa_backward(const qsa_dims *dims, const void *grad_out, const void *
     p.dk = static_cast<uint16_t *>(dk);
     p.dv = static_cast<uint16_t *>(dv);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (events && n_events < QSA_BACKWARD_STAGES + 1) return QSA_ERR_NULL;
+    if (mark(events, 0, s) != hipSuccess) return QSA_ERR_DEVICE;
     if (launch_preprocess(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
-    if (launch_backward(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 1, s) != hipSuccess) return QSA_ERR_DEVICE;
+    if (launch_delta(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 2, s) != hipSuccess) return QSA_ERR_DEVICE;
+    if (launch_dq(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 3, s) != hipSuccess) return QSA_ERR_DEVICE;
+    if (launch_dkdv(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 4, s) != hipSuccess) return QSA_ERR_DEVICE;
     return QSA_OK;
+}
+
+qsa_status qsa_backward(const qsa_dims *dims, const void *grad_out, const void *q, const void *k,
+                        const void *v, const float *out_fp32, const float *lse,
+                        const void *routes, float scale, void *dq, void *dk, void *dv,
+                        void *workspace, size_t workspace_bytes, void *stream)
+{
+    return qsa_backward_timed(dims, grad_out, q, k, v, out_fp32, lse, routes, scale, dq, dk, dv,
+                              workspace, workspace_bytes, stream, nullptr, 0);
 }
 
 qsa_status qsa_preprocess(const qsa_dims *dims, const void *routes, uint8_t *memb,

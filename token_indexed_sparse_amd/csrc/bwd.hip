@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kDqWaves * 64) void k_dq(Problem p)
                 for (int e = 0; e < 4; ++e) {
                     const bool valid = hv && (c0 + kb * 16 + 4 * quad + e < n);
                     const float pr = valid ? exp2f(sa[e] * c - lse2) : 0.f;
-                    ds[kb * 4 + e] = pr * (pa[e] - dlt);
+                    ds[kb * 4 + e] = valid ? pr * (pa[e] - dlt) : 0.f;
                 }
             }
             uint32_t dsb[4];
@@ -158,11 +158,6 @@ __global__ __launch_bounds__(kDqWaves * 64) void k_dq(Problem p)
 // ---------------------------------------------------------------- dK, dV
 constexpr int kKvWaves = 2;
 constexpr int kStage = kGroup * kLdsStride;  // one staged 12-head row block
-
-struct PairState {
-    float pa[4], da[4];  // P and dS of the first row of the pair (heads 4*quad+e, key col)
-    int filled;
-};
 
 __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
 {
@@ -309,7 +304,8 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
                             dl = p.delta[hix];
                         }
                         pn[e2] = pr;
-                        dn[e2] = pr * (pd[e2] - dl);
+                        // select, never multiply: an unselected key's dP may be non-finite
+                        dn[e2] = (hq && kin) ? pr * (pd[e2] - dl) : 0.f;
                     }
                     if (filled == 0) {
 #pragma unroll
@@ -358,13 +354,23 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
 
 }  // namespace
 
-hipError_t launch_backward(const Problem &p, hipStream_t s)
+hipError_t launch_delta(const Problem &p, hipStream_t s)
 {
     const int64_t rows_heads = p.B * p.Sq * p.Hq;
     hipLaunchKernelGGL(k_delta, dim3((unsigned)((rows_heads + 3) / 4)), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_dq(const Problem &p, hipStream_t s)
+{
     const int64_t items = p.B * p.Sq * p.Hkv;
     hipLaunchKernelGGL(k_dq, dim3((unsigned)((items + kDqWaves - 1) / kDqWaves)),
                        dim3(kDqWaves * 64), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_dkdv(const Problem &p, hipStream_t s)
+{
     const int64_t groups = p.B * p.Hkv * (p.stride >> 4);
     hipLaunchKernelGGL(k_dkdv, dim3((unsigned)((groups + kKvWaves - 1) / kKvWaves)),
                        dim3(kKvWaves * 64), 0, s, p);
