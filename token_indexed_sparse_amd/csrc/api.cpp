@@ -33,12 +33,16 @@ qsa_status check_dims(const qsa_dims *d)
         return QSA_ERR_SHAPE;
     const int64_t stride = (d->Skv + kTile - 1) / kTile * kTile;
     if (d->B * d->Hkv * stride > (int64_t(1) << 30)) return QSA_ERR_SHAPE;
+    // Gathers use 32-bit buffer offsets within one batch row of K/V or Q/dO.
+    if (d->Skv * d->Hkv * kD * 2 >= (int64_t(1) << 31)) return QSA_ERR_SHAPE;
+    if (d->Sq * d->Hq * kD * 2 >= (int64_t(1) << 31)) return QSA_ERR_SHAPE;
+    if (d->W * 4 >= (int64_t(1) << 31)) return QSA_ERR_SHAPE;
     return QSA_OK;
 }
 
 struct Layout {
-    size_t memb, has, row_keys, row_cnt, tile_cnt, kinds, fpc, fpi, ffc, ffi, rpc, rpi, rfc, rfi,
-        delta, total;
+    size_t memb, has, mbits, row_keys, row_cnt, tile_cnt, kinds, fpc, fpi, ffc, ffi, rpc, rpi, rfc,
+        rfi, delta, total;
 };
 
 // which: 0 forward, 1 backward, 2 preprocess (only tile counts and, if the
@@ -59,6 +63,7 @@ Layout layout(const qsa_dims *d, int which)
     const size_t none = (size_t)-1;
     L.memb = which == 2 ? none : take((size_t)(rows * stride));
     L.has = which == 2 ? none : take((size_t)rows);
+    L.mbits = which == 1 ? take((size_t)(rows * (stride / 32)) * 4) : none;
     L.row_keys = take((size_t)(rows * d->W) * 4);
     L.row_cnt = take((size_t)rows * 4);
     L.tile_cnt = take((size_t)(d->B * nQT * nKT) * 4);
@@ -128,6 +133,7 @@ void carve(Problem &p, const Layout &L, void *ws)
     const size_t none = (size_t)-1;
     if (L.memb != none) p.memb = reinterpret_cast<uint8_t *>(w + L.memb);
     if (L.has != none) p.has_routes = reinterpret_cast<uint8_t *>(w + L.has);
+    if (L.mbits != none) p.mbits = reinterpret_cast<uint32_t *>(w + L.mbits);
     p.row_keys = reinterpret_cast<int32_t *>(w + L.row_keys);
     p.row_cnt = reinterpret_cast<int32_t *>(w + L.row_cnt);
     p.tile_cnt = reinterpret_cast<int32_t *>(w + L.tile_cnt);

@@ -9,33 +9,27 @@
 // Three kernels, no floating-point atomics anywhere:
 //  * k_delta: one wave per (row, head) reduces dO . out_fp32.
 //  * k_dq: query-major like the forward (one wave per row and KV head walks
-//    the row's sorted key list in 32-slot steps). S^T and dP^T come from the
-//    gathered K and V rows straight into the matrix core; dS^T stays in the
-//    accumulator layout and is the B operand of dQ^T = K^T dS^T, with K staged
-//    in LDS and read transposed.
+//    the row's sorted key list in 32-slot chunks, next chunk's gathers in
+//    flight). S^T and dP^T come from the gathered K and V rows straight into
+//    the matrix core; dS^T stays in the accumulator layout and is the B
+//    operand of dQ^T = K^T dS^T, with K staged in LDS and read transposed.
 //  * k_dkdv: key-major. One wave owns 16 consecutive keys of one KV head and
 //    keeps their K and V rows in registers and their dK, dV accumulators for
 //    the whole run. It walks the reverse tile lists of its 128-key tile column
-//    (partial tiles, then full tiles) and reads the 16-byte membership slice of
-//    every query row in those tiles; rows that select at least one of its keys
-//    are processed in ascending order, two at a time: S = Q K^T and dP = dO V^T
-//    per row (M = heads), then dV += P^T dO and dK += dS^T Q with the two rows'
-//    heads forming the 32-long contraction. Q and dO rows are staged in LDS and
-//    read transposed.
+//    (partial tiles, then full tiles), reads a 16-bit slice of the bit-packed
+//    membership row of every query in those tiles, and collects the rows that
+//    select one of its keys into an LDS list (ascending). Rows are then
+//    processed in that order with the next row's Q, dO, lse and delta loads in
+//    flight: S = Q K^T and dP = dO V^T per row (M = heads), then, two rows at
+//    a time, dV += P^T dO and dK += dS^T Q with the two rows' heads forming the
+//    32-long contraction. Q and dO rows are staged in LDS and read transposed.
+//    Blocks are mapped XCD-aware so the waves of one tile column (which read
+//    the same query rows) share an L2.
 #include "common.h"
 
 namespace qsa {
 
 namespace {
-
-constexpr int kLdsStride = 264;  // bf16 elements per staged row (528 bytes)
-
-__device__ __forceinline__ void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // ---------------------------------------------------------------- delta
 __global__ __launch_bounds__(256) void k_delta(Problem p)
@@ -60,12 +54,17 @@ __global__ __launch_bounds__(256) void k_delta(Problem p)
 constexpr int kDqWaves = 4;
 constexpr int kChunk = 32;
 
+struct Gather {
+    uint4 k[2][8];
+    uint4 v[2][8];
+};
+
 __global__ __launch_bounds__(kDqWaves * 64) void k_dq(Problem p)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t ks_all[kDqWaves][kChunk * kLdsStride];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __shared__ __attribute__((aligned(16))) char ks_all[kDqWaves][2 * kTrBlock];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int col = lane & 15, quad = lane >> 4;
-    const int64_t item = (int64_t)blockIdx.x * kDqWaves + wave;
+    const int64_t item = xcd_logical_block(blockIdx.x, gridDim.x) * kDqWaves + wave;
     if (item >= p.B * p.Sq * p.Hkv) return;
     const int64_t row = item / p.Hkv;
     const int g = (int)(item - row * p.Hkv);
@@ -73,7 +72,7 @@ __global__ __launch_bounds__(kDqWaves * 64) void k_dq(Problem p)
     const int head = g * kGroup + col;
     const bool hv = col < kGroup;
     const int n = p.row_cnt[row];
-    uint16_t *ks = ks_all[wave];
+    char *ks = ks_all[wave];
     uint16_t *dqp = p.dq + (row * p.Hq + head) * (int64_t)kD;
 
     f32x4 acc[16];
@@ -81,67 +80,114 @@ __global__ __launch_bounds__(kDqWaves * 64) void k_dq(Problem p)
     for (int db = 0; db < 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (n > 0) {
+        const uint32_t row_bytes = (uint32_t)(p.Hkv * kD * 2);
+        const uint32_t kv_bytes = (uint32_t)((p.Skv - 1) * p.Hkv * kD * 2 + kD * 2);
+        const rsrc_t rk = make_rsrc(p.k + (b * p.Skv * p.Hkv + g) * (int64_t)kD, kv_bytes);
+        const rsrc_t rv = make_rsrc(p.v + (b * p.Skv * p.Hkv + g) * (int64_t)kD, kv_bytes);
         bf16x8 qf[8], gf[8];
-        const int64_t qoff = (row * p.Hq + (hv ? head : 0)) * (int64_t)kD + quad * 64;
-        const uint4 *qp = reinterpret_cast<const uint4 *>(p.q + qoff);
-        const uint4 *gp = reinterpret_cast<const uint4 *>(p.dout + qoff);
+        {
+            const int64_t rbase = (row * p.Hq + g * kGroup) * (int64_t)kD;
+            const rsrc_t rq = make_rsrc(p.q + rbase, (uint32_t)(kGroup * kD * 2));
+            const rsrc_t rg = make_rsrc(p.dout + rbase, (uint32_t)(kGroup * kD * 2));
+            const uint32_t off = hv ? (uint32_t)(col * kD * 2 + quad * 128) : kOutOfRange;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            qf[s] = as_bf16x8(hv ? qp[s] : zero_u4());
-            gf[s] = as_bf16x8(hv ? gp[s] : zero_u4());
+            for (int s = 0; s < 8; ++s) {
+                qf[s] = as_bf16x8(buf_load16(rq, off + 16 * s));
+                gf[s] = as_bf16x8(buf_load16(rg, off + 16 * s));
+            }
         }
         const float lse2 = hv ? p.lse_in[(b * p.Hq + head) * p.Sq + i] * 1.4426950408889634f : 0.f;
         const float dlt = hv ? p.delta[(b * p.Hq + head) * p.Sq + i] : 0.f;
         const float c = p.scale * 1.4426950408889634f;
-        const int32_t *keys = p.row_keys + row * p.W;
-        const int64_t kv_base = b * p.Skv;
-
-        for (int c0 = 0; c0 < n; c0 += kChunk) {
+        const rsrc_t rkeys = make_rsrc(p.row_keys + row * p.W, (uint32_t)(p.W * 4));
+        auto fetch_keys = [&](int c0, int (&kk)[2]) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int slot = c0 + kb * 16 + col;
+                kk[kb] = (int)__builtin_amdgcn_raw_buffer_load_b32(
+                    rkeys, slot < n ? (uint32_t)slot * 4 : kOutOfRange, 0, 0);
+                kk[kb] = slot < n ? kk[kb] : -1;
+            }
+        };
+        auto offsets = [&](const int (&kk)[2], uint32_t (&off)[2]) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                off[kb] = kk[kb] >= 0 ? (uint32_t)kk[kb] * row_bytes + quad * 128 : kOutOfRange;
+        };
+        auto issue = [&](Gather &G, const uint32_t (&off)[2]) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    G.k[kb][s] = buf_load16(rk, off[kb] + 16 * s);
+                    G.v[kb][s] = buf_load16(rv, off[kb] + 16 * s);
+                }
+        };
+        const int tr_lane = lane_tr_base(col, quad);
+        auto compute = [&](const Gather &G, int c0) {
             float ds[8];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const int slot = kb * 16 + col;
-                const int key = (c0 + slot < n) ? keys[c0 + slot] : -1;
-                const int64_t off =
-                    key >= 0 ? ((kv_base + key) * p.Hkv + g) * (int64_t)kD + quad * 64 : 0;
-                const uint4 *kp = reinterpret_cast<const uint4 *>(p.k + off);
-                const uint4 *vp = reinterpret_cast<const uint4 *>(p.v + off);
-                uint4 *kd = reinterpret_cast<uint4 *>(ks + slot * kLdsStride + quad * 64);
                 f32x4 sa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
-                    const uint4 kv = key >= 0 ? kp[s] : zero_u4();
-                    const uint4 vv = key >= 0 ? vp[s] : zero_u4();
-                    kd[s] = kv;
-                    sa = mfma_16x16x32(as_bf16x8(kv), qf[s], sa);
-                    pa = mfma_16x16x32(as_bf16x8(vv), gf[s], pa);
+                    sa = mfma_16x16x32(as_bf16x8(G.k[kb][s]), qf[s], sa);
+                    pa = mfma_16x16x32(as_bf16x8(G.v[kb][s]), gf[s], pa);
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const bool valid = hv && (c0 + kb * 16 + 4 * quad + e < n);
                     const float pr = valid ? exp2f(sa[e] * c - lse2) : 0.f;
+                    // select, never multiply: a padding slot's dP is not used
                     ds[kb * 4 + e] = valid ? pr * (pa[e] - dlt) : 0.f;
                 }
             }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int s = 0; s < 8; ++s)
+                    tr_store8(ks + kb * kTrBlock, col, quad * 64 + 8 * s, G.k[kb][s]);
             uint32_t dsb[4];
 #pragma unroll
             for (int x = 0; x < 4; ++x) dsb[x] = pack_bf16x2(ds[2 * x], ds[2 * x + 1]);
             const bf16x8 dsv = as_bf16x8(make_uint4(dsb[0], dsb[1], dsb[2], dsb[3]));
             wave_lds_sync();
 #pragma unroll
-            for (int db = 0; db < 16; ++db) {
-                const uint16_t *kc = ks + 16 * db + col;
-                uint32_t a[4];
+            for (int h = 0; h < 4; ++h) {
+                uint2 a0[4], a1[4];
 #pragma unroll
-                for (int x = 0; x < 2; ++x) {
-                    const int s0 = 4 * quad + 2 * x;
-                    a[x] = (uint32_t)kc[s0 * kLdsStride] | ((uint32_t)kc[(s0 + 1) * kLdsStride] << 16);
-                    a[x + 2] = (uint32_t)kc[(s0 + 16) * kLdsStride] |
-                               ((uint32_t)kc[(s0 + 17) * kLdsStride] << 16);
+                for (int x = 0; x < 4; ++x) {
+                    a0[x] = lds_read_tr(ks + tr_lane + tile_tr_offset(4 * h + x));
+                    a1[x] = lds_read_tr(ks + kTrBlock + tr_lane + tile_tr_offset(4 * h + x));
                 }
-                acc[db] = mfma_16x16x32(as_bf16x8(make_uint4(a[0], a[1], a[2], a[3])), dsv, acc[db]);
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    acc[4 * h + x] = mfma_16x16x32(
+                        as_bf16x8(make_uint4(a0[x].x, a0[x].y, a1[x].x, a1[x].y)), dsv,
+                        acc[4 * h + x]);
             }
             wave_lds_sync();
+        };
+
+        const int nchunks = (n + kChunk - 1) / kChunk;
+        Gather G0, G1;
+        int kA[2], kB[2];
+        uint32_t off[2];
+        fetch_keys(0, kA);
+        fetch_keys(kChunk, kB);
+        offsets(kA, off);
+        issue(G0, off);
+        auto step = [&](Gather &cur, Gather &nxt, const int (&kn)[2], int (&kfree)[2], int ch) {
+            fetch_keys((ch + 2) * kChunk, kfree);
+            offsets(kn, off);
+            issue(nxt, off);
+            __builtin_amdgcn_sched_barrier(0);  // keep the gathers ahead of the compute
+            compute(cur, ch * kChunk);
+        };
+        for (int ch = 0; ch < nchunks; ch += 2) {
+            step(G0, G1, kB, kA, ch);
+            if (ch + 1 >= nchunks) break;
+            step(G1, G0, kA, kB, ch + 1);
         }
     }
     if (!hv) return;
@@ -157,16 +203,27 @@ __global__ __launch_bounds__(kDqWaves * 64) void k_dq(Problem p)
 
 // ---------------------------------------------------------------- dK, dV
 constexpr int kKvWaves = 2;
-constexpr int kStage = kGroup * kLdsStride;  // one staged 12-head row block
+constexpr int kHitCap = 320;   // LDS hit list capacity per wave
+constexpr int kHitBatch = 64;  // stop scanning once this many hits are listed
+constexpr int kScanWin = 4;    // 64-row windows scanned per step
+
+struct RowOps {
+    uint4 q[8], g[8];
+    float lse[4], dl[4];
+};
 
 __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
 {
-    // Per wave: Q and dO of two query rows, 12 heads each.
-    __shared__ __attribute__((aligned(16))) uint16_t st_all[kKvWaves][4 * kStage];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // Per wave: Q and dO of two query rows in the transposed staging layout,
+    // and the list of (row, 16-bit mask) hits.
+    __shared__ __attribute__((aligned(16))) char st_all[kKvWaves][4 * kTrBlock];
+    __shared__ int32_t hit_row[kKvWaves][kHitCap];
+    __shared__ uint32_t hit_mask[kKvWaves][kHitCap];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int col = lane & 15, quad = lane >> 4;
     const int64_t ngroups = p.stride >> 4;
-    const int64_t item = (int64_t)blockIdx.x * kKvWaves + wave;  // ((b * Hkv + g) * ngroups + kg)
+    // item = (b * Hkv + g) * ngroups + kg
+    const int64_t item = xcd_logical_block(blockIdx.x, gridDim.x) * kKvWaves + wave;
     if (item >= p.B * p.Hkv * ngroups) return;
     const int64_t kg = item % ngroups;
     const int64_t bg = item / ngroups;
@@ -175,21 +232,28 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
     const int64_t key0 = kg * 16;
     if (key0 >= p.Skv) return;
     const int64_t t = key0 >> 7;
-    uint16_t *stq[2] = {st_all[wave], st_all[wave] + kStage};
-    uint16_t *stg[2] = {st_all[wave] + 2 * kStage, st_all[wave] + 3 * kStage};
+    char *stq[2] = {st_all[wave], st_all[wave] + kTrBlock};
+    char *stg[2] = {st_all[wave] + 2 * kTrBlock, st_all[wave] + 3 * kTrBlock};
+    int32_t *hrow = hit_row[wave];
+    uint32_t *hmask = hit_mask[wave];
+
+    // Clear the staging area: rows 12..15 (heads past the group) stay zero.
+    for (int o = lane * 16; o < 4 * kTrBlock; o += 64 * 16)
+        *reinterpret_cast<uint4 *>(st_all[wave] + o) = zero_u4();
 
     // K and V rows of the 16 keys as B operands of S = Q K^T and dP = dO V^T.
     bf16x8 kf[8], vf[8];
     {
+        const uint32_t kv_bytes = (uint32_t)((p.Skv - 1) * p.Hkv * kD * 2 + kD * 2);
+        const rsrc_t rk = make_rsrc(p.k + (b * p.Skv * p.Hkv + g) * (int64_t)kD, kv_bytes);
+        const rsrc_t rv = make_rsrc(p.v + (b * p.Skv * p.Hkv + g) * (int64_t)kD, kv_bytes);
         const int64_t key = key0 + col;
-        const bool kvalid = key < p.Skv;
-        const int64_t off = kvalid ? ((b * p.Skv + key) * p.Hkv + g) * (int64_t)kD + quad * 64 : 0;
-        const uint4 *kp = reinterpret_cast<const uint4 *>(p.k + off);
-        const uint4 *vp = reinterpret_cast<const uint4 *>(p.v + off);
+        const uint32_t off =
+            key < p.Skv ? (uint32_t)(key * p.Hkv * kD * 2 + quad * 128) : kOutOfRange;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            kf[s] = as_bf16x8(kvalid ? kp[s] : zero_u4());
-            vf[s] = as_bf16x8(kvalid ? vp[s] : zero_u4());
+            kf[s] = as_bf16x8(buf_load16(rk, off + 16 * s));
+            vf[s] = as_bf16x8(buf_load16(rv, off + 16 * s));
         }
     }
     f32x4 adk[16], adv[16];
@@ -199,139 +263,176 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
         adv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const float c = p.scale * 1.4426950408889634f;
-    const bool hq = quad < 3;  // accumulator rows 4*quad+e are real heads
+    const bool hq = quad < 3;      // accumulator rows 4*quad+e are real heads
+    const bool hv = col < kGroup;  // lane loads head `col` of a Q/dO row
+    const int tr_lane = lane_tr_base(col, quad);
+
+    // Q/dO rows of this batch and group; lse/delta of this batch and group.
+    const uint32_t q_bytes = (uint32_t)((p.Sq - 1) * p.Hq * kD * 2 + kGroup * kD * 2);
+    const rsrc_t rq = make_rsrc(p.q + (b * p.Sq * p.Hq + g * kGroup) * (int64_t)kD, q_bytes);
+    const rsrc_t rg = make_rsrc(p.dout + (b * p.Sq * p.Hq + g * kGroup) * (int64_t)kD, q_bytes);
+    const rsrc_t rl = make_rsrc(p.lse_in + (b * p.Hq + g * kGroup) * p.Sq,
+                                (uint32_t)(kGroup * p.Sq * 4));
+    const rsrc_t rd = make_rsrc(p.delta + (b * p.Hq + g * kGroup) * p.Sq,
+                                (uint32_t)(kGroup * p.Sq * 4));
+    auto load_row = [&](RowOps &R, int64_t qi) {
+        const uint32_t off =
+            hv ? (uint32_t)(qi * p.Hq * kD * 2 + col * kD * 2 + quad * 128) : kOutOfRange;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            R.q[s] = buf_load16(rq, off + 16 * s);
+            R.g[s] = buf_load16(rg, off + 16 * s);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = hq ? (uint32_t)(((4 * quad + e) * p.Sq + qi) * 4) : kOutOfRange;
+            R.lse[e] =
+                __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, lo, 0, 0));
+            R.dl[e] =
+                __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, lo, 0, 0));
+        }
+    };
+
     float pa[4] = {0.f, 0.f, 0.f, 0.f}, da[4] = {0.f, 0.f, 0.f, 0.f};
     int filled = 0;
 
     // Contract the staged pair into dV and dK. Slot j of lane group quad is
     // head 4*quad + (j & 3) of row (j < 4 ? first : second).
     auto flush = [&](const float *pb, const float *db_) {
-        uint32_t ap[4], ad[4];
-        ap[0] = pack_bf16x2(pa[0], pa[1]);
-        ap[1] = pack_bf16x2(pa[2], pa[3]);
-        ap[2] = pack_bf16x2(pb[0], pb[1]);
-        ap[3] = pack_bf16x2(pb[2], pb[3]);
-        ad[0] = pack_bf16x2(da[0], da[1]);
-        ad[1] = pack_bf16x2(da[2], da[3]);
-        ad[2] = pack_bf16x2(db_[0], db_[1]);
-        ad[3] = pack_bf16x2(db_[2], db_[3]);
-        const bf16x8 A_p = as_bf16x8(make_uint4(ap[0], ap[1], ap[2], ap[3]));
-        const bf16x8 A_d = as_bf16x8(make_uint4(ad[0], ad[1], ad[2], ad[3]));
+        const bf16x8 A_p =
+            as_bf16x8(make_uint4(pack_bf16x2(pa[0], pa[1]), pack_bf16x2(pa[2], pa[3]),
+                                 pack_bf16x2(pb[0], pb[1]), pack_bf16x2(pb[2], pb[3])));
+        const bf16x8 A_d =
+            as_bf16x8(make_uint4(pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3]),
+                                 pack_bf16x2(db_[0], db_[1]), pack_bf16x2(db_[2], db_[3])));
         wave_lds_sync();
 #pragma unroll
-        for (int dbk = 0; dbk < 16; ++dbk) {
-            uint32_t bg_[4] = {0u, 0u, 0u, 0u}, bq_[4] = {0u, 0u, 0u, 0u};
-            if (hq) {
+        for (int h = 0; h < 4; ++h) {
+            uint2 ga[4], gb[4], qa[4], qb[4];
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int r = x >> 1;              // 0: first row, 1: second row
-                    const int h0 = 4 * quad + 2 * (x & 1);
-                    const uint16_t *gq = stg[r] + h0 * kLdsStride + 16 * dbk + col;
-                    const uint16_t *qq = stq[r] + h0 * kLdsStride + 16 * dbk + col;
-                    bg_[x] = (uint32_t)gq[0] | ((uint32_t)gq[kLdsStride] << 16);
-                    bq_[x] = (uint32_t)qq[0] | ((uint32_t)qq[kLdsStride] << 16);
-                }
+            for (int x = 0; x < 4; ++x) {
+                const int o = tr_lane + tile_tr_offset(4 * h + x);
+                ga[x] = lds_read_tr(stg[0] + o);
+                gb[x] = lds_read_tr(stg[1] + o);
+                qa[x] = lds_read_tr(stq[0] + o);
+                qb[x] = lds_read_tr(stq[1] + o);
             }
-            adv[dbk] = mfma_16x16x32(A_p, as_bf16x8(make_uint4(bg_[0], bg_[1], bg_[2], bg_[3])),
-                                     adv[dbk]);
-            adk[dbk] = mfma_16x16x32(A_d, as_bf16x8(make_uint4(bq_[0], bq_[1], bq_[2], bq_[3])),
-                                     adk[dbk]);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int dbk = 4 * h + x;
+                adv[dbk] = mfma_16x16x32(
+                    A_p, as_bf16x8(make_uint4(ga[x].x, ga[x].y, gb[x].x, gb[x].y)), adv[dbk]);
+                adk[dbk] = mfma_16x16x32(
+                    A_d, as_bf16x8(make_uint4(qa[x].x, qa[x].y, qb[x].x, qb[x].y)), adk[dbk]);
+            }
         }
         wave_lds_sync();
     };
 
-    const int64_t bt = b * p.nKT + t;
-    for (int lst = 0; lst < 2; ++lst) {
-        const int32_t cnt = lst == 0 ? p.rev_p_cnt[bt] : p.rev_f_cnt[bt];
-        const int32_t *idx = (lst == 0 ? p.rev_p_idx : p.rev_f_idx) + bt * p.nQT;
-        for (int e = 0; e < cnt; ++e) {
-            const int64_t r = idx[e];
-            for (int sub = 0; sub < 2; ++sub) {
-                const int64_t qi_l = r * 128 + sub * 64 + lane;
-                uint32_t m16 = 0;
-                if (qi_l < p.Sq) {
-                    const uint4 mv = *reinterpret_cast<const uint4 *>(
-                        p.memb + (b * p.Sq + qi_l) * p.stride + key0);
-                    const uint32_t w[4] = {mv.x, mv.y, mv.z, mv.w};
+    // One query row: S, dP, then P and dS, staged Q/dO, and the pair flush.
+    auto process = [&](const RowOps &R, uint32_t mask) {
+        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, pd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        const uint32_t v = w[x] & 0x01010101u;
-                        m16 |= ((v | (v >> 7) | (v >> 14) | (v >> 21)) & 0xfu) << (4 * x);
-                    }
-                }
-                uint64_t ball = __ballot(m16 != 0);
-                while (ball) {
-                    const int src = __builtin_ctzll(ball);
-                    ball &= ball - 1;
-                    const int64_t qi = r * 128 + sub * 64 + src;
-                    const uint32_t mask = __shfl(m16, src);
-                    const int64_t qrow = b * p.Sq + qi;
-                    // Q and dO rows of this query as A operands (lane: head col, quad).
-                    bf16x8 qf[8], gf[8];
-                    const bool hv = col < kGroup;
-                    const int64_t qoff =
-                        (qrow * p.Hq + g * kGroup + (hv ? col : 0)) * (int64_t)kD + quad * 64;
-                    const uint4 *qp = reinterpret_cast<const uint4 *>(p.q + qoff);
-                    const uint4 *gp = reinterpret_cast<const uint4 *>(p.dout + qoff);
-                    uint4 *sq = reinterpret_cast<uint4 *>(stq[filled] + col * kLdsStride + quad * 64);
-                    uint4 *sg = reinterpret_cast<uint4 *>(stg[filled] + col * kLdsStride + quad * 64);
-                    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, pd = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < 8; ++s) {
+            sa = mfma_16x16x32(as_bf16x8(R.q[s]), kf[s], sa);
+            pd = mfma_16x16x32(as_bf16x8(R.g[s]), vf[s], pd);
+        }
+        if (hv) {
 #pragma unroll
-                    for (int s = 0; s < 8; ++s) {
-                        const uint4 qv = hv ? qp[s] : zero_u4();
-                        const uint4 gv = hv ? gp[s] : zero_u4();
-                        if (hv) {
-                            sq[s] = qv;
-                            sg[s] = gv;
-                        }
-                        qf[s] = as_bf16x8(qv);
-                        gf[s] = as_bf16x8(gv);
-                    }
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) {
-                        sa = mfma_16x16x32(qf[s], kf[s], sa);
-                        pd = mfma_16x16x32(gf[s], vf[s], pd);
-                    }
-                    // Lane holds S[head 4*quad+e][key col].
-                    const bool kin = (mask >> col) & 1u;
-                    float pn[4], dn[4];
-#pragma unroll
-                    for (int e2 = 0; e2 < 4; ++e2) {
-                        float pr = 0.f, dl = 0.f;
-                        if (hq && kin) {
-                            const int64_t hix = (b * p.Hq + g * kGroup + 4 * quad + e2) * p.Sq + qi;
-                            pr = exp2f(sa[e2] * c - p.lse_in[hix] * 1.4426950408889634f);
-                            dl = p.delta[hix];
-                        }
-                        pn[e2] = pr;
-                        // select, never multiply: an unselected key's dP may be non-finite
-                        dn[e2] = (hq && kin) ? pr * (pd[e2] - dl) : 0.f;
-                    }
-                    if (filled == 0) {
-#pragma unroll
-                        for (int e2 = 0; e2 < 4; ++e2) {
-                            pa[e2] = pn[e2];
-                            da[e2] = dn[e2];
-                        }
-                        filled = 1;
-                    } else {
-                        flush(pn, dn);
-                        filled = 0;
-                    }
-                }
+            for (int s = 0; s < 8; ++s) {
+                tr_store8(stq[filled], col, quad * 64 + 8 * s, R.q[s]);
+                tr_store8(stg[filled], col, quad * 64 + 8 * s, R.g[s]);
             }
         }
+        // Lane holds S[head 4*quad+e][key col].
+        const bool on = hq && ((mask >> col) & 1u);
+        float pn[4], dn[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float pr = on ? exp2f(sa[e] * c - R.lse[e] * 1.4426950408889634f) : 0.f;
+            pn[e] = pr;
+            // select, never multiply: an unselected key's dP may be non-finite
+            dn[e] = on ? pr * (pd[e] - R.dl[e]) : 0.f;
+        }
+        if (filled == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pa[e] = pn[e];
+                da[e] = dn[e];
+            }
+            filled = 1;
+        } else {
+            flush(pn, dn);
+            filled = 0;
+        }
+    };
+
+    // Scan windows: window w covers rows 64*(w%2) .. of the w/2-th query tile
+    // of the reverse lists (partial tiles first, then full tiles).
+    const int64_t bt = b * p.nKT + t;
+    const int32_t cnt_p = p.rev_p_cnt[bt], cnt_f = p.rev_f_cnt[bt];
+    const int32_t *idx_p = p.rev_p_idx + bt * p.nQT, *idx_f = p.rev_f_idx + bt * p.nQT;
+    const int64_t nwin = 2 * (int64_t)(cnt_p + cnt_f);
+    const int64_t mstride = p.stride >> 5;
+    const uint32_t *mrow = p.mbits + (b * p.Sq) * mstride + (key0 >> 5);
+    const int shift = (int)(key0 & 16);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    int64_t w = 0;
+    RowOps R0, R1;
+    while (w < nwin) {
+        // Collect hits, kScanWin windows per step, until a batch is listed.
+        int nh = 0;
+        while (w < nwin && nh < kHitBatch) {
+            uint32_t m[kScanWin];
+            int64_t rbase[kScanWin];
+#pragma unroll
+            for (int x = 0; x < kScanWin; ++x) {
+                const int64_t ww = w + x;
+                m[x] = 0u;
+                rbase[x] = 0;
+                if (ww < nwin) {
+                    const int64_t e = ww >> 1;
+                    const int64_t r = e < cnt_p ? idx_p[e] : idx_f[e - cnt_p];
+                    rbase[x] = r * kTile + (ww & 1) * 64;
+                    const int64_t qi = rbase[x] + lane;
+                    if (qi < p.Sq) m[x] = (mrow[qi * mstride] >> shift) & 0xffffu;
+                }
+            }
+#pragma unroll
+            for (int x = 0; x < kScanWin; ++x) {
+                const uint64_t ball = __ballot(m[x] != 0u);
+                if (m[x] != 0u) {
+                    const int pos = nh + __popcll(ball & below);
+                    hrow[pos] = (int32_t)(rbase[x] + lane);
+                    hmask[pos] = m[x];
+                }
+                nh += __popcll(ball);
+            }
+            w += kScanWin;
+        }
+        wave_lds_sync();
+        // Process the batch in order, the next row's operands in flight.
+        if (nh > 0) load_row(R0, hrow[0]);
+        for (int h = 0; h < nh; h += 2) {
+            if (h + 1 < nh) load_row(R1, hrow[h + 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            process(R0, hmask[h]);
+            if (h + 1 >= nh) break;
+            if (h + 2 < nh) load_row(R0, hrow[h + 2]);
+            __builtin_amdgcn_sched_barrier(0);
+            process(R1, hmask[h + 1]);
+        }
+        wave_lds_sync();
     }
     if (filled) {
         // Second row of the last pair is empty: clear its staged rows.
         const float zero4[4] = {0.f, 0.f, 0.f, 0.f};
-        if (col < kGroup) {
-            uint4 *sq = reinterpret_cast<uint4 *>(stq[1] + col * kLdsStride + quad * 64);
-            uint4 *sg = reinterpret_cast<uint4 *>(stg[1] + col * kLdsStride + quad * 64);
+        if (hv) {
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                sq[s] = zero_u4();
-                sg[s] = zero_u4();
+                tr_store8(stq[1], col, quad * 64 + 8 * s, zero_u4());
+                tr_store8(stg[1], col, quad * 64 + 8 * s, zero_u4());
             }
         }
         flush(zero4, zero4);

@@ -29,6 +29,7 @@ struct Problem {
     const float *out_fp32_in, *lse_in;
     // preprocessing results (workspace or caller buffers)
     uint8_t *memb, *has_routes;
+    uint32_t *mbits;  // bit-packed membership [B*Sq, stride/32] (backward only)
     int32_t *row_keys, *row_cnt;
     int32_t *tile_cnt, *kinds;
     int32_t *fwd_p_cnt, *fwd_p_idx, *fwd_f_cnt, *fwd_f_idx;
@@ -72,6 +73,84 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 }
 
 __device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// ---- buffer loads: out-of-range offsets read as zero, without a branch ----
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // >= every num_records used here
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                            0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// ---- LDS staging for operands that must be read transposed ----
+// A staged block holds 16 rows x 256 bf16 columns. Element (row, d) lives at
+// byte (d/4 >> 4) * kTrRegion + ((d/4) & 15) * 128 + row * 8 + (d % 4) * 2:
+// four consecutive columns of one row are one 8-byte unit, and the 16 rows of
+// a 4-column group are 128 contiguous bytes. One ds_read_tr16_b64 per 16
+// columns x 4 rows then reads 512 contiguous bytes, and a lane's 16-byte
+// chunk of a row is written with two 8-byte stores whose four column regions
+// are 2176 bytes apart (a 128-byte bank shift between neighbouring regions).
+constexpr int kTrRegion = 2176;
+constexpr int kTrBlock = 4 * kTrRegion;  // 8704 bytes per 16-row block
+
+__device__ __forceinline__ int tr_offset(int row, int d4)
+{
+    return (d4 >> 4) * kTrRegion + (d4 & 15) * 128 + row * 8;
+}
+
+// Store 8 consecutive columns d0 .. d0+7 (d0 % 8 == 0) of `row`.
+__device__ __forceinline__ void tr_store8(char *blk, int row, int d0, uint4 v)
+{
+    *reinterpret_cast<uint2 *>(blk + tr_offset(row, d0 >> 2)) = make_uint2(v.x, v.y);
+    *reinterpret_cast<uint2 *>(blk + tr_offset(row, (d0 >> 2) + 1)) = make_uint2(v.z, v.w);
+}
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Transposed read. Within each 16-lane group, lane i names the 8-byte unit
+// R_i; lane j receives R_{j/4 + 4v}[j % 4] for v = 0..3.
+__device__ __forceinline__ uint2 lds_read_tr(const char *p)
+{
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                         (lds_bf16x4 *)(const_cast<char *>(p))));
+}
+
+// For the A/B operand of a 16x16x32 MFMA over the 16 x 256 staged block: lane
+// (col = l % 16, quad = l / 16) gets rows 4*quad .. 4*quad+3 of column
+// 16*db + col. lane_tr_base() is the lane's part of the address.
+__device__ __forceinline__ int lane_tr_base(int col, int quad)
+{
+    return tr_offset(4 * quad + (col >> 2), col & 3);
+}
+__device__ __forceinline__ int tile_tr_offset(int db)
+{
+    return tr_offset(0, 4 * db);
+}
+
+// Blocks are dispatched round-robin over the 8 XCDs (block b runs on XCD
+// b % 8). Map them so that every XCD works on one contiguous range of logical
+// blocks: neighbouring rows or key groups then share that XCD's L2.
+__device__ __forceinline__ int64_t xcd_logical_block(int64_t b, int64_t n)
+{
+    const int64_t x = b & 7, y = b >> 3;
+    const int64_t per = n >> 3, rem = n & 7;
+    return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + y;
+}
+
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 #endif
 
 }  // namespace qsa

@@ -65,6 +65,12 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_rows(Problem p)
         }
     }
 
+    // Bit-packed copy of the row for the key-major backward scan.
+    if (p.mbits) {
+        uint32_t *dst = p.mbits + row * (p.stride >> 5);
+        for (int64_t w = tid; w < nwords; w += kPrepThreads) dst[w] = bm[w];
+    }
+
     // Ascending key list: each thread owns a contiguous run of words.
     const int64_t per = (nwords + kPrepThreads - 1) / kPrepThreads;
     const int64_t w0 = tid * per, w1 = (w0 + per < nwords) ? w0 + per : nwords;
