@@ -120,7 +120,18 @@ def main() -> int:
                     help="workload name or index 1-5 (default: the 32k-token long-context one)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = 1 << 28  # 2^28 fp32 = 1 GiB read + 1 GiB written
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n}), flush=True)
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no cross-GPU sharding in this build)", file=sys.stderr)

@@ -49,6 +49,8 @@ SMALL = [
     dict(seed=33, B=1, Sq=64, Skv=1000, Hq=12, Hkv=1, W=300),
     dict(seed=34, B=3, Sq=17, Skv=5, Hq=12, Hkv=1, W=3),
     dict(seed=35, B=1, Sq=200, Skv=200, Hq=12, Hkv=1, W=200, causal=True),
+    # more query rows than one dK/dV query-range phase holds: accumulators carry over
+    dict(seed=36, B=2, Sq=2300, Skv=200, Hq=24, Hkv=2, W=10),
 ]
 
 

@@ -23,6 +23,8 @@
 //    flight: S = Q K^T and dP = dO V^T per row (M = heads), then, two rows at
 //    a time, dV += P^T dO and dK += dS^T Q with the two rows' heads forming the
 //    32-long contraction. Q and dO rows are staged in LDS and read transposed.
+//    P and dS enter these products (and dS the dQ product) as bf16 high + low
+//    parts, so that sums over thousands of query heads keep FP32-level error.
 //    Blocks are mapped XCD-aware so the waves of one tile column (which read
 //    the same query rows) share an L2.
 #include "common.h"
@@ -147,10 +149,11 @@ __global__ __launch_bounds__(kDqWaves * 64) void k_dq(Problem p)
 #pragma unroll
                 for (int s = 0; s < 8; ++s)
                     tr_store8(ks + kb * kTrBlock, col, quad * 64 + 8 * s, G.k[kb][s]);
-            uint32_t dsb[4];
+            uint32_t dsh[4], dsl[4];
 #pragma unroll
-            for (int x = 0; x < 4; ++x) dsb[x] = pack_bf16x2(ds[2 * x], ds[2 * x + 1]);
-            const bf16x8 dsv = as_bf16x8(make_uint4(dsb[0], dsb[1], dsb[2], dsb[3]));
+            for (int x = 0; x < 4; ++x) split_bf16x2(ds[2 * x], ds[2 * x + 1], dsh[x], dsl[x]);
+            const bf16x8 dsv_hi = as_bf16x8(make_uint4(dsh[0], dsh[1], dsh[2], dsh[3]));
+            const bf16x8 dsv_lo = as_bf16x8(make_uint4(dsl[0], dsl[1], dsl[2], dsl[3]));
             wave_lds_sync();
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
@@ -161,10 +164,11 @@ __global__ __launch_bounds__(kDqWaves * 64) void k_dq(Problem p)
                     a1[x] = lds_read_tr(ks + kTrBlock + tr_lane + tile_tr_offset(4 * h + x));
                 }
 #pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    acc[4 * h + x] = mfma_16x16x32(
-                        as_bf16x8(make_uint4(a0[x].x, a0[x].y, a1[x].x, a1[x].y)), dsv,
-                        acc[4 * h + x]);
+                for (int x = 0; x < 4; ++x) {
+                    const bf16x8 ka = as_bf16x8(make_uint4(a0[x].x, a0[x].y, a1[x].x, a1[x].y));
+                    acc[4 * h + x] = mfma_16x16x32(ka, dsv_hi, acc[4 * h + x]);
+                    acc[4 * h + x] = mfma_16x16x32(ka, dsv_lo, acc[4 * h + x]);
+                }
             }
             wave_lds_sync();
         };
@@ -256,11 +260,13 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
             vf[s] = as_bf16x8(buf_load16(rv, off + 16 * s));
         }
     }
+    // Accumulators: zero in the first query-range phase, else carried over.
     f32x4 adk[16], adv[16];
+    f32x4 *part = reinterpret_cast<f32x4 *>(p.dkdv_part) + item * 2 * 16 * 64 + lane;
 #pragma unroll
     for (int db = 0; db < 16; ++db) {
-        adk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-        adv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        adk[db] = p.phase_first ? f32x4{0.f, 0.f, 0.f, 0.f} : part[db * 64];
+        adv[db] = p.phase_first ? f32x4{0.f, 0.f, 0.f, 0.f} : part[(16 + db) * 64];
     }
     const float c = p.scale * 1.4426950408889634f;
     const bool hq = quad < 3;      // accumulator rows 4*quad+e are real heads
@@ -299,12 +305,19 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
     // Contract the staged pair into dV and dK. Slot j of lane group quad is
     // head 4*quad + (j & 3) of row (j < 4 ? first : second).
     auto flush = [&](const float *pb, const float *db_) {
-        const bf16x8 A_p =
-            as_bf16x8(make_uint4(pack_bf16x2(pa[0], pa[1]), pack_bf16x2(pa[2], pa[3]),
-                                 pack_bf16x2(pb[0], pb[1]), pack_bf16x2(pb[2], pb[3])));
-        const bf16x8 A_d =
-            as_bf16x8(make_uint4(pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3]),
-                                 pack_bf16x2(db_[0], db_[1]), pack_bf16x2(db_[2], db_[3])));
+        uint32_t ph[4], pl[4], dh[4], dl[4];
+        split_bf16x2(pa[0], pa[1], ph[0], pl[0]);
+        split_bf16x2(pa[2], pa[3], ph[1], pl[1]);
+        split_bf16x2(pb[0], pb[1], ph[2], pl[2]);
+        split_bf16x2(pb[2], pb[3], ph[3], pl[3]);
+        split_bf16x2(da[0], da[1], dh[0], dl[0]);
+        split_bf16x2(da[2], da[3], dh[1], dl[1]);
+        split_bf16x2(db_[0], db_[1], dh[2], dl[2]);
+        split_bf16x2(db_[2], db_[3], dh[3], dl[3]);
+        const bf16x8 A_p = as_bf16x8(make_uint4(ph[0], ph[1], ph[2], ph[3]));
+        const bf16x8 A_pl = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
+        const bf16x8 A_d = as_bf16x8(make_uint4(dh[0], dh[1], dh[2], dh[3]));
+        const bf16x8 A_dl = as_bf16x8(make_uint4(dl[0], dl[1], dl[2], dl[3]));
         wave_lds_sync();
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
@@ -320,10 +333,12 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int dbk = 4 * h + x;
-                adv[dbk] = mfma_16x16x32(
-                    A_p, as_bf16x8(make_uint4(ga[x].x, ga[x].y, gb[x].x, gb[x].y)), adv[dbk]);
-                adk[dbk] = mfma_16x16x32(
-                    A_d, as_bf16x8(make_uint4(qa[x].x, qa[x].y, qb[x].x, qb[x].y)), adk[dbk]);
+                const bf16x8 Bg = as_bf16x8(make_uint4(ga[x].x, ga[x].y, gb[x].x, gb[x].y));
+                const bf16x8 Bq = as_bf16x8(make_uint4(qa[x].x, qa[x].y, qb[x].x, qb[x].y));
+                adv[dbk] = mfma_16x16x32(A_p, Bg, adv[dbk]);
+                adv[dbk] = mfma_16x16x32(A_pl, Bg, adv[dbk]);
+                adk[dbk] = mfma_16x16x32(A_d, Bq, adk[dbk]);
+                adk[dbk] = mfma_16x16x32(A_dl, Bq, adk[dbk]);
             }
         }
         wave_lds_sync();
@@ -368,10 +383,26 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
     };
 
     // Scan windows: window w covers rows 64*(w%2) .. of the w/2-th query tile
-    // of the reverse lists (partial tiles first, then full tiles).
+    // of the reverse lists (partial tiles first, then full tiles), restricted
+    // to the query tiles of this phase. The lists are ascending, so the tiles
+    // of the phase form one contiguous run in each.
     const int64_t bt = b * p.nKT + t;
-    const int32_t cnt_p = p.rev_p_cnt[bt], cnt_f = p.rev_f_cnt[bt];
-    const int32_t *idx_p = p.rev_p_idx + bt * p.nQT, *idx_f = p.rev_f_idx + bt * p.nQT;
+    const int32_t r_lo = (int32_t)(p.q_lo / kTile), r_hi = (int32_t)((p.q_hi + kTile - 1) / kTile);
+    auto run = [&](const int32_t *idx, int32_t cnt, int32_t &first) {
+        int32_t below_lo = 0, below_hi = 0;
+        for (int32_t e0 = 0; e0 < cnt; e0 += 64) {
+            const int32_t v = e0 + lane < cnt ? idx[e0 + lane] : 0x7fffffff;
+            below_lo += __popcll(__ballot(v < r_lo));
+            below_hi += __popcll(__ballot(v < r_hi));
+        }
+        first = below_lo;
+        return below_hi - below_lo;
+    };
+    int32_t first_p, first_f;
+    const int32_t cnt_p = run(p.rev_p_idx + bt * p.nQT, p.rev_p_cnt[bt], first_p);
+    const int32_t cnt_f = run(p.rev_f_idx + bt * p.nQT, p.rev_f_cnt[bt], first_f);
+    const int32_t *idx_p = p.rev_p_idx + bt * p.nQT + first_p;
+    const int32_t *idx_f = p.rev_f_idx + bt * p.nQT + first_f;
     const int64_t nwin = 2 * (int64_t)(cnt_p + cnt_f);
     const int64_t mstride = p.stride >> 5;
     const uint32_t *mrow = p.mbits + (b * p.Sq) * mstride + (key0 >> 5);
@@ -396,7 +427,8 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
                     const int64_t r = e < cnt_p ? idx_p[e] : idx_f[e - cnt_p];
                     rbase[x] = r * kTile + (ww & 1) * 64;
                     const int64_t qi = rbase[x] + lane;
-                    if (qi < p.Sq) m[x] = (mrow[qi * mstride] >> shift) & 0xffffu;
+                    if (qi < p.q_hi && qi >= p.q_lo)
+                        m[x] = (mrow[qi * mstride] >> shift) & 0xffffu;
                 }
             }
 #pragma unroll
@@ -438,6 +470,14 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
         flush(zero4, zero4);
     }
 
+    if (!p.phase_last) {
+#pragma unroll
+        for (int db = 0; db < 16; ++db) {
+            part[db * 64] = adk[db];
+            part[(16 + db) * 64] = adv[db];
+        }
+        return;
+    }
     // Lane holds dK/dV[key 4*quad+e][d 16*db + col].
 #pragma unroll
     for (int e2 = 0; e2 < 4; ++e2) {
@@ -470,12 +510,22 @@ hipError_t launch_dq(const Problem &p, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_dkdv(const Problem &p, hipStream_t s)
+hipError_t launch_dkdv(const Problem &p0, hipStream_t s)
 {
-    const int64_t groups = p.B * p.Hkv * (p.stride >> 4);
-    hipLaunchKernelGGL(k_dkdv, dim3((unsigned)((groups + kKvWaves - 1) / kKvWaves)),
-                       dim3(kKvWaves * 64), 0, s, p);
-    return hipGetLastError();
+    const int64_t groups = p0.B * p0.Hkv * (p0.stride >> 4);
+    const int64_t phases = (p0.Sq + kDkdvPhaseRows - 1) / kDkdvPhaseRows;
+    for (int64_t ph = 0; ph < phases; ++ph) {
+        Problem p = p0;
+        p.q_lo = ph * kDkdvPhaseRows;
+        p.q_hi = (ph + 1 == phases) ? p0.Sq : (ph + 1) * kDkdvPhaseRows;
+        p.phase_first = ph == 0;
+        p.phase_last = ph + 1 == phases;
+        hipLaunchKernelGGL(k_dkdv, dim3((unsigned)((groups + kKvWaves - 1) / kKvWaves)),
+                           dim3(kKvWaves * 64), 0, s, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace qsa

@@ -40,7 +40,16 @@ struct Problem {
     // backward
     float *delta;
     uint16_t *dq, *dk, *dv;
+    // dK/dV runs in query-range phases [q_lo, q_hi); FP32 accumulators carry
+    // over between phases through dkdv_part.
+    float *dkdv_part;
+    int64_t q_lo, q_hi;
+    int32_t phase_first, phase_last;
 };
+
+// Query rows per dK/dV phase: their Q and dO (12 KB per row and KV head) stay
+// resident in the last-level caches while every wave walks the same window.
+constexpr int64_t kDkdvPhaseRows = int64_t(1) << 40;
 
 hipError_t launch_preprocess(const Problem &p, hipStream_t s);
 hipError_t launch_forward(const Problem &p, hipStream_t s);
@@ -73,6 +82,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 }
 
 __device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): a bf16 MFMA fed with
+// both parts keeps about 16 mantissa bits of an FP32 operand.
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t &hi, uint32_t &lo)
+{
+    const uint16_t ha = f32_to_bf16(a), hb = f32_to_bf16(b);
+    hi = (uint32_t)ha | ((uint32_t)hb << 16);
+    lo = pack_bf16x2(a - bf16_to_f32(ha), b - bf16_to_f32(hb));
+}
 
 // ---- buffer loads: out-of-range offsets read as zero, without a branch ----
 typedef __amdgpu_buffer_rsrc_t rsrc_t;

@@ -170,11 +170,7 @@ __global__ __launch_bounds__(kFwdWaves * 64) void k_forward(Problem p)
         // 16+4*quad+j-4 (j>=4): the lane's own accumulator values.
         uint32_t hi[4], lo[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const uint16_t h0 = f32_to_bf16(pr[2 * x]), h1 = f32_to_bf16(pr[2 * x + 1]);
-            hi[x] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            lo[x] = pack_bf16x2(pr[2 * x] - bf16_to_f32(h0), pr[2 * x + 1] - bf16_to_f32(h1));
-        }
+        for (int x = 0; x < 4; ++x) split_bf16x2(pr[2 * x], pr[2 * x + 1], hi[x], lo[x]);
         const bf16x8 pb_hi = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
         const bf16x8 pb_lo = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
         wave_lds_sync();
