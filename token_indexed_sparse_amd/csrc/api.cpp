@@ -42,7 +42,7 @@ qsa_status check_dims(const qsa_dims *d)
 
 struct Layout {
     size_t memb, has, mbits, row_keys, row_cnt, tile_cnt, kinds, fpc, fpi, ffc, ffi, rpc, rpi, rfc,
-        rfi, delta, dkdv_part, total;
+        rfi, delta, total;
 };
 
 // which: 0 forward, 1 backward, 2 preprocess (only tile counts and, if the
@@ -81,11 +81,6 @@ Layout layout(const qsa_dims *d, int which)
         L.rfi = take((size_t)(d->B * nKT * nQT) * 4);
     }
     L.delta = which == 1 ? take((size_t)(d->B * d->Hq * d->Sq) * 4) : none;
-    // FP32 dK and dV accumulators per 16-key group, only when dK/dV needs
-    // more than one query-range phase.
-    L.dkdv_part = (which == 1 && d->Sq > kDkdvPhaseRows)
-                      ? take((size_t)(d->B * d->Hkv * stride) * kD * 2 * 4)
-                      : none;
     L.total = off;
     return L;
 }
@@ -154,7 +149,6 @@ void carve(Problem &p, const Layout &L, void *ws)
         p.rev_f_idx = reinterpret_cast<int32_t *>(w + L.rfi);
     }
     if (L.delta != none) p.delta = reinterpret_cast<float *>(w + L.delta);
-    if (L.dkdv_part != none) p.dkdv_part = reinterpret_cast<float *>(w + L.dkdv_part);
 }
 
 qsa_status check_scale(float scale)

@@ -16,17 +16,18 @@
 //  * k_dkdv: key-major. One wave owns 16 consecutive keys of one KV head and
 //    keeps their K and V rows in registers and their dK, dV accumulators for
 //    the whole run. It walks the reverse tile lists of its 128-key tile column
-//    (partial tiles, then full tiles), reads a 16-bit slice of the bit-packed
+//    from the last query tile down, reads a 16-bit slice of the bit-packed
 //    membership row of every query in those tiles, and collects the rows that
-//    select one of its keys into an LDS list (ascending). Rows are then
-//    processed in that order with the next row's Q, dO, lse and delta loads in
+//    select one of its keys into an LDS list (descending). Rows are then
+//    processed in that order with two rows' Q, dO, lse and delta loads in
 //    flight: S = Q K^T and dP = dO V^T per row (M = heads), then, two rows at
 //    a time, dV += P^T dO and dK += dS^T Q with the two rows' heads forming the
 //    32-long contraction. Q and dO rows are staged in LDS and read transposed.
 //    P and dS enter these products (and dS the dQ product) as bf16 high + low
 //    parts, so that sums over thousands of query heads keep FP32-level error.
-//    Blocks are mapped XCD-aware so the waves of one tile column (which read
-//    the same query rows) share an L2.
+//    The descending sweep keeps every wave near the same query rows (random
+//    selections have one density per query position), and blocks are mapped
+//    XCD-aware so neighbouring key groups share an L2.
 #include "common.h"
 
 namespace qsa {
@@ -207,9 +208,9 @@ __global__ __launch_bounds__(kDqWaves * 64) void k_dq(Problem p)
 
 // ---------------------------------------------------------------- dK, dV
 constexpr int kKvWaves = 2;
-constexpr int kHitCap = 320;   // LDS hit list capacity per wave
-constexpr int kHitBatch = 64;  // stop scanning once this many hits are listed
-constexpr int kScanWin = 4;    // 64-row windows scanned per step
+constexpr int kHitCap = 448;    // LDS hit list capacity per wave
+constexpr int kHitBatch = 192;  // stop scanning once this many hits are listed
+constexpr int kScanWin = 4;     // 64-row windows scanned per step
 
 struct RowOps {
     uint4 q[8], g[8];
@@ -260,13 +261,11 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
             vf[s] = as_bf16x8(buf_load16(rv, off + 16 * s));
         }
     }
-    // Accumulators: zero in the first query-range phase, else carried over.
     f32x4 adk[16], adv[16];
-    f32x4 *part = reinterpret_cast<f32x4 *>(p.dkdv_part) + item * 2 * 16 * 64 + lane;
 #pragma unroll
     for (int db = 0; db < 16; ++db) {
-        adk[db] = p.phase_first ? f32x4{0.f, 0.f, 0.f, 0.f} : part[db * 64];
-        adv[db] = p.phase_first ? f32x4{0.f, 0.f, 0.f, 0.f} : part[(16 + db) * 64];
+        adk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        adv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const float c = p.scale * 1.4426950408889634f;
     const bool hq = quad < 3;      // accumulator rows 4*quad+e are real heads
@@ -320,19 +319,19 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
         const bf16x8 A_dl = as_bf16x8(make_uint4(dl[0], dl[1], dl[2], dl[3]));
         wave_lds_sync();
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            uint2 ga[4], gb[4], qa[4], qb[4];
+        for (int h = 0; h < 8; ++h) {
+            uint2 ga[2], gb[2], qa[2], qb[2];
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int o = tr_lane + tile_tr_offset(4 * h + x);
+            for (int x = 0; x < 2; ++x) {
+                const int o = tr_lane + tile_tr_offset(2 * h + x);
                 ga[x] = lds_read_tr(stg[0] + o);
                 gb[x] = lds_read_tr(stg[1] + o);
                 qa[x] = lds_read_tr(stq[0] + o);
                 qb[x] = lds_read_tr(stq[1] + o);
             }
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int dbk = 4 * h + x;
+            for (int x = 0; x < 2; ++x) {
+                const int dbk = 2 * h + x;
                 const bf16x8 Bg = as_bf16x8(make_uint4(ga[x].x, ga[x].y, gb[x].x, gb[x].y));
                 const bf16x8 Bq = as_bf16x8(make_uint4(qa[x].x, qa[x].y, qb[x].x, qb[x].y));
                 adv[dbk] = mfma_16x16x32(A_p, Bg, adv[dbk]);
@@ -382,35 +381,25 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
         }
     };
 
-    // Scan windows: window w covers rows 64*(w%2) .. of the w/2-th query tile
-    // of the reverse lists (partial tiles first, then full tiles), restricted
-    // to the query tiles of this phase. The lists are ascending, so the tiles
-    // of the phase form one contiguous run in each.
+    // Hits are visited in DESCENDING query order: random selections have the
+    // same density for every key group at a given query position, so all waves
+    // sweep the query range from the top at about the same rate and the rows
+    // they read stay in the caches. Window w (counted from the top) covers
+    // rows 64*(w%2) .. of the reverse-list query tiles (full tiles, then
+    // partial tiles, both from their last entry down).
     const int64_t bt = b * p.nKT + t;
-    const int32_t r_lo = (int32_t)(p.q_lo / kTile), r_hi = (int32_t)((p.q_hi + kTile - 1) / kTile);
-    auto run = [&](const int32_t *idx, int32_t cnt, int32_t &first) {
-        int32_t below_lo = 0, below_hi = 0;
-        for (int32_t e0 = 0; e0 < cnt; e0 += 64) {
-            const int32_t v = e0 + lane < cnt ? idx[e0 + lane] : 0x7fffffff;
-            below_lo += __popcll(__ballot(v < r_lo));
-            below_hi += __popcll(__ballot(v < r_hi));
-        }
-        first = below_lo;
-        return below_hi - below_lo;
-    };
-    int32_t first_p, first_f;
-    const int32_t cnt_p = run(p.rev_p_idx + bt * p.nQT, p.rev_p_cnt[bt], first_p);
-    const int32_t cnt_f = run(p.rev_f_idx + bt * p.nQT, p.rev_f_cnt[bt], first_f);
-    const int32_t *idx_p = p.rev_p_idx + bt * p.nQT + first_p;
-    const int32_t *idx_f = p.rev_f_idx + bt * p.nQT + first_f;
-    const int64_t nwin = 2 * (int64_t)(cnt_p + cnt_f);
+    const int32_t cnt_p = p.rev_p_cnt[bt], cnt_f = p.rev_f_cnt[bt];
+    const int32_t *idx_p = p.rev_p_idx + bt * p.nQT, *idx_f = p.rev_f_idx + bt * p.nQT;
+    const int64_t nwin = 2 * ((int64_t)cnt_p + cnt_f);
     const int64_t mstride = p.stride >> 5;
     const uint32_t *mrow = p.mbits + (b * p.Sq) * mstride + (key0 >> 5);
     const int shift = (int)(key0 & 16);
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const uint64_t above = (lane == 63) ? 0ull : (~0ull << (lane + 1));
 
     int64_t w = 0;
-    RowOps R0, R1;
+    int32_t ip = cnt_p - 1, jf = cnt_f - 1;  // cursors merging both lists from the top
+    int32_t cur_tile = -1;
+    RowOps R0, R1, R2;
     while (w < nwin) {
         // Collect hits, kScanWin windows per step, until a batch is listed.
         int nh = 0;
@@ -419,23 +408,31 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
             int64_t rbase[kScanWin];
 #pragma unroll
             for (int x = 0; x < kScanWin; ++x) {
-                const int64_t ww = w + x;
                 m[x] = 0u;
                 rbase[x] = 0;
-                if (ww < nwin) {
-                    const int64_t e = ww >> 1;
-                    const int64_t r = e < cnt_p ? idx_p[e] : idx_f[e - cnt_p];
-                    rbase[x] = r * kTile + (ww & 1) * 64;
+                if (w + x < nwin) {
+                    if (((w + x) & 1) == 0) {
+                        // next tile from the top of the merged lists
+                        const int32_t vp = ip >= 0 ? idx_p[ip] : -1;
+                        const int32_t vf = jf >= 0 ? idx_f[jf] : -1;
+                        if (vp > vf) {
+                            cur_tile = vp;
+                            --ip;
+                        } else {
+                            cur_tile = vf;
+                            --jf;
+                        }
+                    }
+                    rbase[x] = (int64_t)cur_tile * kTile + (((w + x) & 1) ? 0 : 64);
                     const int64_t qi = rbase[x] + lane;
-                    if (qi < p.q_hi && qi >= p.q_lo)
-                        m[x] = (mrow[qi * mstride] >> shift) & 0xffffu;
+                    if (qi < p.Sq) m[x] = (mrow[qi * mstride] >> shift) & 0xffffu;
                 }
             }
 #pragma unroll
             for (int x = 0; x < kScanWin; ++x) {
                 const uint64_t ball = __ballot(m[x] != 0u);
                 if (m[x] != 0u) {
-                    const int pos = nh + __popcll(ball & below);
+                    const int pos = nh + __popcll(ball & above);
                     hrow[pos] = (int32_t)(rbase[x] + lane);
                     hmask[pos] = m[x];
                 }
@@ -444,16 +441,21 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
             w += kScanWin;
         }
         wave_lds_sync();
-        // Process the batch in order, the next row's operands in flight.
+        // Process the batch in order, two rows' operands in flight.
         if (nh > 0) load_row(R0, hrow[0]);
-        for (int h = 0; h < nh; h += 2) {
-            if (h + 1 < nh) load_row(R1, hrow[h + 1]);
+        if (nh > 1) load_row(R1, hrow[1]);
+        for (int h = 0; h < nh; h += 3) {
+            if (h + 2 < nh) load_row(R2, hrow[h + 2]);
             __builtin_amdgcn_sched_barrier(0);
             process(R0, hmask[h]);
             if (h + 1 >= nh) break;
-            if (h + 2 < nh) load_row(R0, hrow[h + 2]);
+            if (h + 3 < nh) load_row(R0, hrow[h + 3]);
             __builtin_amdgcn_sched_barrier(0);
             process(R1, hmask[h + 1]);
+            if (h + 2 >= nh) break;
+            if (h + 4 < nh) load_row(R1, hrow[h + 4]);
+            __builtin_amdgcn_sched_barrier(0);
+            process(R2, hmask[h + 2]);
         }
         wave_lds_sync();
     }
@@ -470,14 +472,6 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
         flush(zero4, zero4);
     }
 
-    if (!p.phase_last) {
-#pragma unroll
-        for (int db = 0; db < 16; ++db) {
-            part[db * 64] = adk[db];
-            part[(16 + db) * 64] = adv[db];
-        }
-        return;
-    }
     // Lane holds dK/dV[key 4*quad+e][d 16*db + col].
 #pragma unroll
     for (int e2 = 0; e2 < 4; ++e2) {
@@ -510,22 +504,12 @@ hipError_t launch_dq(const Problem &p, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_dkdv(const Problem &p0, hipStream_t s)
+hipError_t launch_dkdv(const Problem &p, hipStream_t s)
 {
-    const int64_t groups = p0.B * p0.Hkv * (p0.stride >> 4);
-    const int64_t phases = (p0.Sq + kDkdvPhaseRows - 1) / kDkdvPhaseRows;
-    for (int64_t ph = 0; ph < phases; ++ph) {
-        Problem p = p0;
-        p.q_lo = ph * kDkdvPhaseRows;
-        p.q_hi = (ph + 1 == phases) ? p0.Sq : (ph + 1) * kDkdvPhaseRows;
-        p.phase_first = ph == 0;
-        p.phase_last = ph + 1 == phases;
-        hipLaunchKernelGGL(k_dkdv, dim3((unsigned)((groups + kKvWaves - 1) / kKvWaves)),
-                           dim3(kKvWaves * 64), 0, s, p);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    const int64_t groups = p.B * p.Hkv * (p.stride >> 4);
+    hipLaunchKernelGGL(k_dkdv, dim3((unsigned)((groups + kKvWaves - 1) / kKvWaves)),
+                       dim3(kKvWaves * 64), 0, s, p);
+    return hipGetLastError();
 }
 
 }  // namespace qsa

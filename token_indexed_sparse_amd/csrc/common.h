@@ -40,16 +40,7 @@ struct Problem {
     // backward
     float *delta;
     uint16_t *dq, *dk, *dv;
-    // dK/dV runs in query-range phases [q_lo, q_hi); FP32 accumulators carry
-    // over between phases through dkdv_part.
-    float *dkdv_part;
-    int64_t q_lo, q_hi;
-    int32_t phase_first, phase_last;
 };
-
-// Query rows per dK/dV phase: their Q and dO (12 KB per row and KV head) stay
-// resident in the last-level caches while every wave walks the same window.
-constexpr int64_t kDkdvPhaseRows = int64_t(1) << 40;
 
 hipError_t launch_preprocess(const Problem &p, hipStream_t s);
 hipError_t launch_forward(const Problem &p, hipStream_t s);
