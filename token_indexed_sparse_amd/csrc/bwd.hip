@@ -227,8 +227,10 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int col = lane & 15, quad = lane >> 4;
     const int64_t ngroups = p.stride >> 4;
-    // item = (b * Hkv + g) * ngroups + kg
-    const int64_t item = xcd_logical_block(blockIdx.x, gridDim.x) * kKvWaves + wave;
+    // item = (b * Hkv + g) * ngroups + kg. Blocks go to the XCDs round-robin,
+    // so the key groups at the start of a causal range, which every later row
+    // can select and which carry the most hits, are spread over all XCDs.
+    const int64_t item = (int64_t)blockIdx.x * kKvWaves + wave;
     if (item >= p.B * p.Hkv * ngroups) return;
     const int64_t kg = item % ngroups;
     const int64_t bg = item / ngroups;

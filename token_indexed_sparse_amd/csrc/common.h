@@ -58,19 +58,18 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// Round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// Two FP32 values to packed bf16 in one instruction (gfx950's packed convert):
+// round to nearest even, NaN stays NaN. `lo` lands in bits 0..15.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)pack_bf16x2(f, 0.0f); }
 
 __device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
 
@@ -78,9 +77,8 @@ __device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); 
 // both parts keeps about 16 mantissa bits of an FP32 operand.
 __device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t &hi, uint32_t &lo)
 {
-    const uint16_t ha = f32_to_bf16(a), hb = f32_to_bf16(b);
-    hi = (uint32_t)ha | ((uint32_t)hb << 16);
-    lo = pack_bf16x2(a - bf16_to_f32(ha), b - bf16_to_f32(hb));
+    hi = pack_bf16x2(a, b);
+    lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
 // ---- buffer loads: out-of-range offsets read as zero, without a branch ----
