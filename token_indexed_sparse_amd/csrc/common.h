@@ -142,6 +142,62 @@ __device__ __forceinline__ int tile_tr_offset(int db)
     return tr_offset(0, 4 * db);
 }
 
+// ---- gathered rows staged in LDS by direct-to-LDS buffer loads ----
+// One dma16() moves 64 lanes x 16 bytes; lane l's bytes land at lds + 16 l.
+// A gather instruction therefore covers two 512-byte rows: every group of
+// consecutive lanes reads consecutive memory, which the vector memory path
+// serves far faster than a lane-per-row pattern.
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ void dma16(rsrc_t r, lds_char *lds, uint32_t off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, off, 0, 0, 0);
+}
+
+// Row j of a staged region occupies bytes [512 j, 512 j + 512); its 16-byte
+// chunk c (elements 8c .. 8c+7) sits at slot c ^ swz_mask(j). The mask takes
+// 16 distinct values over 16 consecutive rows, so 16 lanes reading the same
+// chunk of 16 rows hit distinct banks; and rows 4q .. 4q+3 differ in mask bits
+// 1..3, so a transposed read of 32-byte column pairs of 4 rows is
+// conflict-free as well.
+__device__ __forceinline__ int swz_mask(int row)
+{
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+}
+__device__ __forceinline__ int swz(int row, int chunk)
+{
+    return row * 512 + ((chunk ^ swz_mask(row)) << 4);
+}
+
+// Lane l of gather instruction s stages row 2s + (l >> 5) at LDS slot l & 31;
+// the chunk it fetches so that the region holds the swizzled layout.
+__device__ __forceinline__ int dma_chunk(int lane, int s)
+{
+    return (lane & 31) ^ swz_mask(2 * s + (lane >> 5));
+}
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+__device__ __forceinline__ uint4 lds_read16(const lds_char *p)
+{
+    return __builtin_bit_cast(uint4, *reinterpret_cast<const lds_u32x4 *>(p));
+}
+
+__device__ __forceinline__ uint2 lds_read_tr(const lds_char *p)
+{
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                         (lds_bf16x4 *)(const_cast<lds_char *>(p))));
+}
+
+// Explicit waits for direct-to-LDS loads, which produce no register the
+// compiler could track. The s_waitcnt immediate of this architecture holds
+// vmcnt in bits 3..0 and 15..14, expcnt in 6..4 and lgkmcnt in 11..8; a
+// field at its maximum does not wait. QSA_WAIT_VM(n): at most n vector memory
+// operations stay in flight. QSA_WAIT_LDS(): every LDS operation has finished.
+#define QSA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
+#define QSA_WAIT_LDS() __builtin_amdgcn_s_waitcnt(0xC07F)
+
 // Blocks are dispatched round-robin over the 8 XCDs (block b runs on XCD
 // b % 8). Map them so that every XCD works on one contiguous range of logical
 // blocks: neighbouring rows or key groups then share that XCD's L2.
