@@ -9,10 +9,12 @@
 // Three kernels, no floating-point atomics anywhere:
 //  * k_delta: one wave per (row, head) reduces dO . out_fp32.
 //  * k_dq: query-major like the forward (one wave per row and KV head walks
-//    the row's sorted key list in 32-slot chunks, next chunk's gathers in
-//    flight). S^T and dP^T come from the gathered K and V rows straight into
-//    the matrix core; dS^T stays in the accumulator layout and is the B
-//    operand of dQ^T = K^T dS^T, with K staged in LDS and read transposed.
+//    the row's sorted key list in 32-slot chunks; each chunk's K and V rows
+//    are gathered straight into LDS by direct-to-LDS loads, read out, and the
+//    next chunk's gathers fly while this chunk is computed). S^T = K Q^T and
+//    dP^T = V dO^T take K and V in the row layout; dS^T stays in the
+//    accumulator layout and is the B operand of dQ^T = K^T dS^T, whose K^T
+//    operand is the transposed read of the same staged K rows.
 //  * k_dkdv: key-major. One wave owns 16 consecutive keys of one KV head and
 //    keeps their K and V rows in registers and their dK, dV accumulators for
 //    the whole run. It walks the reverse tile lists of its 128-key tile column
@@ -54,20 +56,15 @@ __global__ __launch_bounds__(256) void k_delta(Problem p)
 }
 
 // ---------------------------------------------------------------- dQ
-constexpr int kDqWaves = 4;
-constexpr int kChunk = 32;
+constexpr int kChunk = 32;  // key slots per step
 
-struct Gather {
-    uint4 k[2][8];
-    uint4 v[2][8];
-};
-
-__global__ __launch_bounds__(kDqWaves * 64) void k_dq(Problem p)
+// Body of k_dq; ks and vs are the wave's K and V staging regions (32 rows of
+// 512 bytes each, swizzled as described with swz()).
+__device__ __forceinline__ void dq_row(const Problem &p, lds_char *ks, lds_char *vs)
 {
-    __shared__ __attribute__((aligned(16))) char ks_all[kDqWaves][2 * kTrBlock];
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int lane = threadIdx.x;
     const int col = lane & 15, quad = lane >> 4;
-    const int64_t item = xcd_logical_block(blockIdx.x, gridDim.x) * kDqWaves + wave;
+    const int64_t item = xcd_logical_block(blockIdx.x, gridDim.x);
     if (item >= p.B * p.Sq * p.Hkv) return;
     const int64_t row = item / p.Hkv;
     const int g = (int)(item - row * p.Hkv);
@@ -75,7 +72,6 @@ __global__ __launch_bounds__(kDqWaves * 64) void k_dq(Problem p)
     const int head = g * kGroup + col;
     const bool hv = col < kGroup;
     const int n = p.row_cnt[row];
-    char *ks = ks_all[wave];
     uint16_t *dqp = p.dq + (row * p.Hq + head) * (int64_t)kD;
 
     f32x4 acc[16];
@@ -87,113 +83,119 @@ __global__ __launch_bounds__(kDqWaves * 64) void k_dq(Problem p)
         const uint32_t kv_bytes = (uint32_t)((p.Skv - 1) * p.Hkv * kD * 2 + kD * 2);
         const rsrc_t rk = make_rsrc(p.k + (b * p.Skv * p.Hkv + g) * (int64_t)kD, kv_bytes);
         const rsrc_t rv = make_rsrc(p.v + (b * p.Skv * p.Hkv + g) * (int64_t)kD, kv_bytes);
+        // Q and dO as B operands: lane (head col, quad) holds columns
+        // 32t + 8quad .. +7 for step t.
         bf16x8 qf[8], gf[8];
+        float lse2 = 0.f, dlt = 0.f;
         {
             const int64_t rbase = (row * p.Hq + g * kGroup) * (int64_t)kD;
             const rsrc_t rq = make_rsrc(p.q + rbase, (uint32_t)(kGroup * kD * 2));
             const rsrc_t rg = make_rsrc(p.dout + rbase, (uint32_t)(kGroup * kD * 2));
-            const uint32_t off = hv ? (uint32_t)(col * kD * 2 + quad * 128) : kOutOfRange;
+            const uint32_t off = hv ? (uint32_t)(col * kD * 2 + quad * 16) : kOutOfRange;
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                qf[s] = as_bf16x8(buf_load16(rq, off + 16 * s));
-                gf[s] = as_bf16x8(buf_load16(rg, off + 16 * s));
+            for (int t = 0; t < 8; ++t) {
+                qf[t] = as_bf16x8(buf_load16(rq, off + 64 * t));
+                gf[t] = as_bf16x8(buf_load16(rg, off + 64 * t));
             }
+            if (hv) {
+                lse2 = p.lse_in[(b * p.Hq + head) * p.Sq + i] * 1.4426950408889634f;
+                dlt = p.delta[(b * p.Hq + head) * p.Sq + i];
+            }
+            QSA_WAIT_VM(0);  // the counted waits below are then the only ones
         }
-        const float lse2 = hv ? p.lse_in[(b * p.Hq + head) * p.Sq + i] * 1.4426950408889634f : 0.f;
-        const float dlt = hv ? p.delta[(b * p.Hq + head) * p.Sq + i] : 0.f;
         const float c = p.scale * 1.4426950408889634f;
         const rsrc_t rkeys = make_rsrc(p.row_keys + row * p.W, (uint32_t)(p.W * 4));
-        auto fetch_keys = [&](int c0, int (&kk)[2]) {
+        auto fetch_key = [&](int ch) -> int {
+            const int slot = ch * kChunk + (lane & 31);
+            const int kk = (int)__builtin_amdgcn_raw_buffer_load_b32(
+                rkeys, slot < n ? (uint32_t)slot * 4 : kOutOfRange, 0, 0);
+            return slot < n ? kk : -1;
+        };
+        auto offsets = [&](int kk, uint32_t (&off)[16]) {
+            const uint32_t mine = kk >= 0 ? (uint32_t)kk * row_bytes : kOutOfRange;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const int slot = c0 + kb * 16 + col;
-                kk[kb] = (int)__builtin_amdgcn_raw_buffer_load_b32(
-                    rkeys, slot < n ? (uint32_t)slot * 4 : kOutOfRange, 0, 0);
-                kk[kb] = slot < n ? kk[kb] : -1;
+            for (int s = 0; s < 16; ++s) {
+                const uint32_t e = __builtin_amdgcn_readlane(mine, 2 * s);
+                const uint32_t o = __builtin_amdgcn_readlane(mine, 2 * s + 1);
+                off[s] = ((lane >> 5) ? o : e) + ((uint32_t)dma_chunk(lane, s) << 4);
             }
         };
-        auto offsets = [&](const int (&kk)[2], uint32_t (&off)[2]) {
+        auto gather = [&](rsrc_t r, lds_char *dst, const uint32_t (&off)[16]) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                off[kb] = kk[kb] >= 0 ? (uint32_t)kk[kb] * row_bytes + quad * 128 : kOutOfRange;
+            for (int s = 0; s < 16; ++s) dma16(r, dst + s * 1024, off[s]);
         };
-        auto issue = [&](Gather &G, const uint32_t (&off)[2]) {
+        // Row-layout reads (A operands of S^T = K Q^T and dP^T = V dO^T) and
+        // the transposed read of K (A operand of dQ^T = K^T dS^T), as in the
+        // forward's K and V reads.
+        const int kmask = swz_mask(col);
+        const int tkey = 4 * quad + (col >> 2);
+        const int tm = swz_mask(tkey);
+        const int tbase = tkey * 512 + ((((col >> 1) & 1) ^ (tm & 1)) << 4) + (col & 1) * 8;
+        const int txor = tm >> 1;
+
+        const int nchunks = (n + kChunk - 1) / kChunk;
+        int knext = fetch_key(1);
+        uint32_t off[16];
+        offsets(fetch_key(0), off);
+        gather(rk, ks, off);
+        gather(rv, vs, off);
+        for (int ch = 0; ch < nchunks; ++ch) {
+            // Read the whole chunk out of LDS, then gather the next one (the
+            // compiler orders LDS reads after all earlier direct-to-LDS loads).
+            QSA_WAIT_VM(0);
+            offsets(knext, off);
+            knext = fetch_key(ch + 2);
+            uint4 kr[2][8], vr[2][8];
+            uint2 kt[2][16];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    G.k[kb][s] = buf_load16(rk, off[kb] + 16 * s);
-                    G.v[kb][s] = buf_load16(rv, off[kb] + 16 * s);
+                for (int t = 0; t < 8; ++t) {
+                    const int o = (kb * 16 + col) * 512 + (((4 * t + quad) ^ kmask) << 4);
+                    kr[kb][t] = lds_read16(ks + o);
+                    vr[kb][t] = lds_read16(vs + o);
                 }
-        };
-        const int tr_lane = lane_tr_base(col, quad);
-        auto compute = [&](const Gather &G, int c0) {
+#pragma unroll
+            for (int db = 0; db < 16; ++db) {
+                const int o = tbase + ((db ^ txor) << 5);
+                kt[0][db] = lds_read_tr(ks + o);
+                kt[1][db] = lds_read_tr(ks + o + 16 * 512);
+            }
+            QSA_WAIT_LDS();
+            gather(rk, ks, off);
+            gather(rv, vs, off);
+
             float ds[8];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 f32x4 sa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    sa = mfma_16x16x32(as_bf16x8(G.k[kb][s]), qf[s], sa);
-                    pa = mfma_16x16x32(as_bf16x8(G.v[kb][s]), gf[s], pa);
+                for (int t = 0; t < 8; ++t) {
+                    sa = mfma_16x16x32(as_bf16x8(kr[kb][t]), qf[t], sa);
+                    pa = mfma_16x16x32(as_bf16x8(vr[kb][t]), gf[t], pa);
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const bool valid = hv && (c0 + kb * 16 + 4 * quad + e < n);
+                    const bool valid = hv && (ch * kChunk + kb * 16 + 4 * quad + e < n);
                     const float pr = valid ? exp2f(sa[e] * c - lse2) : 0.f;
                     // select, never multiply: a padding slot's dP is not used
                     ds[kb * 4 + e] = valid ? pr * (pa[e] - dlt) : 0.f;
                 }
             }
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int s = 0; s < 8; ++s)
-                    tr_store8(ks + kb * kTrBlock, col, quad * 64 + 8 * s, G.k[kb][s]);
             uint32_t dsh[4], dsl[4];
 #pragma unroll
             for (int x = 0; x < 4; ++x) split_bf16x2(ds[2 * x], ds[2 * x + 1], dsh[x], dsl[x]);
             const bf16x8 dsv_hi = as_bf16x8(make_uint4(dsh[0], dsh[1], dsh[2], dsh[3]));
             const bf16x8 dsv_lo = as_bf16x8(make_uint4(dsl[0], dsl[1], dsl[2], dsl[3]));
-            wave_lds_sync();
 #pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                uint2 a0[4], a1[4];
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    a0[x] = lds_read_tr(ks + tr_lane + tile_tr_offset(4 * h + x));
-                    a1[x] = lds_read_tr(ks + kTrBlock + tr_lane + tile_tr_offset(4 * h + x));
-                }
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const bf16x8 ka = as_bf16x8(make_uint4(a0[x].x, a0[x].y, a1[x].x, a1[x].y));
-                    acc[4 * h + x] = mfma_16x16x32(ka, dsv_hi, acc[4 * h + x]);
-                    acc[4 * h + x] = mfma_16x16x32(ka, dsv_lo, acc[4 * h + x]);
-                }
+            for (int db = 0; db < 16; ++db) {
+                const bf16x8 ka =
+                    as_bf16x8(make_uint4(kt[0][db].x, kt[0][db].y, kt[1][db].x, kt[1][db].y));
+                acc[db] = mfma_16x16x32(ka, dsv_hi, acc[db]);
+                acc[db] = mfma_16x16x32(ka, dsv_lo, acc[db]);
             }
-            wave_lds_sync();
-        };
-
-        const int nchunks = (n + kChunk - 1) / kChunk;
-        Gather G0, G1;
-        int kA[2], kB[2];
-        uint32_t off[2];
-        fetch_keys(0, kA);
-        fetch_keys(kChunk, kB);
-        offsets(kA, off);
-        issue(G0, off);
-        auto step = [&](Gather &cur, Gather &nxt, const int (&kn)[2], int (&kfree)[2], int ch) {
-            fetch_keys((ch + 2) * kChunk, kfree);
-            offsets(kn, off);
-            issue(nxt, off);
-            __builtin_amdgcn_sched_barrier(0);  // keep the gathers ahead of the compute
-            compute(cur, ch * kChunk);
-        };
-        for (int ch = 0; ch < nchunks; ch += 2) {
-            step(G0, G1, kB, kA, ch);
-            if (ch + 1 >= nchunks) break;
-            step(G1, G0, kA, kB, ch + 1);
         }
+        QSA_WAIT_VM(0);  // no gather may outlive the wave's LDS
     }
     if (!hv) return;
 #pragma unroll
@@ -204,6 +206,13 @@ __global__ __launch_bounds__(kDqWaves * 64) void k_dq(Problem p)
             make_uint2(pack_bf16x2(acc[db][0] * s, acc[db][1] * s),
                        pack_bf16x2(acc[db][2] * s, acc[db][3] * s));
     }
+}
+
+__global__ __launch_bounds__(64) void k_dq(Problem p)
+{
+    __shared__ __attribute__((aligned(16))) char ks[kChunk * 512];
+    __shared__ __attribute__((aligned(16))) char vs[kChunk * 512];
+    dq_row(p, (lds_char *)ks, (lds_char *)vs);
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -501,8 +510,7 @@ hipError_t launch_delta(const Problem &p, hipStream_t s)
 hipError_t launch_dq(const Problem &p, hipStream_t s)
 {
     const int64_t items = p.B * p.Sq * p.Hkv;
-    hipLaunchKernelGGL(k_dq, dim3((unsigned)((items + kDqWaves - 1) / kDqWaves)),
-                       dim3(kDqWaves * 64), 0, s, p);
+    hipLaunchKernelGGL(k_dq, dim3((unsigned)items), dim3(64), 0, s, p);
     return hipGetLastError();
 }
 
