@@ -33,6 +33,9 @@ qsa_status check_dims(const qsa_dims *d)
         return QSA_ERR_SHAPE;
     const int64_t stride = (d->Skv + kTile - 1) / kTile * kTile;
     if (d->B * d->Hkv * stride > (int64_t(1) << 30)) return QSA_ERR_SHAPE;
+    // dK/dV work items: one per query segment and 16-key group.
+    const int64_t nseg = ((d->Sq + kTile - 1) / kTile + kSegTiles - 1) / kSegTiles;
+    if (nseg * d->B * d->Hkv * (stride / 16) >= (int64_t(1) << 31)) return QSA_ERR_SHAPE;
     // Gathers use 32-bit buffer offsets within one batch row of K/V or Q/dO.
     if (d->Skv * d->Hkv * kD * 2 >= (int64_t(1) << 31)) return QSA_ERR_SHAPE;
     if (d->Sq * d->Hq * kD * 2 >= (int64_t(1) << 31)) return QSA_ERR_SHAPE;
@@ -42,7 +45,7 @@ qsa_status check_dims(const qsa_dims *d)
 
 struct Layout {
     size_t memb, has, mbits, row_keys, row_cnt, tile_cnt, kinds, fpc, fpi, ffc, ffi, rpc, rpi, rfc,
-        rfi, delta, total;
+        rfi, delta, kv_part, kv_flag, total;
 };
 
 // which: 0 forward, 1 backward, 2 preprocess (only tile counts and, if the
@@ -81,6 +84,9 @@ Layout layout(const qsa_dims *d, int which)
         L.rfi = take((size_t)(d->B * nKT * nQT) * 4);
     }
     L.delta = which == 1 ? take((size_t)(d->B * d->Hq * d->Sq) * 4) : none;
+    const int64_t nseg = (nQT + kSegTiles - 1) / kSegTiles;
+    L.kv_part = which == 1 ? take((size_t)(d->B * d->Hkv * nseg * stride) * 2 * kD * 4) : none;
+    L.kv_flag = which == 1 ? take((size_t)(d->B * d->Hkv * nseg * (stride / 16))) : none;
     L.total = off;
     return L;
 }
@@ -123,6 +129,7 @@ void fill_common(Problem &p, const qsa_dims *d, const void *routes, float scale)
     p.nQT = (d->Sq + kTile - 1) / kTile;
     p.nKT = (d->Skv + kTile - 1) / kTile;
     p.stride = p.nKT * kTile;
+    p.nseg = (p.nQT + kSegTiles - 1) / kSegTiles;
     p.scale = scale;
     p.routes = routes;
 }
@@ -149,6 +156,8 @@ void carve(Problem &p, const Layout &L, void *ws)
         p.rev_f_idx = reinterpret_cast<int32_t *>(w + L.rfi);
     }
     if (L.delta != none) p.delta = reinterpret_cast<float *>(w + L.delta);
+    if (L.kv_part != none) p.kv_part = reinterpret_cast<float *>(w + L.kv_part);
+    if (L.kv_flag != none) p.kv_flag = reinterpret_cast<uint8_t *>(w + L.kv_flag);
 }
 
 qsa_status check_scale(float scale)

@@ -16,20 +16,23 @@
 //    accumulator layout and is the B operand of dQ^T = K^T dS^T, whose K^T
 //    operand is the transposed read of the same staged K rows.
 //  * k_dkdv: key-major. One wave owns 16 consecutive keys of one KV head and
-//    keeps their K and V rows in registers and their dK, dV accumulators for
-//    the whole run. It walks the reverse tile lists of its 128-key tile column
-//    from the last query tile down, reads a 16-bit slice of the bit-packed
-//    membership row of every query in those tiles, and collects the rows that
-//    select one of its keys into an LDS list (descending). Rows are then
-//    processed in that order with two rows' Q, dO, lse and delta loads in
-//    flight: S = Q K^T and dP = dO V^T per row (M = heads), then, two rows at
-//    a time, dV += P^T dO and dK += dS^T Q with the two rows' heads forming the
-//    32-long contraction. Q and dO rows are staged in LDS and read transposed.
-//    P and dS enter these products (and dS the dQ product) as bf16 high + low
-//    parts, so that sums over thousands of query heads keep FP32-level error.
-//    The descending sweep keeps every wave near the same query rows (random
-//    selections have one density per query position), and blocks are mapped
-//    XCD-aware so neighbouring key groups share an L2.
+//    one segment of 32 query tiles, keeps the 16 K and V rows in registers and
+//    their dK, dV accumulators for the whole item. It walks the reverse tile
+//    lists of its 128-key tile column inside the segment from the last query
+//    tile down, reads a 16-bit slice of the bit-packed membership row of every
+//    query in those tiles, and lists the rows that select one of its keys in
+//    LDS. Each listed row's Q and dO (12 heads x 512 bytes each) are gathered
+//    into a 2-slot LDS ring by direct-to-LDS loads, one row ahead, then read
+//    in the row layout (A operands of S = Q K^T and dP = dO V^T, M = heads)
+//    and transposed (B operands of dV += P^T dO and dK += dS^T Q, where two
+//    rows' heads form the 32-long contraction). P and dS enter these products
+//    (and dS the dQ product) as bf16 high + low parts, so that sums over
+//    thousands of query heads keep FP32-level error.
+//  * k_dkdv_reduce: the FP32 partial sums of the segments are added in
+//    segment order (deterministic, no atomics) and written as bf16 dK, dV.
+//    Splitting the long causal key columns into segments keeps every SIMD
+//    busy to the end: the first key groups are selected by almost every later
+//    row and would otherwise dominate the run time.
 #include "common.h"
 
 namespace qsa {
@@ -216,48 +219,65 @@ __global__ __launch_bounds__(64) void k_dq(Problem p)
 }
 
 // ---------------------------------------------------------------- dK, dV
-constexpr int kKvWaves = 2;
-constexpr int kHitCap = 448;    // LDS hit list capacity per wave
-constexpr int kHitBatch = 192;  // stop scanning once this many hits are listed
-constexpr int kScanWin = 4;     // 64-row windows scanned per step
+constexpr int kHitCap = 512;  // LDS hit list entries per batch
+constexpr int kScanWin = 4;   // 64-row windows scanned per step
+constexpr int kSlot = 2 * kGroup * 512;  // Q then dO rows of the group's heads
 
-struct RowOps {
-    uint4 q[8], g[8];
-    float lse[4], dl[4];
-};
-
-__global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
+// Body of k_dkdv. slots: two staging slots of kSlot bytes; zero: 4 rows of
+// 512 zero bytes read in place of the padding heads 12..15; hrow/hmask: the
+// wave's hit list.
+__device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, lds_char *zero,
+                                          int32_t *hrow, uint32_t *hmask)
 {
-    // Per wave: Q and dO of two query rows in the transposed staging layout,
-    // and the list of (row, 16-bit mask) hits.
-    __shared__ __attribute__((aligned(16))) char st_all[kKvWaves][4 * kTrBlock];
-    __shared__ int32_t hit_row[kKvWaves][kHitCap];
-    __shared__ uint32_t hit_mask[kKvWaves][kHitCap];
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int lane = threadIdx.x;
     const int col = lane & 15, quad = lane >> 4;
     const int64_t ngroups = p.stride >> 4;
-    // item = (b * Hkv + g) * ngroups + kg. Blocks go to the XCDs round-robin,
-    // so the key groups at the start of a causal range, which every later row
-    // can select and which carry the most hits, are spread over all XCDs.
-    const int64_t item = (int64_t)blockIdx.x * kKvWaves + wave;
-    if (item >= p.B * p.Hkv * ngroups) return;
-    const int64_t kg = item % ngroups;
-    const int64_t bg = item / ngroups;
+    const int64_t per_seg = p.B * p.Hkv * ngroups;
+    // item = (nseg - 1 - seg) * per_seg + (b * Hkv + g) * ngroups + kg: all key
+    // groups of one query segment run side by side and read the same rows.
+    const int64_t item = blockIdx.x;
+    if (item >= p.nseg * per_seg) return;
+    const int64_t seg = p.nseg - 1 - item / per_seg;
+    const int64_t rem = item - (p.nseg - 1 - seg) * per_seg;
+    const int64_t kg = rem % ngroups, bg = rem / ngroups;
     const int g = (int)(bg % p.Hkv);
     const int64_t b = bg / p.Hkv;
     const int64_t key0 = kg * 16;
-    if (key0 >= p.Skv) return;
+    uint8_t *flag = p.kv_flag + (bg * p.nseg + seg) * ngroups + kg;
+    if (key0 >= p.Skv) {
+        if (lane == 0) *flag = 0;
+        return;
+    }
+
+    // This item's query tiles: the entries of the tile column's reverse lists
+    // that fall in [t_lo, t_hi).
     const int64_t t = key0 >> 7;
-    char *stq[2] = {st_all[wave], st_all[wave] + kTrBlock};
-    char *stg[2] = {st_all[wave] + 2 * kTrBlock, st_all[wave] + 3 * kTrBlock};
-    int32_t *hrow = hit_row[wave];
-    uint32_t *hmask = hit_mask[wave];
+    const int64_t bt = b * p.nKT + t;
+    const int32_t t_lo = (int32_t)(seg * kSegTiles);
+    const int32_t t_hi = (int32_t)((seg + 1) * kSegTiles);
+    const int32_t *idx_p = p.rev_p_idx + bt * p.nQT, *idx_f = p.rev_f_idx + bt * p.nQT;
+    auto lower_bound = [&](const int32_t *a, int32_t cnt, int32_t x) {
+        int32_t lo = 0, hi = cnt;
+        while (lo < hi) {
+            const int32_t mid = (lo + hi) >> 1;
+            if (a[mid] < x) lo = mid + 1;
+            else hi = mid;
+        }
+        return lo;
+    };
+    const int32_t cnt_p = p.rev_p_cnt[bt], cnt_f = p.rev_f_cnt[bt];
+    const int32_t p_lo = lower_bound(idx_p, cnt_p, t_lo), p_hi = lower_bound(idx_p, cnt_p, t_hi);
+    const int32_t f_lo = lower_bound(idx_f, cnt_f, t_lo), f_hi = lower_bound(idx_f, cnt_f, t_hi);
+    const int64_t nwin = 2 * ((int64_t)(p_hi - p_lo) + (f_hi - f_lo));
+    if (lane == 0) *flag = nwin > 0 ? 1 : 0;
+    if (nwin == 0) return;
 
-    // Clear the staging area: rows 12..15 (heads past the group) stay zero.
-    for (int o = lane * 16; o < 4 * kTrBlock; o += 64 * 16)
-        *reinterpret_cast<uint4 *>(st_all[wave] + o) = zero_u4();
+    // Padding heads of the transposed operands read zeros.
+    for (int o = lane * 16; o < 4 * 512; o += 64 * 16)
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4 *>(zero + o) = u32x4{0u, 0u, 0u, 0u};
 
-    // K and V rows of the 16 keys as B operands of S = Q K^T and dP = dO V^T.
+    // K and V rows of the 16 keys as B operands of S = Q K^T and dP = dO V^T:
+    // lane (key col, quad) holds columns 32t + 8quad .. +7 for step t.
     bf16x8 kf[8], vf[8];
     {
         const uint32_t kv_bytes = (uint32_t)((p.Skv - 1) * p.Hkv * kD * 2 + kD * 2);
@@ -265,11 +285,11 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
         const rsrc_t rv = make_rsrc(p.v + (b * p.Skv * p.Hkv + g) * (int64_t)kD, kv_bytes);
         const int64_t key = key0 + col;
         const uint32_t off =
-            key < p.Skv ? (uint32_t)(key * p.Hkv * kD * 2 + quad * 128) : kOutOfRange;
+            key < p.Skv ? (uint32_t)(key * p.Hkv * kD * 2 + quad * 16) : kOutOfRange;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            kf[s] = as_bf16x8(buf_load16(rk, off + 16 * s));
-            vf[s] = as_bf16x8(buf_load16(rv, off + 16 * s));
+            kf[s] = as_bf16x8(buf_load16(rk, off + 64 * s));
+            vf[s] = as_bf16x8(buf_load16(rv, off + 64 * s));
         }
     }
     f32x4 adk[16], adv[16];
@@ -279,11 +299,10 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
         adv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const float c = p.scale * 1.4426950408889634f;
-    const bool hq = quad < 3;      // accumulator rows 4*quad+e are real heads
-    const bool hv = col < kGroup;  // lane loads head `col` of a Q/dO row
-    const int tr_lane = lane_tr_base(col, quad);
+    const bool hq = quad < 3;  // accumulator rows 4*quad+e of S are real heads
 
-    // Q/dO rows of this batch and group; lse/delta of this batch and group.
+    // Rows of Q and dO of this batch and group (12 heads x 512 bytes each,
+    // contiguous), lse and delta of this batch and group.
     const uint32_t q_bytes = (uint32_t)((p.Sq - 1) * p.Hq * kD * 2 + kGroup * kD * 2);
     const rsrc_t rq = make_rsrc(p.q + (b * p.Sq * p.Hq + g * kGroup) * (int64_t)kD, q_bytes);
     const rsrc_t rg = make_rsrc(p.dout + (b * p.Sq * p.Hq + g * kGroup) * (int64_t)kD, q_bytes);
@@ -291,30 +310,48 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
                                 (uint32_t)(kGroup * p.Sq * 4));
     const rsrc_t rd = make_rsrc(p.delta + (b * p.Hq + g * kGroup) * p.Sq,
                                 (uint32_t)(kGroup * p.Sq * 4));
-    auto load_row = [&](RowOps &R, int64_t qi) {
-        const uint32_t off =
-            hv ? (uint32_t)(qi * p.Hq * kD * 2 + col * kD * 2 + quad * 128) : kOutOfRange;
+    // Gather of one row into a slot: instruction x < 6 stages Q heads 2x and
+    // 2x+1, instruction 6+x the same dO heads, in the swizzled layout.
+    auto gather_row = [&](int64_t qi, lds_char *slot) {
+        const uint32_t rb = (uint32_t)(qi * p.Hq * kD * 2);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            R.q[s] = buf_load16(rq, off + 16 * s);
-            R.g[s] = buf_load16(rg, off + 16 * s);
+        for (int x = 0; x < 6; ++x) {
+            const uint32_t o = rb + (uint32_t)(x * 1024 + (lane >> 5) * 512 + (dma_chunk(lane, x) << 4));
+            dma16(rq, slot + x * 1024, o);
+            dma16(rg, slot + kGroup * 512 + x * 1024, o);
         }
+    };
+    auto load_stats = [&](int64_t qi, float (&ls)[4], float (&dl)[4]) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const uint32_t lo = hq ? (uint32_t)(((4 * quad + e) * p.Sq + qi) * 4) : kOutOfRange;
-            R.lse[e] =
-                __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, lo, 0, 0));
-            R.dl[e] =
-                __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, lo, 0, 0));
+            ls[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, lo, 0, 0));
+            dl[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, lo, 0, 0));
         }
     };
 
-    float pa[4] = {0.f, 0.f, 0.f, 0.f}, da[4] = {0.f, 0.f, 0.f, 0.f};
-    int filled = 0;
+    // Row-layout read (A operand of S and dP): lane (head col, quad) takes
+    // chunk 4t + quad of its head; the padding heads 12..15 read head 11 (their
+    // S rows are never selected).
+    const int ahead = col < kGroup ? col : kGroup - 1;
+    const int amask = swz_mask(ahead);
+    // Transposed read (B operand of dV and dK): lane i of group quad names the
+    // 8-byte unit of head 4*quad + i/4 holding columns 16db + 4(i%4) .. +3;
+    // group 3 (heads 12..15) reads the zero rows.
+    const int th = 4 * quad + (col >> 2);
+    const int tm = swz_mask(th);
+    const int tlane = (quad < 3 ? th * 512 : (col >> 2) * 512) +
+                      ((((col >> 1) & 1) ^ (tm & 1)) << 4) + (col & 1) * 8;
+    const int txor = tm >> 1;
 
-    // Contract the staged pair into dV and dK. Slot j of lane group quad is
-    // head 4*quad + (j & 3) of row (j < 4 ? first : second).
-    auto flush = [&](const float *pb, const float *db_) {
+    // Pending row of the current pair: its P, dS and transposed operands.
+    float pa[4] = {0.f, 0.f, 0.f, 0.f}, da[4] = {0.f, 0.f, 0.f, 0.f};
+    uint2 pq[16], pg[16];
+    bool pending = false;
+
+    // dV += P^T dO and dK += dS^T Q for the pending row (k slots 0..3 of each
+    // lane group) and a second row (slots 4..7); P and dS as bf16 high + low.
+    auto flush = [&](const float *pb, const float *db_, const uint2 *bq, const uint2 *bg_) {
         uint32_t ph[4], pl[4], dh[4], dl[4];
         split_bf16x2(pa[0], pa[1], ph[0], pl[0]);
         split_bf16x2(pa[2], pa[3], ph[1], pl[1]);
@@ -328,93 +365,32 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
         const bf16x8 A_pl = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
         const bf16x8 A_d = as_bf16x8(make_uint4(dh[0], dh[1], dh[2], dh[3]));
         const bf16x8 A_dl = as_bf16x8(make_uint4(dl[0], dl[1], dl[2], dl[3]));
-        wave_lds_sync();
 #pragma unroll
-        for (int h = 0; h < 8; ++h) {
-            uint2 ga[2], gb[2], qa[2], qb[2];
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const int o = tr_lane + tile_tr_offset(2 * h + x);
-                ga[x] = lds_read_tr(stg[0] + o);
-                gb[x] = lds_read_tr(stg[1] + o);
-                qa[x] = lds_read_tr(stq[0] + o);
-                qb[x] = lds_read_tr(stq[1] + o);
-            }
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const int dbk = 2 * h + x;
-                const bf16x8 Bg = as_bf16x8(make_uint4(ga[x].x, ga[x].y, gb[x].x, gb[x].y));
-                const bf16x8 Bq = as_bf16x8(make_uint4(qa[x].x, qa[x].y, qb[x].x, qb[x].y));
-                adv[dbk] = mfma_16x16x32(A_p, Bg, adv[dbk]);
-                adv[dbk] = mfma_16x16x32(A_pl, Bg, adv[dbk]);
-                adk[dbk] = mfma_16x16x32(A_d, Bq, adk[dbk]);
-                adk[dbk] = mfma_16x16x32(A_dl, Bq, adk[dbk]);
-            }
-        }
-        wave_lds_sync();
-    };
-
-    // One query row: S, dP, then P and dS, staged Q/dO, and the pair flush.
-    auto process = [&](const RowOps &R, uint32_t mask) {
-        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, pd = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            sa = mfma_16x16x32(as_bf16x8(R.q[s]), kf[s], sa);
-            pd = mfma_16x16x32(as_bf16x8(R.g[s]), vf[s], pd);
-        }
-        if (hv) {
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                tr_store8(stq[filled], col, quad * 64 + 8 * s, R.q[s]);
-                tr_store8(stg[filled], col, quad * 64 + 8 * s, R.g[s]);
-            }
-        }
-        // Lane holds S[head 4*quad+e][key col].
-        const bool on = hq && ((mask >> col) & 1u);
-        float pn[4], dn[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float pr = on ? exp2f(sa[e] * c - R.lse[e] * 1.4426950408889634f) : 0.f;
-            pn[e] = pr;
-            // select, never multiply: an unselected key's dP may be non-finite
-            dn[e] = on ? pr * (pd[e] - R.dl[e]) : 0.f;
-        }
-        if (filled == 0) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pa[e] = pn[e];
-                da[e] = dn[e];
-            }
-            filled = 1;
-        } else {
-            flush(pn, dn);
-            filled = 0;
+        for (int db = 0; db < 16; ++db) {
+            const bf16x8 Bg = as_bf16x8(make_uint4(pg[db].x, pg[db].y, bg_[db].x, bg_[db].y));
+            const bf16x8 Bq = as_bf16x8(make_uint4(pq[db].x, pq[db].y, bq[db].x, bq[db].y));
+            adv[db] = mfma_16x16x32(A_p, Bg, adv[db]);
+            adv[db] = mfma_16x16x32(A_pl, Bg, adv[db]);
+            adk[db] = mfma_16x16x32(A_d, Bq, adk[db]);
+            adk[db] = mfma_16x16x32(A_dl, Bq, adk[db]);
         }
     };
 
-    // Hits are visited in DESCENDING query order: random selections have the
-    // same density for every key group at a given query position, so all waves
-    // sweep the query range from the top at about the same rate and the rows
-    // they read stay in the caches. Window w (counted from the top) covers
-    // rows 64*(w%2) .. of the reverse-list query tiles (full tiles, then
-    // partial tiles, both from their last entry down).
-    const int64_t bt = b * p.nKT + t;
-    const int32_t cnt_p = p.rev_p_cnt[bt], cnt_f = p.rev_f_cnt[bt];
-    const int32_t *idx_p = p.rev_p_idx + bt * p.nQT, *idx_f = p.rev_f_idx + bt * p.nQT;
-    const int64_t nwin = 2 * ((int64_t)cnt_p + cnt_f);
+    // Hits are visited in DESCENDING query order (tiles from the top of the
+    // merged reverse lists, the upper 64 rows of a tile first): all items of a
+    // segment sweep its rows at about the same rate, so the rows they read
+    // stay in the caches.
     const int64_t mstride = p.stride >> 5;
     const uint32_t *mrow = p.mbits + (b * p.Sq) * mstride + (key0 >> 5);
     const int shift = (int)(key0 & 16);
     const uint64_t above = (lane == 63) ? 0ull : (~0ull << (lane + 1));
-
     int64_t w = 0;
-    int32_t ip = cnt_p - 1, jf = cnt_f - 1;  // cursors merging both lists from the top
+    int32_t ip = p_hi - 1, jf = f_hi - 1;
     int32_t cur_tile = -1;
-    RowOps R0, R1, R2;
+    float ls_n[4], dl_n[4];
     while (w < nwin) {
-        // Collect hits, kScanWin windows per step, until a batch is listed.
         int nh = 0;
-        while (w < nwin && nh < kHitBatch) {
+        while (w < nwin && nh <= kHitCap - kScanWin * 64) {
             uint32_t m[kScanWin];
             int64_t rbase[kScanWin];
 #pragma unroll
@@ -423,14 +399,13 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
                 rbase[x] = 0;
                 if (w + x < nwin) {
                     if (((w + x) & 1) == 0) {
-                        // next tile from the top of the merged lists
-                        const int32_t vp = ip >= 0 ? idx_p[ip] : -1;
-                        const int32_t vf = jf >= 0 ? idx_f[jf] : -1;
-                        if (vp > vf) {
+                        const int32_t vp = ip >= p_lo ? idx_p[ip] : -1;
+                        const int32_t vq = jf >= f_lo ? idx_f[jf] : -1;
+                        if (vp > vq) {
                             cur_tile = vp;
                             --ip;
                         } else {
-                            cur_tile = vf;
+                            cur_tile = vq;
                             --jf;
                         }
                     }
@@ -451,51 +426,147 @@ __global__ __launch_bounds__(kKvWaves * 64) void k_dkdv(Problem p)
             }
             w += kScanWin;
         }
+        if (nh == 0) continue;
         wave_lds_sync();
-        // Process the batch in order, two rows' operands in flight.
-        if (nh > 0) load_row(R0, hrow[0]);
-        if (nh > 1) load_row(R1, hrow[1]);
-        for (int h = 0; h < nh; h += 3) {
-            if (h + 2 < nh) load_row(R2, hrow[h + 2]);
-            __builtin_amdgcn_sched_barrier(0);
-            process(R0, hmask[h]);
-            if (h + 1 >= nh) break;
-            if (h + 3 < nh) load_row(R0, hrow[h + 3]);
-            __builtin_amdgcn_sched_barrier(0);
-            process(R1, hmask[h + 1]);
-            if (h + 2 >= nh) break;
-            if (h + 4 < nh) load_row(R1, hrow[h + 4]);
-            __builtin_amdgcn_sched_barrier(0);
-            process(R2, hmask[h + 2]);
-        }
-        wave_lds_sync();
-    }
-    if (filled) {
-        // Second row of the last pair is empty: clear its staged rows.
-        const float zero4[4] = {0.f, 0.f, 0.f, 0.f};
-        if (hv) {
+        // Rows of the batch in order; row h is staged in slot h & 1 while the
+        // wave computes row h - 1.
+        int64_t rcur = hrow[0];
+        uint32_t mcur = hmask[0];
+        float ls_c[4], dl_c[4];
+        QSA_WAIT_LDS();
+        gather_row(rcur, slots);
+        load_stats(rcur, ls_c, dl_c);
+        for (int h = 0; h < nh; ++h) {
+            lds_char *slot = slots + (h & 1) * kSlot;
+            QSA_WAIT_VM(0);
+            uint4 qa[8], ga[8];
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                tr_store8(stq[1], col, quad * 64 + 8 * s, zero_u4());
-                tr_store8(stg[1], col, quad * 64 + 8 * s, zero_u4());
+            for (int t8 = 0; t8 < 8; ++t8) {
+                const int o = ahead * 512 + (((4 * t8 + quad) ^ amask) << 4);
+                qa[t8] = lds_read16(slot + o);
+                ga[t8] = lds_read16(slot + kGroup * 512 + o);
+            }
+            uint2 tq[16], tg[16];
+#pragma unroll
+            for (int db = 0; db < 16; ++db) {
+                const int o = tlane + ((db ^ txor) << 5);
+                tq[db] = lds_read_tr((quad < 3 ? slot : zero) + o);
+                tg[db] = lds_read_tr((quad < 3 ? slot + kGroup * 512 : zero) + o);
+            }
+            const bool more = h + 1 < nh;
+            const int64_t rnext = more ? hrow[h + 1] : 0;
+            const uint32_t mnext = more ? hmask[h + 1] : 0u;
+            QSA_WAIT_LDS();
+            if (more) {
+                gather_row(rnext, slots + ((h + 1) & 1) * kSlot);
+                load_stats(rnext, ls_n, dl_n);
+            }
+
+            f32x4 sa = {0.f, 0.f, 0.f, 0.f}, pd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t8 = 0; t8 < 8; ++t8) {
+                sa = mfma_16x16x32(as_bf16x8(qa[t8]), kf[t8], sa);
+                pd = mfma_16x16x32(as_bf16x8(ga[t8]), vf[t8], pd);
+            }
+            // Lane holds S[head 4*quad+e][key col].
+            const bool on = hq && ((mcur >> col) & 1u);
+            float pn[4], dn[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float pr = on ? exp2f(sa[e] * c - ls_c[e] * 1.4426950408889634f) : 0.f;
+                pn[e] = pr;
+                // select, never multiply: an unselected key's dP may be non-finite
+                dn[e] = on ? pr * (pd[e] - dl_c[e]) : 0.f;
+            }
+            if (pending) {
+                flush(pn, dn, tq, tg);
+                pending = false;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pa[e] = pn[e];
+                    da[e] = dn[e];
+                }
+#pragma unroll
+                for (int db = 0; db < 16; ++db) {
+                    pq[db] = tq[db];
+                    pg[db] = tg[db];
+                }
+                pending = true;
+            }
+            rcur = rnext;
+            mcur = mnext;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ls_c[e] = ls_n[e];
+                dl_c[e] = dl_n[e];
             }
         }
-        flush(zero4, zero4);
+        wave_lds_sync();
+    }
+    if (pending) {
+        const float zero4[4] = {0.f, 0.f, 0.f, 0.f};
+        uint2 z[16];
+#pragma unroll
+        for (int db = 0; db < 16; ++db) z[db] = make_uint2(0u, 0u);
+        flush(zero4, zero4, z, z);
     }
 
-    // Lane holds dK/dV[key 4*quad+e][d 16*db + col].
+    // Lane holds dK/dV[key 4*quad+e][d 16*db + col]; the partial sums of this
+    // segment go to its slice of the workspace, dK first, then dV.
+    float *part = p.kv_part + ((bg * p.nseg + seg) * p.stride + key0) * (int64_t)(2 * kD);
 #pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-        const int64_t key = key0 + 4 * quad + e2;
-        if (key >= p.Skv) continue;
-        uint16_t *dkp = p.dk + ((b * p.Skv + key) * p.Hkv + g) * (int64_t)kD + col;
-        uint16_t *dvp = p.dv + ((b * p.Skv + key) * p.Hkv + g) * (int64_t)kD + col;
+    for (int e = 0; e < 4; ++e) {
+        float *pk = part + (4 * quad + e) * (int64_t)(2 * kD) + col;
 #pragma unroll
         for (int db = 0; db < 16; ++db) {
-            dkp[16 * db] = f32_to_bf16(adk[db][e2] * p.scale);
-            dvp[16 * db] = f32_to_bf16(adv[db][e2]);
+            pk[16 * db] = adk[db][e];
+            pk[kD + 16 * db] = adv[db][e];
         }
     }
+}
+
+__global__ __launch_bounds__(64) void k_dkdv(Problem p)
+{
+    __shared__ __attribute__((aligned(16))) char slots[2 * kSlot];
+    __shared__ __attribute__((aligned(16))) char zero[4 * 512];
+    __shared__ int32_t hrow[kHitCap];
+    __shared__ uint32_t hmask[kHitCap];
+    dkdv_item(p, (lds_char *)slots, (lds_char *)zero, hrow, hmask);
+}
+
+// dK = scale * sum of the segment partials, dV = sum, in segment order; one
+// thread per (batch, KV head, key, 4 columns).
+__global__ __launch_bounds__(256) void k_dkdv_reduce(Problem p)
+{
+    const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t per_bg = p.stride * (2 * kD / 4);
+    if (x >= p.B * p.Hkv * per_bg) return;
+    const int64_t bg = x / per_bg;
+    const int64_t r = x - bg * per_bg;
+    const int64_t key = r / (2 * kD / 4);
+    const int f4 = (int)(r - key * (2 * kD / 4));
+    const int64_t b = bg / p.Hkv;
+    const int g = (int)(bg - b * p.Hkv);
+    if (key >= p.Skv) return;
+    const int64_t ngroups = p.stride >> 4;
+    const uint8_t *flag = p.kv_flag + bg * p.nseg * ngroups + (key >> 4);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t seg = 0; seg < p.nseg; ++seg) {
+        if (!flag[seg * ngroups]) continue;
+        const float4 v = *reinterpret_cast<const float4 *>(
+            p.kv_part + ((bg * p.nseg + seg) * p.stride + key) * (int64_t)(2 * kD) + 4 * f4);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    const bool is_k = f4 < kD / 4;
+    const int d = 4 * (is_k ? f4 : f4 - kD / 4);
+    const float s = is_k ? p.scale : 1.f;
+    uint16_t *dst = (is_k ? p.dk : p.dv) + ((b * p.Skv + key) * p.Hkv + g) * (int64_t)kD + d;
+    *reinterpret_cast<uint2 *>(dst) =
+        make_uint2(pack_bf16x2(acc.x * s, acc.y * s), pack_bf16x2(acc.z * s, acc.w * s));
 }
 
 }  // namespace
@@ -516,9 +587,10 @@ hipError_t launch_dq(const Problem &p, hipStream_t s)
 
 hipError_t launch_dkdv(const Problem &p, hipStream_t s)
 {
-    const int64_t groups = p.B * p.Hkv * (p.stride >> 4);
-    hipLaunchKernelGGL(k_dkdv, dim3((unsigned)((groups + kKvWaves - 1) / kKvWaves)),
-                       dim3(kKvWaves * 64), 0, s, p);
+    const int64_t items = p.nseg * p.B * p.Hkv * (p.stride >> 4);
+    hipLaunchKernelGGL(k_dkdv, dim3((unsigned)items), dim3(64), 0, s, p);
+    const int64_t threads = p.B * p.Hkv * p.stride * (2 * kD / 4);
+    hipLaunchKernelGGL(k_dkdv_reduce, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

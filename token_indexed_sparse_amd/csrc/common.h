@@ -11,6 +11,7 @@ namespace qsa {
 constexpr int kD = 256;     // head dimension (QSA page, "Support and execution")
 constexpr int kGroup = 12;  // query heads per KV head
 constexpr int kTile = 128;  // query and key tile edge of the membership table
+constexpr int kSegTiles = 32;  // query tiles per dK/dV work segment
 constexpr int kMaxSkvLog2 = 19;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -40,6 +41,11 @@ struct Problem {
     // backward
     float *delta;
     uint16_t *dq, *dk, *dv;
+    // dK/dV partial sums per query segment: [B*Hkv][nseg][stride][dK 256 | dV 256]
+    // FP32, and per (B*Hkv, segment, 16-key group) whether a partial was written
+    float *kv_part;
+    uint8_t *kv_flag;
+    int64_t nseg;
 };
 
 hipError_t launch_preprocess(const Problem &p, hipStream_t s);
