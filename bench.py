@@ -41,7 +41,7 @@ FLOP_PER_PAIR_HEAD = {
 COUNTED_FWD = 4 * 256
 COUNTED_BWD = 10 * 256
 FWD_STAGES = ["preprocess_fwd", "forward"]
-BWD_STAGES = ["preprocess_bwd", "delta", "dq", "dkdv"]
+BWD_STAGES = ["preprocess_bwd", "delta", "dq", "dkdv", "dkdv_reduce"]
 
 
 def pairs_per_row(routes: np.ndarray, Skv: int) -> np.ndarray:
@@ -180,7 +180,7 @@ def main() -> int:
     stream = torch.cuda.current_stream().cuda_stream
     K, W = args.steps, args.warmup
     fev = [Events(hip, 3) for _ in range(K)]
-    bev = [Events(hip, 5) for _ in range(K)]
+    bev = [Events(hip, 6) for _ in range(K)]
 
     def step(i=None):
         fe = ctypes.cast(fev[i].ev, ctypes.c_void_p) if i is not None else None
@@ -194,7 +194,7 @@ def main() -> int:
                                     v.data_ptr(), out32.data_ptr(), lse.data_ptr(),
                                     routes.data_ptr(), wl.scale, dq.data_ptr(), dk.data_ptr(),
                                     dv.data_ptr(), ws_b.data_ptr(), ws_b.numel(), stream,
-                                    be, 5 if be is not None else 0)
+                                    be, 6 if be is not None else 0)
         assert st == 0, st
 
     print(f"[bench] warmup {W}", file=sys.stderr, flush=True)
@@ -211,10 +211,10 @@ def main() -> int:
     stage_ms = {}
     for name, a in zip(FWD_STAGES, range(2)):
         stage_ms[name] = float(np.mean([e.elapsed(a, a + 1) for e in fev]))
-    for name, a in zip(BWD_STAGES, range(4)):
+    for name, a in zip(BWD_STAGES, range(5)):
         stage_ms[name] = float(np.mean([e.elapsed(a, a + 1) for e in bev]))
     fwd_ms = float(np.mean([e.elapsed(0, 2) for e in fev]))
-    bwd_ms = float(np.mean([e.elapsed(0, 4) for e in bev]))
+    bwd_ms = float(np.mean([e.elapsed(0, 5) for e in bev]))
     flop_fwd = COUNTED_FWD * wl.Hq * nnz
     flop_bwd = COUNTED_BWD * wl.Hq * nnz
     value = (flop_fwd + flop_bwd) / (ms_step * 1e-3) / 1e12

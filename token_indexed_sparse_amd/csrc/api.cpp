@@ -279,6 +279,8 @@ qsa_status qsa_backward_timed(const qsa_dims *dims, const void *grad_out, const 
     if (mark(events, 3, s) != hipSuccess) return QSA_ERR_DEVICE;
     if (launch_dkdv(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
     if (mark(events, 4, s) != hipSuccess) return QSA_ERR_DEVICE;
+    if (launch_dkdv_reduce(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 5, s) != hipSuccess) return QSA_ERR_DEVICE;
     return QSA_OK;
 }
 

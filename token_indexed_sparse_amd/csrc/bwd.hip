@@ -589,6 +589,11 @@ hipError_t launch_dkdv(const Problem &p, hipStream_t s)
 {
     const int64_t items = p.nseg * p.B * p.Hkv * (p.stride >> 4);
     hipLaunchKernelGGL(k_dkdv, dim3((unsigned)items), dim3(64), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_dkdv_reduce(const Problem &p, hipStream_t s)
+{
     const int64_t threads = p.B * p.Hkv * p.stride * (2 * kD / 4);
     hipLaunchKernelGGL(k_dkdv_reduce, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p);
     return hipGetLastError();

@@ -53,6 +53,7 @@ hipError_t launch_forward(const Problem &p, hipStream_t s);
 hipError_t launch_delta(const Problem &p, hipStream_t s);
 hipError_t launch_dq(const Problem &p, hipStream_t s);
 hipError_t launch_dkdv(const Problem &p, hipStream_t s);
+hipError_t launch_dkdv_reduce(const Problem &p, hipStream_t s);
 
 #if defined(__HIPCC__)
 __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
