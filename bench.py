@@ -10,7 +10,9 @@ Prints one JSON line:
              number of distinct valid (query, key) pairs of the routes
   roofline   the longest-running kernel: algorithmic FLOP per launch / its
              average duration measured with HIP events on its own stream,
-             against the MI355X dense bf16 MFMA peak
+             against the MI355X dense bf16 MFMA peak; `traffic` is its HBM
+             bytes per launch from the committed rocprofv3 counter summary
+             (profiles/traffic_<workload>.txt), null once the kernels changed
   cpu_baseline  the FP64 oracle on a bounded sample of the same workload,
              on this host's cores, scaled to TFLOP/s
 """
@@ -53,6 +55,33 @@ def pairs_per_row(routes: np.ndarray, Skv: int) -> np.ndarray:
         s = np.sort(np.where((c >= 0) & (c < Skv), c, -1), axis=-1)
         out[a:a + 4096] = (s[:, 0] >= 0) + ((s[:, 1:] != s[:, :-1]) & (s[:, 1:] >= 0)).sum(1)
     return out
+
+
+TRAFFIC_SOURCES = ("token_indexed_sparse_amd/csrc/common.h", "token_indexed_sparse_amd/csrc/bwd.hip",
+                   "token_indexed_sparse_amd/csrc/fwd.hip")
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` (calibrated FETCH_SIZE + WRITE_SIZE) from the
+    committed rocprofv3 summary, or None if there is none or the kernels changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    sha, rows = None, {}
+    for line in open(path):
+        parts = line.split()
+        if line.startswith("source_sha256:"):
+            sha = parts[1]
+        elif line.startswith("traffic ") and len(parts) == 4:
+            rows[parts[1]] = int(parts[2]) + int(parts[3])
+    if sha != h.hexdigest():
+        return None
+    return rows.get("k_" + kernel)
 
 
 def hip_runtime():
@@ -224,7 +253,8 @@ def main() -> int:
     dom_flop = FLOP_PER_PAIR_HEAD[dom] * wl.Hq * nnz
     achieved = dom_flop / (stage_ms[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": measured_traffic(wl.name, dom),
                 "flop_per_launch": dom_flop, "avg_launch_ms": stage_ms[dom]}
 
     # algorithmic HBM bytes of one step (each tensor once per call, membership once per call)
