@@ -161,15 +161,38 @@ __device__ __forceinline__ void dma16(rsrc_t r, lds_char *lds, uint32_t off)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, off, 0, 0, 0);
 }
 
+// The same with an immediate byte offset IMM added to every lane's memory
+// offset. The instruction adds its immediate to the LDS address too, so the
+// LDS base passed down is lds - IMM: the 64 x 16 bytes still land at lds.
+template <int IMM>
+__device__ __forceinline__ void dma16_imm(rsrc_t r, lds_char *lds, uint32_t off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds - IMM, 16, off, 0, IMM, 0);
+}
+
+// Column-sliced staging of 32 gathered rows of 512 bytes (16 KB): gather
+// instruction s (0..15) loads the 32-byte column slice s of every row, lane l
+// taking row (l & 31) ^ (8 (l >> 5)) and half l >> 5 of the slice. Each lane
+// therefore serves one row for all 16 instructions and addresses them with
+// one register plus an immediate. Byte (row r, 16-byte chunk c) sits at
+// (c >> 1) * 1024 + (c & 1) * 512 + (r ^ 8 (c & 1)) * 16: 16 lanes reading
+// one chunk of 16 consecutive rows, and 32 lanes reading 8-byte units of 8
+// consecutive rows in both halves of a slice, touch distinct banks.
+__device__ __forceinline__ int colslice_row(int lane) { return (lane & 31) ^ ((lane >> 5) << 3); }
+__device__ __forceinline__ int colslice(int row, int chunk)
+{
+    return (chunk >> 1) * 1024 + (chunk & 1) * 512 + ((row ^ ((chunk & 1) << 3)) << 4);
+}
+
 // Row j of a staged region occupies bytes [512 j, 512 j + 512); its 16-byte
 // chunk c (elements 8c .. 8c+7) sits at slot c ^ swz_mask(j). The mask takes
 // 16 distinct values over 16 consecutive rows, so 16 lanes reading the same
-// chunk of 16 rows hit distinct banks; and rows 4q .. 4q+3 differ in mask bits
-// 1..3, so a transposed read of 32-byte column pairs of 4 rows is
-// conflict-free as well.
+// chunk of 16 rows hit distinct banks; and its bits 1..3 are j mod 8, so a
+// transposed read of 32-byte column pairs of 8 consecutive rows (32 lanes)
+// touches 8 distinct 32-byte bank groups.
 __device__ __forceinline__ int swz_mask(int row)
 {
-    return ((row & 3) << 2) | ((row >> 2) & 3);
+    return ((row & 7) << 1) | ((row >> 3) & 1);
 }
 __device__ __forceinline__ int swz(int row, int chunk)
 {
@@ -195,6 +218,66 @@ __device__ __forceinline__ uint2 lds_read_tr(const lds_char *p)
 {
     return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                                          (lds_bf16x4 *)(const_cast<lds_char *>(p))));
+}
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t lds_addr(const lds_char *p)
+{
+    return (uint32_t)(uintptr_t)p;
+}
+
+// LDS reads written in inline assembly. The compiler makes every LDS read it
+// emits wait for all direct-to-LDS loads the wave has in flight, which would
+// cap the gather pipeline at one chunk; these blocks are invisible to that
+// rule, and the counted waits at the call sites order them after the loads
+// they depend on. Each block ends with its own lgkmcnt(0), so all outputs are
+// written when it ends, and the outputs are early-clobber, so no read can
+// land in a register that a later read of the block still uses as address.
+// OFF is an immediate byte offset added to every address.
+template <int OFF>
+__device__ __forceinline__ void lds_read16_x8(u32x4 (&d)[8], const uint32_t (&a)[8])
+{
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%c16\n"
+        "ds_read_b128 %1, %9 offset:%c16\n"
+        "ds_read_b128 %2, %10 offset:%c16\n"
+        "ds_read_b128 %3, %11 offset:%c16\n"
+        "ds_read_b128 %4, %12 offset:%c16\n"
+        "ds_read_b128 %5, %13 offset:%c16\n"
+        "ds_read_b128 %6, %14 offset:%c16\n"
+        "ds_read_b128 %7, %15 offset:%c16\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]),
+          "=&v"(d[6]), "=&v"(d[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+          "n"(OFF)
+        : "memory");
+}
+
+template <int OFF>
+__device__ __forceinline__ void lds_read_tr_x8(u32x2 (&d)[8], const uint32_t (&a)[8])
+{
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%c16\n"
+        "ds_read_b64_tr_b16 %1, %9 offset:%c16\n"
+        "ds_read_b64_tr_b16 %2, %10 offset:%c16\n"
+        "ds_read_b64_tr_b16 %3, %11 offset:%c16\n"
+        "ds_read_b64_tr_b16 %4, %12 offset:%c16\n"
+        "ds_read_b64_tr_b16 %5, %13 offset:%c16\n"
+        "ds_read_b64_tr_b16 %6, %14 offset:%c16\n"
+        "ds_read_b64_tr_b16 %7, %15 offset:%c16\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]),
+          "=&v"(d[6]), "=&v"(d[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+          "n"(OFF)
+        : "memory");
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x16(bf16x4 a, bf16x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 // Explicit waits for direct-to-LDS loads, which produce no register the

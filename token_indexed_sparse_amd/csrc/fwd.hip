@@ -24,9 +24,12 @@
 //    which is exactly the B operand layout of O^T = V^T P^T, so P never leaves
 //    registers. Each lane owns one head: the running maximum and sum are per
 //    lane and the rescale of O is a per-lane scalar.
-//  * The running maximum is raised only when a chunk exceeds it by more than
-//    2^8 (in exp2 units), so the 64-register rescale of O is rare; P then
-//    stays below 256, which FP32 and the bf16 split handle exactly as before.
+//  * The first chunk fixes each head's reference maximum. P = exp2(s - ref)
+//    may then grow up to 2^64, which FP32 and the bf16 split carry exactly as
+//    well; a chunk further above the reference raises it and has the row
+//    recomputed from its first chunk (the result is the same, only the work
+//    repeats). O is therefore never rescaled inside the loop, and its
+//    accumulators stay in the matrix-core registers.
 //  * P is split into bf16 high and low parts (two MFMAs) so that the FP32
 //    output keeps about 16 mantissa bits of P; the normaliser is summed from
 //    the FP32 P.
@@ -41,7 +44,7 @@ namespace qsa {
 namespace {
 
 constexpr int kChunk = 32;            // key slots per step (two 16-slot MFMA blocks)
-constexpr float kRescaleSlack = 8.f;  // log2 of the largest unnormalised P
+constexpr float kSlack = 64.f;        // log2 of the largest unnormalised P
 
 // Body of k_forward; ks and vs are the wave's K and V staging regions.
 __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_char *vs)
@@ -92,28 +95,43 @@ __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_
         QSA_WAIT_VM(0);
     }
 
-    // Lane l fetches the key of slot ch*32 + (l & 31); slots at or past n give
-    // no key.
+    // Gather instruction s stages key slot s (lanes 0..31) and slot s + 16
+    // (lanes 32..63), each lane one 16-byte chunk of the row, so every
+    // instruction reads two whole rows. A lane's 16 keys per chunk (slots
+    // 16h .. 16h+15 for its half h) are fetched one chunk ahead with four
+    // 16-byte loads; slots at or past n read as zero.
+    const int half = lane >> 5;
     const rsrc_t rkeys = make_rsrc(p.row_keys + row * p.W, (uint32_t)(p.W * 4));
-    auto fetch_key = [&](int ch) -> int {
-        const int slot = ch * kChunk + (lane & 31);
-        const int kk = (int)__builtin_amdgcn_raw_buffer_load_b32(
-            rkeys, slot < n ? (uint32_t)slot * 4 : kOutOfRange, 0, 0);
-        return slot < n ? kk : -1;
-    };
-    // Per-lane byte offsets of the 16 gather instructions of a chunk.
-    auto offsets = [&](int kk, uint32_t (&off)[16]) {
-        const uint32_t mine = kk >= 0 ? (uint32_t)kk * row_bytes : kOutOfRange;
+    auto fetch_keys = [&](int ch, uint4 (&kk)[4]) {
+        const int base = ch * kChunk + 16 * half;
 #pragma unroll
-        for (int s = 0; s < 16; ++s) {
-            const uint32_t e = __builtin_amdgcn_readlane(mine, 2 * s);
-            const uint32_t o = __builtin_amdgcn_readlane(mine, 2 * s + 1);
-            off[s] = ((lane >> 5) ? o : e) + ((uint32_t)dma_chunk(lane, s) << 4);
+        for (int q = 0; q < 4; ++q)
+            kk[q] = buf_load16(rkeys, base + 4 * q < n ? (uint32_t)(base + 4 * q) * 4 : kOutOfRange);
+    };
+    // Row slot j sits at rowbase(j) = (j & 15) * 1024 + (j >> 4) * 512 with
+    // its chunks swizzled by swz_mask(j & 15); lane l of instruction s holds
+    // chunk (l & 31) ^ swz_mask(s) of slot s + 16h.
+    const uint32_t lane16 = (uint32_t)((lane & 31) << 4);
+    auto offsets = [&](const uint4 (&kk)[4], int ch, uint32_t (&off)[16]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t k4[4] = {kk[q].x, kk[q].y, kk[q].z, kk[q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s2 = 4 * q + e;
+                // key < 2^19 and row_bytes < 2^21: the 24-bit multiply-add is exact
+                off[s2] = __umul24(k4[e], row_bytes) + (lane16 ^ (uint32_t)(swz_mask(s2) << 4));
+            }
+        }
+        if ((ch + 1) * kChunk > n) {  // the last chunk: slots past n read zeros
+            const int rem = n - ch * kChunk - 16 * half;
+#pragma unroll
+            for (int s2 = 0; s2 < 16; ++s2) off[s2] = s2 < rem ? off[s2] : kOutOfRange;
         }
     };
     auto gather = [&](rsrc_t r, lds_char *dst, const uint32_t (&off)[16]) {
 #pragma unroll
-        for (int s = 0; s < 16; ++s) dma16(r, dst + s * 1024, off[s]);
+        for (int s2 = 0; s2 < 16; ++s2) dma16(r, dst + s2 * 1024, off[s2]);
     };
 
     const float c = p.scale * 1.4426950408889634f;  // scores in log2 units
@@ -122,106 +140,128 @@ __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_
 #pragma unroll
     for (int db = 0; db < 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // K read: lane (key slot col, quad) takes chunk 4t + quad of its key.
+    // K read: lane (key slot col, quad) takes chunk 4t + quad of slot kb*16 +
+    // col. V transposed read: lane i of group quad names the 8-byte unit of
+    // slot kb*16 + 4*quad + i/4 holding columns 16db + 4(i%4) .. +3, which is
+    // half (i & 1) of chunk 2db + ((i >> 1) & 1); with the swizzle that
+    // chunk's slot is 2 (db ^ (m >> 1)) + (((i >> 1) & 1) ^ (m & 1)) for the
+    // row's mask m. Slot kb*16 + j lies 512 kb above slot j.
     const int kmask = swz_mask(col);
-    // V transposed read: lane i of group quad names the 8-byte unit of key
-    // 4*quad + i/4 holding columns 16db + 4(i%4) .. +3, which is half (i & 1)
-    // of chunk 2db + ((i >> 1) & 1); with the swizzle that chunk's slot is
-    // 2 (db ^ (m >> 1)) + (((i >> 1) & 1) ^ (m & 1)) for the row's mask m.
     const int vkey = 4 * quad + (col >> 2);
     const int vm = swz_mask(vkey);
-    const int vbase_lane = vkey * 512 + ((((col >> 1) & 1) ^ (vm & 1)) << 4) + (col & 1) * 8;
+    const int vbase_lane = vkey * 1024 + ((((col >> 1) & 1) ^ (vm & 1)) << 4) + (col & 1) * 8;
     const int vxor = vm >> 1;
 
     const int nchunks = (n + kChunk - 1) / kChunk;
-    int knext = fetch_key(1);
-    uint32_t off[16];
-    offsets(fetch_key(0), off);
-    gather(rk, ks, off);
-    gather(rv, vs, off);
-
-    for (int ch = 0; ch < nchunks; ++ch) {
-        // The compiler orders every LDS read after all direct-to-LDS loads
-        // issued before it, so a chunk's K and V are read out whole, and the
-        // next chunk is gathered only then, overlapping this chunk's products
-        // and softmax.
-        QSA_WAIT_VM(0);
-        offsets(knext, off);  // next chunk
-        knext = fetch_key(ch + 2);
-        uint4 kr[2][8];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-                kr[kb][t] = lds_read16(ks + (kb * 16 + col) * 512 + (((4 * t + quad) ^ kmask) << 4));
-        uint2 va[2][16];
-#pragma unroll
-        for (int db = 0; db < 16; ++db) {
-            const int o = vbase_lane + ((db ^ vxor) << 5);
-            va[0][db] = lds_read_tr(vs + o);
-            va[1][db] = lds_read_tr(vs + o + 16 * 512);
-        }
-        QSA_WAIT_LDS();  // both regions are free
+    bool restart = false;
+    for (;;) {
+        uint4 kn[4];
+        uint32_t off[16];
+        fetch_keys(0, kn);
+        offsets(kn, 0, off);
+        fetch_keys(1, kn);
         gather(rk, ks, off);
         gather(rv, vs, off);
 
-        f32x4 st[2];
+        for (int ch = 0; ch < nchunks; ++ch) {
+            // The compiler orders every LDS read after all direct-to-LDS loads
+            // issued before it, so a chunk's K and V are read out whole, and
+            // the next chunk is gathered only then, overlapping this chunk's
+            // products and softmax.
+            QSA_WAIT_VM(0);
+            offsets(kn, ch + 1, off);  // next chunk
+            fetch_keys(ch + 2, kn);
+            uint4 kr[2][8];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) a = mfma_16x16x32(as_bf16x8(kr[kb][t]), qf[t], a);
-            st[kb] = a;
-        }
+                for (int t = 0; t < 8; ++t)
+                    kr[kb][t] = lds_read16(ks + col * 1024 + 512 * kb + (((4 * t + quad) ^ kmask) << 4));
+            uint2 va[2][16];
+#pragma unroll
+            for (int db = 0; db < 16; ++db) {
+                const int o = vbase_lane + ((db ^ vxor) << 5);
+                va[0][db] = lds_read_tr(vs + o);
+                va[1][db] = lds_read_tr(vs + o + 512);
+            }
+            QSA_WAIT_LDS();  // both regions are free
+            gather(rk, ks, off);
+            gather(rv, vs, off);
 
-        // Online softmax; lane holds key slots kb*16 + 4*quad + e of head col.
-        float t[2][4];
-        float mx = -INFINITY;
+            f32x4 st[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb) {
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bool valid = ch * kChunk + kb * 16 + 4 * quad + e < n;
-                t[kb][e] = valid ? st[kb][e] * c : -INFINITY;
-                mx = fmaxf(mx, t[kb][e]);
+                for (int t = 0; t < 8; ++t) a = mfma_16x16x32(as_bf16x8(kr[kb][t]), qf[t], a);
+                st[kb] = a;
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = exp2f(m_run - m_new);
+
+            // Softmax numerators; lane holds key slots kb*16 + 4*quad + e of head col.
+            float t[2][4];
+            float mx = -INFINITY;
+            if ((ch + 1) * kChunk <= n) {
 #pragma unroll
-            for (int db = 0; db < 16; ++db) acc[db] *= alpha;
-            l_part *= alpha;
-            m_run = m_new;
-        }
-        float pr[8];
-        float psum = 0.f;
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+                    for (int e = 0; e < 4; ++e) {
+                        t[kb][e] = st[kb][e] * c;
+                        mx = fmaxf(mx, t[kb][e]);
+                    }
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float pv = exp2f(t[kb][e] - m_run);
-                pr[kb * 4 + e] = pv;
-                psum += pv;
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const bool valid = ch * kChunk + kb * 16 + 4 * quad + e < n;
+                        t[kb][e] = valid ? st[kb][e] * c : -INFINITY;
+                        mx = fmaxf(mx, t[kb][e]);
+                    }
             }
-        l_part += psum;
-        // B operand P^T: slot j of lane group quad is key 4*quad+j (j<4) or
-        // 16+4*quad+j-4 (j>=4): the lane's own accumulator values.
-        uint32_t hi[4], lo[4];
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            // The first chunk fixes each head's reference maximum (O and the
+            // sum are still zero). A later chunk more than 2^kSlack above it
+            // raises the reference and has the whole row recomputed, so O is
+            // never rescaled inside the loop.
+            if (ch == 0) {
+                m_run = fmaxf(m_run, mx);
+            } else if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0) {
+                m_run = fmaxf(m_run, mx);
+                restart = true;
+                break;
+            }
+            float pr[8];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) split_bf16x2(pr[2 * x], pr[2 * x + 1], hi[x], lo[x]);
-        const bf16x8 pb_hi = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
-        const bf16x8 pb_lo = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int db = 0; db < 16; ++db) {
-            const bf16x8 v8 =
-                as_bf16x8(make_uint4(va[0][db].x, va[0][db].y, va[1][db].x, va[1][db].y));
-            acc[db] = mfma_16x16x32(v8, pb_hi, acc[db]);
-            acc[db] = mfma_16x16x32(v8, pb_lo, acc[db]);
+                for (int e = 0; e < 4; ++e) {
+                    const float pv = __builtin_amdgcn_exp2f(t[kb][e] - m_run);
+                    pr[kb * 4 + e] = pv;
+                    l_part += pv;
+                }
+            // B operand P^T: slot j of lane group quad is key 4*quad+j (j<4) or
+            // 16+4*quad+j-4 (j>=4): the lane's own accumulator values.
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) split_bf16x2(pr[2 * x], pr[2 * x + 1], hi[x], lo[x]);
+            const bf16x8 pb_hi = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+            const bf16x8 pb_lo = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+#pragma unroll
+            for (int db = 0; db < 16; ++db) {
+                const bf16x8 v8 =
+                    as_bf16x8(make_uint4(va[0][db].x, va[0][db].y, va[1][db].x, va[1][db].y));
+                acc[db] = mfma_16x16x32(v8, pb_hi, acc[db]);
+                acc[db] = mfma_16x16x32(v8, pb_lo, acc[db]);
+            }
         }
+        QSA_WAIT_VM(0);  // no gather may outlive this pass or the wave's LDS
+        if (!restart) break;
+        restart = false;
+#pragma unroll
+        for (int db = 0; db < 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        l_part = 0.f;
     }
-    QSA_WAIT_VM(0);  // no gather may outlive the wave's LDS
 
     float l = l_part + __shfl_xor(l_part, 16);
     l += __shfl_xor(l, 32);
