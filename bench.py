@@ -34,15 +34,19 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "QSA fwd+bwd sparse TFLOP/s (12Q/1KV, d=256) and % of MFMA peak, 1 GPU"
 
-# Algorithmic FLOP per (distinct valid pair, query head), by kernel.
+# Algorithmic FLOP per (distinct valid pair, query head), by kernel, and which
+# pairs each kernel computes: "partial" = pairs outside full 128 x 128 tiles
+# (gathered kernels), "full" = pairs inside them (dense kernels).
 FLOP_PER_PAIR_HEAD = {
-    "forward": 4 * 256,   # S = QK^T and O = PV
-    "dq": 6 * 256,        # S, dP = dO V^T, dQ = dS K
-    "dkdv": 8 * 256,      # S, dP, dV = P^T dO, dK = dS^T Q
+    "forward": 4 * 256,        # S = QK^T and O = PV
+    "forward_dense": 4 * 256,
+    "dq": 6 * 256,             # S, dP = dO V^T, dQ = dS K
+    "dkdv": 8 * 256,           # S, dP, dV = P^T dO, dK = dS^T Q
 }
+KERNEL_PAIRS = {"forward": "partial", "forward_dense": "full", "dq": "all", "dkdv": "all"}
 COUNTED_FWD = 4 * 256
 COUNTED_BWD = 10 * 256
-FWD_STAGES = ["preprocess_fwd", "forward"]
+FWD_STAGES = ["preprocess_fwd", "forward", "forward_dense"]
 BWD_STAGES = ["preprocess_bwd", "delta", "dq", "dkdv", "dkdv_reduce"]
 
 
@@ -57,8 +61,28 @@ def pairs_per_row(routes: np.ndarray, Skv: int) -> np.ndarray:
     return out
 
 
+def full_tile_pairs(routes: np.ndarray, Sq: int, Skv: int) -> int:
+    """Pairs inside full 128 x 128 tiles (every row of the query tile selects every key of
+    the key tile; edge tiles are never full)."""
+    B = routes.shape[0]
+    nQT, nKT = (Sq + 127) // 128, (Skv + 127) // 128
+    total = 0
+    for b in range(B):
+        cnt = np.zeros((nQT, nKT), np.int64)
+        r = routes[b]
+        for a in range(0, Sq, 1024):
+            c = r[a:a + 1024].astype(np.int64)
+            s = np.sort(np.where((c >= 0) & (c < Skv), c, -1), axis=-1)
+            keep = s >= 0
+            keep[:, 1:] &= s[:, 1:] != s[:, :-1]
+            rows = np.broadcast_to(np.arange(a, a + c.shape[0])[:, None] // 128, s.shape)
+            np.add.at(cnt, (rows[keep], s[keep] // 128), 1)
+        total += int((cnt == 128 * 128).sum()) * 128 * 128
+    return total
+
+
 TRAFFIC_SOURCES = ("token_indexed_sparse_amd/csrc/common.h", "token_indexed_sparse_amd/csrc/bwd.hip",
-                   "token_indexed_sparse_amd/csrc/fwd.hip")
+                   "token_indexed_sparse_amd/csrc/fwd.hip", "token_indexed_sparse_amd/csrc/dense.hip")
 
 
 def measured_traffic(workload: str, kernel: str):
@@ -179,6 +203,8 @@ def main() -> int:
     inp = synth.make_inputs(wl)
     nnz_row = pairs_per_row(inp.routes, wl.Skv)
     nnz = int(nnz_row.sum())
+    nnz_full = full_tile_pairs(inp.routes, wl.Sq, wl.Skv)
+    pairs = {"all": nnz, "full": nnz_full, "partial": nnz - nnz_full}
 
     dev = torch.device("cuda:0")
 
@@ -208,8 +234,9 @@ def main() -> int:
     hip = hip_runtime()
     stream = torch.cuda.current_stream().cuda_stream
     K, W = args.steps, args.warmup
-    fev = [Events(hip, 3) for _ in range(K)]
-    bev = [Events(hip, 6) for _ in range(K)]
+    NF, NB = len(FWD_STAGES), len(BWD_STAGES)
+    fev = [Events(hip, NF + 1) for _ in range(K)]
+    bev = [Events(hip, NB + 1) for _ in range(K)]
 
     def step(i=None):
         fe = ctypes.cast(fev[i].ev, ctypes.c_void_p) if i is not None else None
@@ -217,13 +244,13 @@ def main() -> int:
         st = lib.qsa_forward_timed(ctypes.byref(dims), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                    routes.data_ptr(), wl.scale, out.data_ptr(), out32.data_ptr(),
                                    lse.data_ptr(), ws_f.data_ptr(), ws_f.numel(), stream,
-                                   fe, 3 if fe is not None else 0)
+                                   fe, NF + 1 if fe is not None else 0)
         assert st == 0, st
         st = lib.qsa_backward_timed(ctypes.byref(dims), g.data_ptr(), q.data_ptr(), k.data_ptr(),
                                     v.data_ptr(), out32.data_ptr(), lse.data_ptr(),
                                     routes.data_ptr(), wl.scale, dq.data_ptr(), dk.data_ptr(),
                                     dv.data_ptr(), ws_b.data_ptr(), ws_b.numel(), stream,
-                                    be, 6 if be is not None else 0)
+                                    be, NB + 1 if be is not None else 0)
         assert st == 0, st
 
     print(f"[bench] warmup {W}", file=sys.stderr, flush=True)
@@ -238,19 +265,18 @@ def main() -> int:
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / K
     stage_ms = {}
-    for name, a in zip(FWD_STAGES, range(2)):
+    for a, name in enumerate(FWD_STAGES):
         stage_ms[name] = float(np.mean([e.elapsed(a, a + 1) for e in fev]))
-    for name, a in zip(BWD_STAGES, range(5)):
+    for a, name in enumerate(BWD_STAGES):
         stage_ms[name] = float(np.mean([e.elapsed(a, a + 1) for e in bev]))
-    fwd_ms = float(np.mean([e.elapsed(0, 2) for e in fev]))
-    bwd_ms = float(np.mean([e.elapsed(0, 5) for e in bev]))
+    fwd_ms = float(np.mean([e.elapsed(0, NF) for e in fev]))
+    bwd_ms = float(np.mean([e.elapsed(0, NB) for e in bev]))
     flop_fwd = COUNTED_FWD * wl.Hq * nnz
     flop_bwd = COUNTED_BWD * wl.Hq * nnz
     value = (flop_fwd + flop_bwd) / (ms_step * 1e-3) / 1e12
 
-    kernels = {"forward": "forward", "dq": "dq", "dkdv": "dkdv"}
-    dom = max(kernels, key=lambda s: stage_ms[s])
-    dom_flop = FLOP_PER_PAIR_HEAD[dom] * wl.Hq * nnz
+    dom = max(KERNEL_PAIRS, key=lambda s: stage_ms[s])
+    dom_flop = FLOP_PER_PAIR_HEAD[dom] * wl.Hq * pairs[KERNEL_PAIRS[dom]]
     achieved = dom_flop / (stage_ms[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
@@ -271,7 +297,7 @@ def main() -> int:
         "warmup": W, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "Sq": wl.Sq, "Skv": wl.Skv, "Hq": wl.Hq,
-                   "Hkv": wl.Hkv, "D": wl.D, "W": wl.W, "nnz_pairs": nnz,
+                   "Hkv": wl.Hkv, "D": wl.D, "W": wl.W, "nnz_pairs": nnz, "full_tile_pairs": nnz_full,
                    "flop_per_step": flop_fwd + flop_bwd, "parallelism": "single GPU"},
         "mfma_peak_frac": value / PEAK_BF16_TFLOPS,
         "forward_tflops": flop_fwd / (fwd_ms * 1e-3) / 1e12,

@@ -63,6 +63,29 @@ def test_small_cases_full_parity(case):
     _full_compare(inp, 0.0625, run)
 
 
+# Full 128 x 128 tiles (the dense path) next to gathered keys: the hand-over
+# between the two forward passes, rows with no gathered keys, causal-complete
+# and all-full tile rows, edge tiles that are chosen whole but cannot be full,
+# and large scores in a full key tile that make the dense pass raise its
+# reference maximum.
+TILED = [
+    dict(seed=51, B=1, Sq=384, Skv=384, Hq=12, Hkv=1, p_full=0.5, extra=30),
+    dict(seed=52, B=2, Sq=300, Skv=520, Hq=24, Hkv=2, p_full=0.6, extra=10, bare_rows=True),
+    dict(seed=53, B=1, Sq=384, Skv=384, Hq=12, Hkv=1, causal=True, extra=0),
+    dict(seed=54, B=1, Sq=256, Skv=384, Hq=12, Hkv=1, p_full=0.5, extra=20, loud_keys=8.0),
+    dict(seed=55, B=1, Sq=256, Skv=256, Hq=12, Hkv=1, all_keys=True, extra=0),
+]
+
+
+@pytest.mark.parametrize("case", TILED, ids=lambda c: f"seed{c['seed']}")
+def test_full_tile_cases_parity(case):
+    log(f"case {case}")
+    inp = synth.tiled_case(**case)
+    run = GpuRun(inp, 0.0625)
+    check_preprocess_exact(inp.routes, case["Skv"], run.routes)
+    _full_compare(inp, 0.0625, run)
+
+
 def test_int64_routes_huge_values_match_int32():
     inp = synth.random_case(41, 1, 150, 140, 12, 1, 30, route_dtype=np.int64)
     log("int64 routes with values beyond 2^31")

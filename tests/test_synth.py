@@ -94,3 +94,34 @@ def test_random_case_has_padding_duplicates_and_invalid():
                for x in r.reshape(-1, 16))
     assert dups > 0
     assert ((r == -1).all(-1)).sum() >= 2
+
+
+def test_tiled_cases_have_full_and_partial_tiles():
+    import oracle
+    for kw, want_partial in ((dict(seed=51, B=1, Sq=384, Skv=384, Hq=12, Hkv=1, p_full=0.5,
+                                   extra=30), True),
+                             (dict(seed=52, B=2, Sq=300, Skv=520, Hq=24, Hkv=2, p_full=0.6,
+                                   extra=10, bare_rows=True), True),
+                             (dict(seed=53, B=1, Sq=384, Skv=384, Hq=12, Hkv=1, causal=True,
+                                   extra=0), True),
+                             (dict(seed=55, B=1, Sq=256, Skv=256, Hq=12, Hkv=1, all_keys=True,
+                                   extra=0), False)):
+        inp = synth.tiled_case(**kw)
+        memb, _ = oracle.membership(inp.routes, kw["Skv"])
+        kinds = oracle.tiles(memb, kw["Skv"])["kinds"]
+        assert (kinds == 2).any(), kw
+        assert ((kinds == 1).any()) == want_partial, kw
+        # route slots hold a duplicate and an out-of-range value on every row
+        r = inp.routes
+        assert ((r == kw["Skv"] + 3).sum(-1) == 1).all()
+    # causal-complete: full strictly below the diagonal, partial on it
+    inp = synth.tiled_case(53, 1, 384, 384, 12, 1, causal=True, extra=0)
+    memb, _ = oracle.membership(inp.routes, 384)
+    kinds = oracle.tiles(memb, 384)["kinds"][0]
+    assert (kinds == np.array([[1, 0, 0], [2, 1, 0], [2, 2, 1]])).all()
+    # bare rows: odd query tiles of batch 0 select only whole tiles
+    inp = synth.tiled_case(52, 2, 300, 520, 24, 2, p_full=0.6, extra=10, bare_rows=True)
+    for row in inp.routes[0, 128:256]:
+        keys = np.unique(row[(row >= 0) & (row < 520)])
+        for t in np.unique(keys // 128):
+            assert np.isin(np.arange(128 * t, min(128 * t + 128, 520)), keys).all()

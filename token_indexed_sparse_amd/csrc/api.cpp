@@ -44,8 +44,8 @@ qsa_status check_dims(const qsa_dims *d)
 }
 
 struct Layout {
-    size_t memb, has, mbits, row_keys, row_cnt, tile_cnt, kinds, fpc, fpi, ffc, ffi, rpc, rpi, rfc,
-        rfi, delta, kv_part, kv_flag, total;
+    size_t memb, has, mbits, row_keys, row_cnt, pkeys, pcnt, tile_cnt, kinds, fpc, fpi, ffc, ffi,
+        rpc, rpi, rfc, rfi, fstate, delta, kv_part, kv_flag, total;
 };
 
 // which: 0 forward, 1 backward, 2 preprocess (only tile counts and, if the
@@ -69,6 +69,8 @@ Layout layout(const qsa_dims *d, int which)
     L.mbits = which == 1 ? take((size_t)(rows * (stride / 32)) * 4) : none;
     L.row_keys = take((size_t)(rows * d->W) * 4);
     L.row_cnt = take((size_t)rows * 4);
+    L.pkeys = which == 2 ? none : take((size_t)(rows * d->W) * 4);
+    L.pcnt = which == 2 ? none : take((size_t)rows * 4);
     L.tile_cnt = take((size_t)(d->B * nQT * nKT) * 4);
     if (which == 2) {
         L.kinds = L.fpc = L.fpi = L.ffc = L.ffi = L.rpc = L.rpi = L.rfc = L.rfi = none;
@@ -83,9 +85,14 @@ Layout layout(const qsa_dims *d, int which)
         L.rfc = take((size_t)(d->B * nKT) * 4);
         L.rfi = take((size_t)(d->B * nKT * nQT) * 4);
     }
+    L.fstate = which == 0 ? take((size_t)(d->B * d->Hq * d->Sq) * 8) : none;
     L.delta = which == 1 ? take((size_t)(d->B * d->Hq * d->Sq) * 4) : none;
     const int64_t nseg = (nQT + kSegTiles - 1) / kSegTiles;
-    L.kv_part = which == 1 ? take((size_t)(d->B * d->Hkv * nseg * stride) * 2 * kD * 4) : none;
+    // The dK/dV partial sums and the dQ hand-over are never live together
+    // (dQ finishes before dK/dV starts), so they share one region.
+    const size_t kv_bytes = (size_t)(d->B * d->Hkv * nseg * stride) * 2 * kD * 4;
+    const size_t dq_bytes = (size_t)(rows * d->Hq) * kD * 4;
+    L.kv_part = which == 1 ? take(kv_bytes > dq_bytes ? kv_bytes : dq_bytes) : none;
     L.kv_flag = which == 1 ? take((size_t)(d->B * d->Hkv * nseg * (stride / 16))) : none;
     L.total = off;
     return L;
@@ -143,6 +150,10 @@ void carve(Problem &p, const Layout &L, void *ws)
     if (L.mbits != none) p.mbits = reinterpret_cast<uint32_t *>(w + L.mbits);
     p.row_keys = reinterpret_cast<int32_t *>(w + L.row_keys);
     p.row_cnt = reinterpret_cast<int32_t *>(w + L.row_cnt);
+    if (L.pkeys != none) {
+        p.pkeys = reinterpret_cast<int32_t *>(w + L.pkeys);
+        p.pcnt = reinterpret_cast<int32_t *>(w + L.pcnt);
+    }
     p.tile_cnt = reinterpret_cast<int32_t *>(w + L.tile_cnt);
     if (L.kinds != none) {
         p.kinds = reinterpret_cast<int32_t *>(w + L.kinds);
@@ -155,8 +166,12 @@ void carve(Problem &p, const Layout &L, void *ws)
         p.rev_f_cnt = reinterpret_cast<int32_t *>(w + L.rfc);
         p.rev_f_idx = reinterpret_cast<int32_t *>(w + L.rfi);
     }
+    if (L.fstate != none) p.fstate = reinterpret_cast<float *>(w + L.fstate);
     if (L.delta != none) p.delta = reinterpret_cast<float *>(w + L.delta);
-    if (L.kv_part != none) p.kv_part = reinterpret_cast<float *>(w + L.kv_part);
+    if (L.kv_part != none) {
+        p.kv_part = reinterpret_cast<float *>(w + L.kv_part);
+        p.dq_part = p.kv_part;
+    }
     if (L.kv_flag != none) p.kv_flag = reinterpret_cast<uint8_t *>(w + L.kv_flag);
 }
 
@@ -222,9 +237,12 @@ qsa_status qsa_forward_timed(const qsa_dims *dims, const void *q, const void *k,
     if (events && n_events < QSA_FORWARD_STAGES + 1) return QSA_ERR_NULL;
     if (mark(events, 0, s) != hipSuccess) return QSA_ERR_DEVICE;
     if (launch_preprocess(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (launch_partial_keys(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
     if (mark(events, 1, s) != hipSuccess) return QSA_ERR_DEVICE;
     if (launch_forward(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
     if (mark(events, 2, s) != hipSuccess) return QSA_ERR_DEVICE;
+    if (launch_forward_dense(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 3, s) != hipSuccess) return QSA_ERR_DEVICE;
     return QSA_OK;
 }
 

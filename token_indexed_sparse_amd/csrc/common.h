@@ -32,12 +32,19 @@ struct Problem {
     uint8_t *memb, *has_routes;
     uint32_t *mbits;  // bit-packed membership [B*Sq, stride/32] (backward only)
     int32_t *row_keys, *row_cnt;
+    // Row key lists without the keys of full tiles (those take the dense
+    // path): same layout as row_keys, only the first pcnt[row] entries valid.
+    int32_t *pkeys, *pcnt;
     int32_t *tile_cnt, *kinds;
     int32_t *fwd_p_cnt, *fwd_p_idx, *fwd_f_cnt, *fwd_f_idx;
     int32_t *rev_p_cnt, *rev_p_idx, *rev_f_cnt, *rev_f_idx;
     // forward outputs
     uint16_t *out;
     float *out_fp32, *lse;
+    // Hand-off from the gathered to the dense forward for rows whose tile row
+    // has full tiles: out_fp32 holds the unnormalised output and fstate the
+    // (reference maximum in log2 units, sum) pair, [B, Hq, Sq] x 2.
+    float *fstate;
     // backward
     float *delta;
     uint16_t *dq, *dk, *dv;
@@ -46,10 +53,16 @@ struct Problem {
     float *kv_part;
     uint8_t *kv_flag;
     int64_t nseg;
+    // Hand-off from the gathered to the dense dQ: unscaled FP32 sums
+    // [B, Sq, Hq, 256] of the rows whose tile row has full tiles.
+    float *dq_part;
 };
 
 hipError_t launch_preprocess(const Problem &p, hipStream_t s);
+hipError_t launch_partial_keys(const Problem &p, hipStream_t s);
 hipError_t launch_forward(const Problem &p, hipStream_t s);
+hipError_t launch_forward_dense(const Problem &p, hipStream_t s);
+hipError_t launch_dq_dense(const Problem &p, hipStream_t s);
 hipError_t launch_delta(const Problem &p, hipStream_t s);
 hipError_t launch_dq(const Problem &p, hipStream_t s);
 hipError_t launch_dkdv(const Problem &p, hipStream_t s);
@@ -291,6 +304,39 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(bf16x4 a, bf16x4 b, f32x4 c)
 // Blocks are dispatched round-robin over the 8 XCDs (block b runs on XCD
 // b % 8). Map them so that every XCD works on one contiguous range of logical
 // blocks: neighbouring rows or key groups then share that XCD's L2.
+// Direct-to-LDS loads written in assembly. The compiler tracks its own
+// direct-to-LDS loads, and when it reuses one of their address registers
+// while the load is in flight it waits for every load of the wave, which
+// drains a staging pipeline. These blocks carry their own M0 set-up (the
+// kernels that use them keep nothing else in M0, so the clobber loses
+// nothing); their callers order the LDS reads after them with counted waits
+// and a work-group barrier. Descriptor words: 48-bit base, stride 0,
+// num_records, raw 32-bit data format.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
+// 64 lanes x 16 bytes: lane l's bytes land at LDS address lds + 16 l.
+__device__ __forceinline__ void dma16_asm(i32x4 r, uint32_t lds, uint32_t voff)
+{
+    asm volatile("s_mov_b32 m0, %0\n s_nop 0\n buffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(r)
+                 : "memory", "m0");
+}
+
+// An address that the compiler cannot know before this point: LDS reads made
+// through it stay after the barrier that precedes it.
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t x)
+{
+    asm volatile("" : "+s"(x) : : "memory");
+    return x;
+}
+
 __device__ __forceinline__ int64_t xcd_logical_block(int64_t b, int64_t n)
 {
     const int64_t x = b & 7, y = b >> 3;

@@ -1,0 +1,339 @@
+// Full 128 x 128 tiles of route-set grouped-query attention on gfx950.
+//
+// Definition: cuDNN Frontend "Query Sparse Attention (QSA)" page, section
+// "Selection and components" (same scores, softmax and products as the
+// gathered kernels) and its note that the kernel computes dense tiles where
+// a tile of queries selects a whole key span and gathers only for the rest.
+// A tile is full when all 128 query rows select all 128 keys of the key tile
+// ("fa4_qsa" page, `_block_kinds`: count == 128 * 128); such pairs are
+// exactly the keys the partial key lists leave out.
+//
+// Design (one work group of four waves per query tile, KV head and block of
+// 128 (row, head) vectors):
+//  * Inside a full tile every (row, head) vector of the tile sees the same
+//    keys, so the MFMA blocks take 16 consecutive vectors of the tile (rows
+//    and heads mixed) instead of the 12 heads of one row: no padding lanes.
+//    A wave owns two such blocks (32 vectors), a work group 128, and the 12
+//    work groups of a query tile are consecutive blocks, which the XCD-aware
+//    mapping keeps on one XCD so the key tiles they share stay in its L2.
+//  * Keys come in chunks of 32 from the tile row's full key tiles. A chunk's
+//    K and V rows are contiguous, staged once per work group into LDS by
+//    direct-to-LDS loads (each wave issues a quarter) in the swizzled layout
+//    of the gathered forward, double-buffered: the next chunk flies while
+//    the current one is computed. A wave waits for its own loads, then the
+//    work-group barrier makes every wave's loads visible and frees the other
+//    buffer.
+//  * S^T = K Q^T and O^T = V^T P^T exactly as in the gathered forward (K in
+//    the row layout, V through the transposing read, P^T straight from the
+//    accumulators, P as bf16 high + low), per vector block.
+//  * The forward starts from the state the gathered pass handed over
+//    (unnormalised output, reference maximum, sum) and rescales only when a
+//    chunk rises more than 2^64 above the reference, which random-scale
+//    scores never do; it then writes out_fp32, out and lse.
+#include "common.h"
+
+namespace qsa {
+
+namespace {
+
+constexpr int kDenseWaves = 4;
+constexpr int kVecBlocks = 2;                                  // 16-vector blocks per wave
+constexpr int kGroupVecs = kDenseWaves * 16 * kVecBlocks;      // vectors per work group
+constexpr int kTileVecs = kTile * kGroup;                      // vectors of a query tile
+constexpr int kVBlocks = kTileVecs / kGroupVecs;               // work groups per query tile
+constexpr int kKeys = 32;                                      // keys per staged chunk
+constexpr int kHalf = kKeys * 512;                             // K (or V) bytes of a chunk
+constexpr int kBuf = 2 * kHalf;                                // K then V
+constexpr float kSlack = 64.f;  // log2 of the largest unnormalised P
+static_assert(kTileVecs % kGroupVecs == 0, "work groups must tile the query tile");
+static_assert(kDenseWaves * 4 == 16, "each wave stages four of the 16 row pairs");
+
+struct DenseTile {
+    int64_t b, r;
+    int g, vb;
+};
+
+// Work group -> (batch, KV head, query tile, vector block); the vector blocks
+// of one query tile are consecutive logical blocks.
+__device__ __forceinline__ bool dense_tile(const Problem &p, DenseTile &t)
+{
+    const int64_t item = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int64_t per_bg = p.nQT * kVBlocks;
+    if (item >= p.B * p.Hkv * per_bg) return false;
+    const int64_t bg = item / per_bg;
+    const int64_t rem = item - bg * per_bg;
+    t.b = bg / p.Hkv;
+    t.g = (int)(bg - t.b * p.Hkv);
+    t.r = rem / kVBlocks;
+    t.vb = (int)(rem - t.r * kVBlocks);
+    return true;
+}
+
+__device__ __forceinline__ void forward_dense_item(const Problem &p, lds_char *buf,
+                                                   volatile uint32_t *redo_flag)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 15, quad = lane >> 4;
+    DenseTile dt;
+    if (!dense_tile(p, dt)) return;
+    const int64_t b = dt.b, r = dt.r;
+    const int g = dt.g;
+    const int fcnt = p.fwd_f_cnt[b * p.nQT + r];
+    if (fcnt == 0) return;
+    // The tile list was written by an earlier launch: read it as constant
+    // data, which gives scalar loads.
+    const __attribute__((address_space(4))) int32_t *fidx =
+        (const __attribute__((address_space(4))) int32_t *)(p.fwd_f_idx + (b * p.nQT + r) * p.nKT);
+
+    // Vector 16x + col of the wave: (row i, head) of the tile. Full tiles are
+    // never edge tiles, so every row exists.
+    int64_t vrow[kVecBlocks], sidx[kVecBlocks];
+#pragma unroll
+    for (int x = 0; x < kVecBlocks; ++x) {
+        const int v = dt.vb * kGroupVecs + wave * 16 * kVecBlocks + 16 * x + col;
+        const int rt = v / kGroup, hd = v - kGroup * rt;
+        const int64_t i = r * kTile + rt;
+        const int head = g * kGroup + hd;
+        vrow[x] = (b * p.Sq + i) * p.Hq + head;
+        sidx[x] = (b * p.Hq + head) * p.Sq + i;
+    }
+
+    // Q as the B operand: lane (vector col, quad) holds columns 32t + 8quad ..
+    // +7 for step t. The handed-over state: reference maximum and sum.
+    bf16x8 qf[kVecBlocks][8];
+    float m_hand[kVecBlocks], l_hand[kVecBlocks], m_ref[kVecBlocks];
+#pragma unroll
+    for (int x = 0; x < kVecBlocks; ++x) {
+        const uint16_t *qr = p.q + vrow[x] * kD + 8 * quad;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) qf[x][t] = as_bf16x8(*reinterpret_cast<const uint4 *>(qr + 32 * t));
+        const float2 st = *reinterpret_cast<const float2 *>(p.fstate + 2 * sidx[x]);
+        m_hand[x] = st.x;
+        l_hand[x] = st.y;
+        m_ref[x] = -INFINITY;
+    }
+    f32x4 acc[kVecBlocks][16];
+    float l_part[kVecBlocks];
+
+    // Staging: instruction s (0..15) puts key slot s (lanes 0..31) and s + 16
+    // (lanes 32..63) of a chunk at s * 1024, lane l taking chunk
+    // (l & 31) ^ swz_mask(s) of its row; wave w issues s = 4w .. 4w+3 for K
+    // and for V. The chunk's first key goes into the descriptors, so the lane
+    // offsets never change.
+    const uint32_t row_bytes = (uint32_t)(p.Hkv * kD * 2);
+    const uint16_t *kbase = p.k + (b * p.Skv * p.Hkv + g) * (int64_t)kD;
+    const uint16_t *vbase = p.v + (b * p.Skv * p.Hkv + g) * (int64_t)kD;
+    uint32_t loff[4];
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+        const int s = 4 * wave + y;
+        loff[y] = (uint32_t)(s + 16 * (lane >> 5)) * row_bytes +
+                  ((uint32_t)((lane & 31) ^ swz_mask(s)) << 4);
+    }
+    const uint32_t base = lds_addr(buf);
+    auto issue = [&](int c) {
+        const int64_t key0 = (int64_t)fidx[c >> 2] * kTile + (c & 3) * kKeys;
+        const i32x4 rk = rsrc_words(kbase + key0 * p.Hkv * kD, kKeys * row_bytes);
+        const i32x4 rv = rsrc_words(vbase + key0 * p.Hkv * kD, kKeys * row_bytes);
+        const uint32_t dst = base + (uint32_t)((c & 1) * kBuf);
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+            const uint32_t s = (uint32_t)(4 * wave + y);
+            dma16_asm(rk, dst + s * 1024, loff[y]);
+            dma16_asm(rv, dst + kHalf + s * 1024, loff[y]);
+        }
+    };
+
+    // Reads as in the gathered forward: K row layout, lane (key slot col,
+    // quad) takes chunk 4t + quad of slot kb*16 + col; V transposed, lane i of
+    // group quad names the 8-byte unit of slot kb*16 + 4*quad + i/4 holding
+    // columns 16db + 4(i%4) .. +3.
+    const int kmask = swz_mask(col);
+    const int vkey = 4 * quad + (col >> 2);
+    const int vm = swz_mask(vkey);
+    const int vlane = vkey * 1024 + ((((col >> 1) & 1) ^ (vm & 1)) << 4) + (col & 1) * 8;
+    const int vxor = vm >> 1;
+    const float c = p.scale * 1.4426950408889634f;  // scores in log2 units
+
+    auto compute = [&](uint32_t cb, bool first, auto rescale_tag) {
+        constexpr bool kRescale = decltype(rescale_tag)::value;
+        const lds_char *ks = (const lds_char *)(uintptr_t)cb;
+        const lds_char *vs = ks + kHalf;
+        // S^T one key block at a time (eight K reads live, not sixteen).
+        f32x4 st[kVecBlocks][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            uint4 kr[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                kr[t] = lds_read16(ks + col * 1024 + 512 * kb + (((4 * t + quad) ^ kmask) << 4));
+#pragma unroll
+            for (int x = 0; x < kVecBlocks; ++x) {
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < 8; ++t) a = mfma_16x16x32(as_bf16x8(kr[t]), qf[x][t], a);
+                st[x][kb] = a;
+            }
+        }
+        bf16x8 pb_hi[kVecBlocks], pb_lo[kVecBlocks];
+#pragma unroll
+        for (int x = 0; x < kVecBlocks; ++x) {
+            // lane holds key slots kb*16 + 4*quad + e of vector col
+            float tv[8];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    tv[kb * 4 + e] = st[x][kb][e] * c;
+                    mx = fmaxf(mx, tv[kb * 4 + e]);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            // The first chunk fixes the reference (the sums are still zero;
+            // the hand-over is added at the end, scaled to the reference).
+            if (first) m_ref[x] = fmaxf(m_hand[x], mx);
+            if (__builtin_amdgcn_ballot_w64(mx > m_ref[x] + kSlack) != 0) {
+                if constexpr (kRescale) {
+                    const float mn = fmaxf(m_ref[x], mx);
+                    const float f = __builtin_amdgcn_exp2f(m_ref[x] - mn);
+#pragma unroll
+                    for (int db = 0; db < 16; ++db) acc[x][db] *= f;
+                    l_part[x] *= f;
+                    m_ref[x] = mn;
+                } else {
+                    // Rare: raise the reference and have the work group redo
+                    // the full tiles from the hand-over on the rescaling path
+                    // (an empty hand-over has -inf). This pass's sums are
+                    // discarded, so P may keep using the raised reference.
+                    m_ref[x] = fmaxf(m_ref[x], mx);
+                    if (lane == 0) *redo_flag = 1;
+                }
+            }
+            float pr[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                pr[k] = __builtin_amdgcn_exp2f(tv[k] - m_ref[x]);
+                l_part[x] += pr[k];
+            }
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) split_bf16x2(pr[2 * k], pr[2 * k + 1], hi[k], lo[k]);
+            pb_hi[x] = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+            pb_lo[x] = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+        }
+        // O^T += V^T P^T, V read in two halves of eight column blocks.
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint2 va[2][8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int o = vlane + (((8 * h + j) ^ vxor) << 5);
+                va[0][j] = lds_read_tr(vs + o);
+                va[1][j] = lds_read_tr(vs + o + 512);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int db = 8 * h + j;
+                const bf16x8 v8 =
+                    as_bf16x8(make_uint4(va[0][j].x, va[0][j].y, va[1][j].x, va[1][j].y));
+#pragma unroll
+                for (int x = 0; x < kVecBlocks; ++x) {
+                    acc[x][db] = mfma_16x16x32(v8, pb_hi[x], acc[x][db]);
+                    acc[x][db] = mfma_16x16x32(v8, pb_lo[x], acc[x][db]);
+                }
+            }
+        }
+    };
+
+    const int nch = fcnt * (kTile / kKeys);
+    // The dense sums start at zero: no vector instruction touches the
+    // accumulators inside the loop, so they stay in the matrix-core registers.
+    auto init = [&]() {
+#pragma unroll
+        for (int x = 0; x < kVecBlocks; ++x) {
+#pragma unroll
+            for (int db = 0; db < 16; ++db) acc[x][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+            l_part[x] = 0.f;
+        }
+    };
+    // One pass over the full tiles. Without rescaling, a wave that needs it
+    // raises the flag; every wave reads the flag between the same two
+    // barriers, so all leave together and the pass reports it.
+    auto pass = [&](auto rescale_tag) {
+        constexpr bool kRescale = decltype(rescale_tag)::value;
+        issue(0);
+        bool redo = false;
+        for (int ch = 0; ch < nch; ++ch) {
+            QSA_WAIT_VM(0);  // this wave's loads of chunk ch have landed
+            __builtin_amdgcn_s_barrier();
+            if (!kRescale && opaque_u32(__builtin_amdgcn_readfirstlane(*redo_flag)) != 0u) {
+                redo = true;
+                break;
+            }
+            const uint32_t cb = opaque_u32(base + (uint32_t)((ch & 1) * kBuf));
+            if (ch + 1 < nch) issue(ch + 1);
+            compute(cb, !kRescale && ch == 0, rescale_tag);
+        }
+        QSA_WAIT_VM(0);
+        __builtin_amdgcn_s_barrier();
+        if (!kRescale && !redo) redo = opaque_u32(__builtin_amdgcn_readfirstlane(*redo_flag)) != 0u;
+        return redo;
+    };
+    init();
+    if (pass(std::false_type())) {
+        init();
+        pass(std::true_type());
+    }
+
+    // O = (dense sums + f * hand-over) / (dense sum + f * hand-over sum), with
+    // f = 2^(m_hand - m_ref) (0 for an empty hand-over).
+#pragma unroll
+    for (int x = 0; x < kVecBlocks; ++x) {
+        const float f = m_hand[x] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_hand[x] - m_ref[x]);
+        float l = l_part[x] + __shfl_xor(l_part[x], 16);
+        l += __shfl_xor(l, 32);
+        l += l_hand[x] * f;
+        const float inv = 1.f / l;
+        float *of = p.out_fp32 + vrow[x] * kD + 4 * quad;
+        uint16_t *ob = p.out + vrow[x] * kD + 4 * quad;
+#pragma unroll
+        for (int db = 0; db < 16; ++db) {
+            const float4 h = *reinterpret_cast<const float4 *>(of + 16 * db);
+            const float o0 = (acc[x][db][0] + h.x * f) * inv, o1 = (acc[x][db][1] + h.y * f) * inv,
+                        o2 = (acc[x][db][2] + h.z * f) * inv, o3 = (acc[x][db][3] + h.w * f) * inv;
+            *reinterpret_cast<float4 *>(of + 16 * db) = make_float4(o0, o1, o2, o3);
+            *reinterpret_cast<uint2 *>(ob + 16 * db) =
+                make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+        }
+        if (quad == 0) p.lse[sidx[x]] = (m_ref[x] + log2f(l)) * 0.6931471805599453f;
+    }
+}
+
+__global__ __launch_bounds__(64 * kDenseWaves) void k_forward_dense(Problem p)
+{
+    __shared__ __attribute__((aligned(16))) char buf[2 * kBuf];
+    __shared__ uint32_t redo_flag;
+    if (threadIdx.x == 0) redo_flag = 0;
+    __syncthreads();
+    forward_dense_item(p, (lds_char *)buf, &redo_flag);
+}
+
+}  // namespace
+
+hipError_t launch_forward_dense(const Problem &p, hipStream_t s)
+{
+    const int64_t items = p.B * p.Hkv * p.nQT * kVBlocks;
+    hipLaunchKernelGGL(k_forward_dense, dim3((unsigned)items), dim3(64 * kDenseWaves), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_dq_dense(const Problem &p, hipStream_t s)
+{
+    (void)p;
+    (void)s;
+    return hipSuccess;
+}
+
+}  // namespace qsa

@@ -58,10 +58,23 @@ __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_
     const int64_t b = row / p.Sq, i = row - b * p.Sq;
     const int head = g * kGroup + col;
     const bool hv = col < kGroup;
-    const int n = p.row_cnt[row];
+    // Keys of partial tiles only; when the row's tile row has full tiles the
+    // dense pass adds them and writes the outputs, and this pass hands over
+    // its unnormalised state instead.
+    const int n = p.pcnt[row];
+    const bool handoff = p.fwd_f_cnt[b * p.nQT + (i >> 7)] > 0;
+    const int64_t sidx = (b * p.Hq + head) * p.Sq + i;
 
     float *of = p.out_fp32 + (row * p.Hq + head) * (int64_t)kD;
     uint16_t *ob = p.out + (row * p.Hq + head) * (int64_t)kD;
+    if (n == 0 && handoff) {
+        if (hv) {
+            for (int db = 0; db < 16; ++db)
+                *reinterpret_cast<float4 *>(of + 16 * db + 4 * quad) = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (quad == 0) *reinterpret_cast<float2 *>(p.fstate + 2 * sidx) = make_float2(-INFINITY, 0.f);
+        }
+        return;
+    }
     if (n == 0) {
         if (hv) {
             for (int db = 0; db < 16; ++db) {
@@ -101,7 +114,7 @@ __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_
     // 16h .. 16h+15 for its half h) are fetched one chunk ahead with four
     // 16-byte loads; slots at or past n read as zero.
     const int half = lane >> 5;
-    const rsrc_t rkeys = make_rsrc(p.row_keys + row * p.W, (uint32_t)(p.W * 4));
+    const rsrc_t rkeys = make_rsrc(p.pkeys + row * p.W, (uint32_t)(p.W * 4));
     auto fetch_keys = [&](int ch, uint4 (&kk)[4]) {
         const int base = ch * kChunk + 16 * half;
 #pragma unroll
@@ -266,6 +279,14 @@ __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_
     float l = l_part + __shfl_xor(l_part, 16);
     l += __shfl_xor(l, 32);
     if (!hv) return;
+    if (handoff) {
+#pragma unroll
+        for (int db = 0; db < 16; ++db)
+            *reinterpret_cast<float4 *>(of + 16 * db + 4 * quad) =
+                make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+        if (quad == 0) *reinterpret_cast<float2 *>(p.fstate + 2 * sidx) = make_float2(m_run, l);
+        return;
+    }
     const float inv = 1.f / l;
 #pragma unroll
     for (int db = 0; db < 16; ++db) {

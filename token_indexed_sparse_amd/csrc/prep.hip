@@ -175,7 +175,40 @@ __global__ __launch_bounds__(64) void k_lists_rev(Problem p)
     }
 }
 
+// One wave per row: the row's sorted key list without the keys of full tiles
+// (order kept). Full tiles are computed densely; every other selected key
+// stays on the gathered path.
+__global__ __launch_bounds__(256) void k_partial_keys(Problem p)
+{
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= p.B * p.Sq) return;
+    const int lane = threadIdx.x & 63;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int64_t b = row / p.Sq, i = row - b * p.Sq;
+    const int32_t *kd = p.kinds + (b * p.nQT + (i >> 7)) * p.nKT;
+    const int32_t *keys = p.row_keys + row * p.W;
+    int32_t *out = p.pkeys + row * p.W;
+    const int n = p.row_cnt[row];
+    int cnt = 0;
+    for (int s0 = 0; s0 < n; s0 += 64) {
+        const int s = s0 + lane;
+        const int32_t key = s < n ? keys[s] : 0;
+        const bool keep = s < n && kd[key >> 7] != 2;
+        const uint64_t ball = __ballot(keep);
+        if (keep) out[cnt + __popcll(ball & below)] = key;
+        cnt += __popcll(ball);
+    }
+    if (lane == 0) p.pcnt[row] = cnt;
+}
+
 }  // namespace
+
+hipError_t launch_partial_keys(const Problem &p, hipStream_t s)
+{
+    const int64_t rows = p.B * p.Sq;
+    hipLaunchKernelGGL(k_partial_keys, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_preprocess(const Problem &p, hipStream_t s)
 {

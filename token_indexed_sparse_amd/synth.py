@@ -220,3 +220,61 @@ def random_case(seed: int, B: int, Sq: int, Skv: int, Hq: int, Hkv: int, W: int,
     wl = Workload(f"random_{seed}", B, Sq, Skv, Hq, Hkv, D, (W - 4) // 4 if W >= 4 else 0,
                   "random", seed)
     return Inputs(wl, routes, q, k, v, go, {"W": W})
+
+
+def tiled_case(seed: int, B: int, Sq: int, Skv: int, Hq: int, Hkv: int, p_full: float = 0.5,
+               extra: int = 16, D: int = 256, bare_rows: bool = False, loud_keys: float = 0.0,
+               all_keys: bool = False, causal: bool = False) -> Inputs:
+    """Routes that select whole 128 x 128 tiles, so that full tiles occur.
+
+    Each (batch, query tile, key tile) is chosen with probability ``p_full``
+    (``all_keys``: every one; ``causal``: key tiles at or below the query
+    tile, the diagonal one only up to the row's own position); every row then
+    selects all keys of its chosen tiles plus ``extra`` uniform keys. With
+    ``bare_rows`` the odd query tiles of batch 0 get no extra keys. Route slots
+    are shuffled; spare slots hold -1, a duplicate and an out-of-range value.
+    ``loud_keys`` > 0 multiplies the K rows of the first chosen key tile of
+    batch 0 by that factor (large scores there).
+    """
+    rng = np.random.default_rng(seed)
+    nQT, nKT = -(-Sq // 128), -(-Skv // 128)
+    chosen = rng.random((B, nQT, nKT)) < p_full
+    if all_keys:
+        chosen[:] = True
+    if causal:
+        chosen = np.broadcast_to(np.arange(nKT)[None, :] <= np.arange(nQT)[:, None],
+                                 (B, nQT, nKT)).copy()
+    per_row = []
+    for b in range(B):
+        for i in range(Sq):
+            r = i // 128
+            parts = []
+            for t in np.nonzero(chosen[b, r])[0]:
+                hi = min(128 * t + 128, Skv)
+                if causal and t == r:
+                    hi = min(hi, i + 1)
+                parts.append(np.arange(128 * t, hi))
+            n_extra = 0 if (bare_rows and b == 0 and r % 2 == 1) else extra
+            parts.append(rng.integers(0, Skv, n_extra))
+            per_row.append(np.concatenate(parts).astype(np.int64))
+    W = max(len(k) for k in per_row) + 3
+    routes = np.full((B, Sq, W), -1, np.int64)
+    for idx, keys in enumerate(per_row):
+        b, i = divmod(idx, Sq)
+        vals = np.full(W, -1, np.int64)
+        vals[:len(keys)] = keys
+        vals[len(keys)] = keys[0] if len(keys) else -1
+        vals[len(keys) + 1] = Skv + 3
+        routes[b, i, rng.permutation(W)] = vals
+    routes = routes.astype(np.int32)
+    q = bf16_bits(rng.standard_normal((B, Sq, Hq, D), dtype=np.float32))
+    kf = rng.standard_normal((B, Skv, Hkv, D), dtype=np.float32)
+    if loud_keys > 0:
+        t0 = np.nonzero(chosen[0].any(axis=0))[0]
+        if len(t0):
+            kf[0, 128 * t0[0]:128 * t0[0] + 128] *= loud_keys
+    k = bf16_bits(kf)
+    v = bf16_bits(rng.standard_normal((B, Skv, Hkv, D), dtype=np.float32))
+    go = bf16_bits(rng.standard_normal((B, Sq, Hq, D), dtype=np.float32))
+    wl = Workload(f"tiled_{seed}", B, Sq, Skv, Hq, Hkv, D, 0, "tiled", seed)
+    return Inputs(wl, routes, q, k, v, go, {"W": W})
