@@ -41,13 +41,16 @@ FLOP_PER_PAIR_HEAD = {
     "forward": 4 * 256,        # S = QK^T and O = PV
     "forward_dense": 4 * 256,
     "dq": 6 * 256,             # S, dP = dO V^T, dQ = dS K
+    "dq_dense": 6 * 256,
     "dkdv": 8 * 256,           # S, dP, dV = P^T dO, dK = dS^T Q
+    "dkdv_dense": 8 * 256,
 }
-KERNEL_PAIRS = {"forward": "partial", "forward_dense": "full", "dq": "all", "dkdv": "all"}
+KERNEL_PAIRS = {"forward": "partial", "forward_dense": "full", "dq": "partial",
+                "dq_dense": "full", "dkdv": "partial", "dkdv_dense": "full"}
 COUNTED_FWD = 4 * 256
 COUNTED_BWD = 10 * 256
 FWD_STAGES = ["preprocess_fwd", "forward", "forward_dense"]
-BWD_STAGES = ["preprocess_bwd", "delta", "dq", "dkdv", "dkdv_reduce"]
+BWD_STAGES = ["preprocess_bwd", "delta", "dq", "dq_dense", "dkdv", "dkdv_dense", "dkdv_reduce"]
 
 
 def pairs_per_row(routes: np.ndarray, Skv: int) -> np.ndarray:

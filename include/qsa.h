@@ -152,13 +152,15 @@ qsa_status qsa_preprocess(const qsa_dims *dims, const void *routes, uint8_t *mem
  * events[0] is recorded before the first launch and events[s + 1] after
  * stage s. Forward stages: 0 route preprocessing, 1 attention over the keys
  * of partial tiles (gathered), 2 attention over full tiles (dense) and the
- * output write. Backward stages: 0 route preprocessing, 1 delta, 2 dQ, 3 dK/dV
- * partial sums per query segment, 4 the sum of the segments and the bf16
+ * output write. Backward stages: 0 route preprocessing, 1 delta, 2 dQ over
+ * the keys of partial tiles (gathered), 3 dQ over full tiles (dense) and the
+ * dQ write, 4 dK/dV partial sums of partial tiles per query segment, 5 dK/dV
+ * partial sums of full tiles (dense), 6 the sum of the partials and the bf16
  * cast. events == NULL behaves exactly like the plain call; too few events
  * gives QSA_ERR_NULL.
  */
 #define QSA_FORWARD_STAGES 3
-#define QSA_BACKWARD_STAGES 5
+#define QSA_BACKWARD_STAGES 7
 qsa_status qsa_forward_timed(const qsa_dims *dims, const void *q, const void *k, const void *v,
                              const void *routes, float scale, void *out, float *out_fp32,
                              float *lse, void *workspace, size_t workspace_bytes, void *stream,

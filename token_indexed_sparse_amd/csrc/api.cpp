@@ -90,10 +90,10 @@ Layout layout(const qsa_dims *d, int which)
     const int64_t nseg = (nQT + kSegTiles - 1) / kSegTiles;
     // The dK/dV partial sums and the dQ hand-over are never live together
     // (dQ finishes before dK/dV starts), so they share one region.
-    const size_t kv_bytes = (size_t)(d->B * d->Hkv * nseg * stride) * 2 * kD * 4;
+    const size_t kv_bytes = (size_t)(d->B * d->Hkv * (nseg + 1) * stride) * 2 * kD * 4;
     const size_t dq_bytes = (size_t)(rows * d->Hq) * kD * 4;
     L.kv_part = which == 1 ? take(kv_bytes > dq_bytes ? kv_bytes : dq_bytes) : none;
-    L.kv_flag = which == 1 ? take((size_t)(d->B * d->Hkv * nseg * (stride / 16))) : none;
+    L.kv_flag = which == 1 ? take((size_t)(d->B * d->Hkv * (nseg + 1) * (stride / 16))) : none;
     L.total = off;
     return L;
 }
@@ -137,6 +137,7 @@ void fill_common(Problem &p, const qsa_dims *d, const void *routes, float scale)
     p.nKT = (d->Skv + kTile - 1) / kTile;
     p.stride = p.nKT * kTile;
     p.nseg = (p.nQT + kSegTiles - 1) / kSegTiles;
+    p.nslot = p.nseg + 1;
     p.scale = scale;
     p.routes = routes;
 }
@@ -290,15 +291,20 @@ qsa_status qsa_backward_timed(const qsa_dims *dims, const void *grad_out, const 
     if (events && n_events < QSA_BACKWARD_STAGES + 1) return QSA_ERR_NULL;
     if (mark(events, 0, s) != hipSuccess) return QSA_ERR_DEVICE;
     if (launch_preprocess(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (launch_partial_keys(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
     if (mark(events, 1, s) != hipSuccess) return QSA_ERR_DEVICE;
     if (launch_delta(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
     if (mark(events, 2, s) != hipSuccess) return QSA_ERR_DEVICE;
     if (launch_dq(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
     if (mark(events, 3, s) != hipSuccess) return QSA_ERR_DEVICE;
-    if (launch_dkdv(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (launch_dq_dense(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
     if (mark(events, 4, s) != hipSuccess) return QSA_ERR_DEVICE;
-    if (launch_dkdv_reduce(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (launch_dkdv(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
     if (mark(events, 5, s) != hipSuccess) return QSA_ERR_DEVICE;
+    if (launch_dkdv_dense(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 6, s) != hipSuccess) return QSA_ERR_DEVICE;
+    if (launch_dkdv_reduce(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 7, s) != hipSuccess) return QSA_ERR_DEVICE;
     return QSA_OK;
 }
 

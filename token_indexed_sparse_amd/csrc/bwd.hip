@@ -17,9 +17,10 @@
 //    operand is the transposed read of the same staged K rows.
 //  * k_dkdv: key-major. One wave owns 16 consecutive keys of one KV head and
 //    one segment of 32 query tiles, keeps the 16 K and V rows in registers and
-//    their dK, dV accumulators for the whole item. It walks the reverse tile
-//    lists of its 128-key tile column inside the segment from the last query
-//    tile down, reads a 16-bit slice of the bit-packed membership row of every
+//    their dK, dV accumulators for the whole item. It walks the partial
+//    entries of the reverse tile list of its 128-key tile column inside the
+//    segment from the last query tile down (full tiles are summed by the dense
+//    pass), reads a 16-bit slice of the bit-packed membership row of every
 //    query in those tiles, and lists the rows that select one of its keys in
 //    LDS. Each listed row's Q and dO (12 heads x 512 bytes each) are gathered
 //    into a 2-slot LDS ring by direct-to-LDS loads, one row ahead, then read
@@ -28,8 +29,9 @@
 //    rows' heads form the 32-long contraction). P and dS enter these products
 //    (and dS the dQ product) as bf16 high + low parts, so that sums over
 //    thousands of query heads keep FP32-level error.
-//  * k_dkdv_reduce: the FP32 partial sums of the segments are added in
-//    segment order (deterministic, no atomics) and written as bf16 dK, dV.
+//  * k_dkdv_reduce: the FP32 partial sums of the segments and then of the
+//    dense full-tile pass are added in that fixed order (deterministic, no
+//    atomics) and written as bf16 dK, dV.
 //    Splitting the long causal key columns into segments keeps every SIMD
 //    busy to the end: the first key groups are selected by almost every later
 //    row and would otherwise dominate the run time.
@@ -74,7 +76,11 @@ __device__ __forceinline__ void dq_row(const Problem &p, lds_char *ks, lds_char 
     const int64_t b = row / p.Sq, i = row - b * p.Sq;
     const int head = g * kGroup + col;
     const bool hv = col < kGroup;
-    const int n = p.row_cnt[row];
+    // Keys of partial tiles only; when the row's tile row has full tiles the
+    // dense pass adds them and writes dQ, and this pass hands over its
+    // unscaled FP32 sums instead.
+    const int n = p.pcnt[row];
+    const bool handoff = p.fwd_f_cnt[b * p.nQT + (i >> 7)] > 0;
     uint16_t *dqp = p.dq + (row * p.Hq + head) * (int64_t)kD;
 
     f32x4 acc[16];
@@ -107,7 +113,7 @@ __device__ __forceinline__ void dq_row(const Problem &p, lds_char *ks, lds_char 
             QSA_WAIT_VM(0);  // the counted waits below are then the only ones
         }
         const float c = p.scale * 1.4426950408889634f;
-        const rsrc_t rkeys = make_rsrc(p.row_keys + row * p.W, (uint32_t)(p.W * 4));
+        const rsrc_t rkeys = make_rsrc(p.pkeys + row * p.W, (uint32_t)(p.W * 4));
         auto fetch_key = [&](int ch) -> int {
             const int slot = ch * kChunk + (lane & 31);
             const int kk = (int)__builtin_amdgcn_raw_buffer_load_b32(
@@ -201,6 +207,14 @@ __device__ __forceinline__ void dq_row(const Problem &p, lds_char *ks, lds_char 
         QSA_WAIT_VM(0);  // no gather may outlive the wave's LDS
     }
     if (!hv) return;
+    if (handoff) {
+        float *hp = p.dq_part + (row * p.Hq + head) * (int64_t)kD + 4 * quad;
+#pragma unroll
+        for (int db = 0; db < 16; ++db)
+            *reinterpret_cast<float4 *>(hp + 16 * db) =
+                make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+        return;
+    }
 #pragma unroll
     for (int db = 0; db < 16; ++db) {
         const int d = 16 * db + 4 * quad;
@@ -243,7 +257,7 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, lds
     const int g = (int)(bg % p.Hkv);
     const int64_t b = bg / p.Hkv;
     const int64_t key0 = kg * 16;
-    uint8_t *flag = p.kv_flag + (bg * p.nseg + seg) * ngroups + kg;
+    uint8_t *flag = p.kv_flag + (bg * p.nslot + seg) * ngroups + kg;
     if (key0 >= p.Skv) {
         if (lane == 0) *flag = 0;
         return;
@@ -265,7 +279,8 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, lds
         }
         return lo;
     };
-    const int32_t cnt_p = p.rev_p_cnt[bt], cnt_f = p.rev_f_cnt[bt];
+    // Partial tiles only: the full ones are summed by the dense pass.
+    const int32_t cnt_p = p.rev_p_cnt[bt], cnt_f = 0;
     const int32_t p_lo = lower_bound(idx_p, cnt_p, t_lo), p_hi = lower_bound(idx_p, cnt_p, t_hi);
     const int32_t f_lo = lower_bound(idx_f, cnt_f, t_lo), f_hi = lower_bound(idx_f, cnt_f, t_hi);
     const int64_t nwin = 2 * ((int64_t)(p_hi - p_lo) + (f_hi - f_lo));
@@ -514,7 +529,7 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, lds
 
     // Lane holds dK/dV[key 4*quad+e][d 16*db + col]; the partial sums of this
     // segment go to its slice of the workspace, dK first, then dV.
-    float *part = p.kv_part + ((bg * p.nseg + seg) * p.stride + key0) * (int64_t)(2 * kD);
+    float *part = p.kv_part + ((bg * p.nslot + seg) * p.stride + key0) * (int64_t)(2 * kD);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         float *pk = part + (4 * quad + e) * (int64_t)(2 * kD) + col;
@@ -535,8 +550,8 @@ __global__ __launch_bounds__(64) void k_dkdv(Problem p)
     dkdv_item(p, (lds_char *)slots, (lds_char *)zero, hrow, hmask);
 }
 
-// dK = scale * sum of the segment partials, dV = sum, in segment order; one
-// thread per (batch, KV head, key, 4 columns).
+// dK = scale * sum of the partials, dV = sum, in slot order (the segments,
+// then the full tiles); one thread per (batch, KV head, key, 4 columns).
 __global__ __launch_bounds__(256) void k_dkdv_reduce(Problem p)
 {
     const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -550,12 +565,12 @@ __global__ __launch_bounds__(256) void k_dkdv_reduce(Problem p)
     const int g = (int)(bg - b * p.Hkv);
     if (key >= p.Skv) return;
     const int64_t ngroups = p.stride >> 4;
-    const uint8_t *flag = p.kv_flag + bg * p.nseg * ngroups + (key >> 4);
+    const uint8_t *flag = p.kv_flag + bg * p.nslot * ngroups + (key >> 4);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int64_t seg = 0; seg < p.nseg; ++seg) {
+    for (int64_t seg = 0; seg < p.nslot; ++seg) {
         if (!flag[seg * ngroups]) continue;
         const float4 v = *reinterpret_cast<const float4 *>(
-            p.kv_part + ((bg * p.nseg + seg) * p.stride + key) * (int64_t)(2 * kD) + 4 * f4);
+            p.kv_part + ((bg * p.nslot + seg) * p.stride + key) * (int64_t)(2 * kD) + 4 * f4);
         acc.x += v.x;
         acc.y += v.y;
         acc.z += v.z;

@@ -48,11 +48,13 @@ struct Problem {
     // backward
     float *delta;
     uint16_t *dq, *dk, *dv;
-    // dK/dV partial sums per query segment: [B*Hkv][nseg][stride][dK 256 | dV 256]
-    // FP32, and per (B*Hkv, segment, 16-key group) whether a partial was written
+    // dK/dV partial sums: [B*Hkv][nseg + 1][stride][dK 256 | dV 256] FP32, one
+    // slot per query segment of the gathered pass plus one for the full tiles,
+    // and per (B*Hkv, slot, 16-key group) whether a partial was written
     float *kv_part;
     uint8_t *kv_flag;
     int64_t nseg;
+    int64_t nslot;  // nseg + 1 partial-sum slots per (batch, KV head)
     // Hand-off from the gathered to the dense dQ: unscaled FP32 sums
     // [B, Sq, Hq, 256] of the rows whose tile row has full tiles.
     float *dq_part;
@@ -63,6 +65,7 @@ hipError_t launch_partial_keys(const Problem &p, hipStream_t s);
 hipError_t launch_forward(const Problem &p, hipStream_t s);
 hipError_t launch_forward_dense(const Problem &p, hipStream_t s);
 hipError_t launch_dq_dense(const Problem &p, hipStream_t s);
+hipError_t launch_dkdv_dense(const Problem &p, hipStream_t s);
 hipError_t launch_delta(const Problem &p, hipStream_t s);
 hipError_t launch_dq(const Problem &p, hipStream_t s);
 hipError_t launch_dkdv(const Problem &p, hipStream_t s);
@@ -324,6 +327,15 @@ __device__ __forceinline__ i32x4 rsrc_words(const void *base, uint32_t bytes)
 __device__ __forceinline__ void dma16_asm(i32x4 r, uint32_t lds, uint32_t voff)
 {
     asm volatile("s_mov_b32 m0, %0\n s_nop 0\n buffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(r)
+                 : "memory", "m0");
+}
+
+// 4 bytes per active lane: lane l's word lands at LDS address lds + 4 l.
+__device__ __forceinline__ void dma4_asm(i32x4 r, uint32_t lds, uint32_t voff)
+{
+    asm volatile("s_mov_b32 m0, %0\n s_nop 0\n buffer_load_dword %1, %2, 0 offen lds"
                  :
                  : "s"(lds), "v"(voff), "s"(r)
                  : "memory", "m0");

@@ -19,10 +19,10 @@
 //  * Keys come in chunks of 32 from the tile row's full key tiles. A chunk's
 //    K and V rows are contiguous, staged once per work group into LDS by
 //    direct-to-LDS loads (each wave issues a quarter) in the swizzled layout
-//    of the gathered forward, double-buffered: the next chunk flies while
-//    the current one is computed. A wave waits for its own loads, then the
-//    work-group barrier makes every wave's loads visible and frees the other
-//    buffer.
+//    of the gathered forward, into a ring of four chunk buffers: three chunks
+//    fly while one is computed. A wave waits (counted) for its own loads of
+//    the chunk, then the work-group barrier makes every wave's loads visible
+//    and frees the buffer of the previous chunk for the next load.
 //  * S^T = K Q^T and O^T = V^T P^T exactly as in the gathered forward (K in
 //    the row layout, V through the transposing read, P^T straight from the
 //    accumulators, P as bf16 high + low), per vector block.
@@ -44,9 +44,21 @@ constexpr int kVBlocks = kTileVecs / kGroupVecs;               // work groups pe
 constexpr int kKeys = 32;                                      // keys per staged chunk
 constexpr int kHalf = kKeys * 512;                             // K (or V) bytes of a chunk
 constexpr int kBuf = 2 * kHalf;                                // K then V
+constexpr int kRing = 4;        // chunk buffers: three chunks in flight ahead
+constexpr int kChunkOps = 8;    // direct-to-LDS loads a wave issues per chunk
 constexpr float kSlack = 64.f;  // log2 of the largest unnormalised P
 static_assert(kTileVecs % kGroupVecs == 0, "work groups must tile the query tile");
 static_assert(kDenseWaves * 4 == 16, "each wave stages four of the 16 row pairs");
+
+// This wave's loads of chunk ch have landed once at most the loads of the
+// chunks issued after it (up to kRing - 2 of them) are in flight.
+__device__ __forceinline__ void wait_chunk(int ch, int nch)
+{
+    static_assert(kRing == 4, "the counted waits assume three chunks in flight");
+    if (ch + 2 < nch) QSA_WAIT_VM(2 * kChunkOps);
+    else if (ch + 1 < nch) QSA_WAIT_VM(kChunkOps);
+    else QSA_WAIT_VM(0);
+}
 
 struct DenseTile {
     int64_t b, r;
@@ -69,8 +81,10 @@ __device__ __forceinline__ bool dense_tile(const Problem &p, DenseTile &t)
     return true;
 }
 
+typedef volatile __attribute__((address_space(3))) uint32_t lds_flag;
+
 __device__ __forceinline__ void forward_dense_item(const Problem &p, lds_char *buf,
-                                                   volatile uint32_t *redo_flag)
+                                                   lds_flag *redo_flag)
 {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -113,6 +127,10 @@ __device__ __forceinline__ void forward_dense_item(const Problem &p, lds_char *b
         l_hand[x] = st.y;
         m_ref[x] = -INFINITY;
     }
+    // Settle these loads before the staging starts: the compiler cannot count
+    // the assembly loads, and the counted waits in the loop are then the only
+    // vector memory waits there.
+    QSA_WAIT_VM(0);
     f32x4 acc[kVecBlocks][16];
     float l_part[kVecBlocks];
 
@@ -136,7 +154,7 @@ __device__ __forceinline__ void forward_dense_item(const Problem &p, lds_char *b
         const int64_t key0 = (int64_t)fidx[c >> 2] * kTile + (c & 3) * kKeys;
         const i32x4 rk = rsrc_words(kbase + key0 * p.Hkv * kD, kKeys * row_bytes);
         const i32x4 rv = rsrc_words(vbase + key0 * p.Hkv * kD, kKeys * row_bytes);
-        const uint32_t dst = base + (uint32_t)((c & 1) * kBuf);
+        const uint32_t dst = base + (uint32_t)((c % kRing) * kBuf);
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
             const uint32_t s = (uint32_t)(4 * wave + y);
@@ -263,17 +281,17 @@ __device__ __forceinline__ void forward_dense_item(const Problem &p, lds_char *b
     // barriers, so all leave together and the pass reports it.
     auto pass = [&](auto rescale_tag) {
         constexpr bool kRescale = decltype(rescale_tag)::value;
-        issue(0);
+        for (int c0 = 0; c0 < kRing - 1 && c0 < nch; ++c0) issue(c0);
         bool redo = false;
         for (int ch = 0; ch < nch; ++ch) {
-            QSA_WAIT_VM(0);  // this wave's loads of chunk ch have landed
+            wait_chunk(ch, nch);
             __builtin_amdgcn_s_barrier();
             if (!kRescale && opaque_u32(__builtin_amdgcn_readfirstlane(*redo_flag)) != 0u) {
                 redo = true;
                 break;
             }
-            const uint32_t cb = opaque_u32(base + (uint32_t)((ch & 1) * kBuf));
-            if (ch + 1 < nch) issue(ch + 1);
+            const uint32_t cb = opaque_u32(base + (uint32_t)((ch % kRing) * kBuf));
+            if (ch + kRing - 1 < nch) issue(ch + kRing - 1);
             compute(cb, !kRescale && ch == 0, rescale_tag);
         }
         QSA_WAIT_VM(0);
@@ -313,14 +331,412 @@ __device__ __forceinline__ void forward_dense_item(const Problem &p, lds_char *b
 
 __global__ __launch_bounds__(64 * kDenseWaves) void k_forward_dense(Problem p)
 {
-    __shared__ __attribute__((aligned(16))) char buf[2 * kBuf];
+    __shared__ __attribute__((aligned(16))) char buf[kRing * kBuf];
     __shared__ uint32_t redo_flag;
     if (threadIdx.x == 0) redo_flag = 0;
     __syncthreads();
-    forward_dense_item(p, (lds_char *)buf, &redo_flag);
+    forward_dense_item(p, (lds_char *)buf, (lds_flag *)&redo_flag);
+}
+
+// dQ over full tiles: same tiling and staging as the forward. P = 2^(S c -
+// lse log2 e) needs no running maximum; dS = P (dP - delta); dQ^T += K^T dS^T
+// with dS as bf16 high + low and K^T through the transposing read of the
+// staged K rows. The gathered pass handed over its unscaled FP32 sums.
+__device__ __forceinline__ void dq_dense_item(const Problem &p, lds_char *buf)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 15, quad = lane >> 4;
+    DenseTile dt;
+    if (!dense_tile(p, dt)) return;
+    const int64_t b = dt.b, r = dt.r;
+    const int g = dt.g;
+    const int fcnt = p.fwd_f_cnt[b * p.nQT + r];
+    if (fcnt == 0) return;
+    const __attribute__((address_space(4))) int32_t *fidx =
+        (const __attribute__((address_space(4))) int32_t *)(p.fwd_f_idx + (b * p.nQT + r) * p.nKT);
+
+    int64_t vrow[kVecBlocks];
+    bf16x8 qf[kVecBlocks][8], gf[kVecBlocks][8];
+    float lse2[kVecBlocks], dlt[kVecBlocks];
+#pragma unroll
+    for (int x = 0; x < kVecBlocks; ++x) {
+        const int v = dt.vb * kGroupVecs + wave * 16 * kVecBlocks + 16 * x + col;
+        const int rt = v / kGroup, hd = v - kGroup * rt;
+        const int64_t i = r * kTile + rt;
+        const int head = g * kGroup + hd;
+        vrow[x] = (b * p.Sq + i) * p.Hq + head;
+        const int64_t sidx = (b * p.Hq + head) * p.Sq + i;
+        lse2[x] = p.lse_in[sidx] * 1.4426950408889634f;
+        dlt[x] = p.delta[sidx];
+        const uint16_t *qr = p.q + vrow[x] * kD + 8 * quad;
+        const uint16_t *gr = p.dout + vrow[x] * kD + 8 * quad;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            qf[x][t] = as_bf16x8(*reinterpret_cast<const uint4 *>(qr + 32 * t));
+            gf[x][t] = as_bf16x8(*reinterpret_cast<const uint4 *>(gr + 32 * t));
+        }
+    }
+    QSA_WAIT_VM(0);  // as in the forward: settle before the staging starts
+    f32x4 acc[kVecBlocks][16];
+#pragma unroll
+    for (int x = 0; x < kVecBlocks; ++x)
+#pragma unroll
+        for (int db = 0; db < 16; ++db) acc[x][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const uint32_t row_bytes = (uint32_t)(p.Hkv * kD * 2);
+    const uint16_t *kbase = p.k + (b * p.Skv * p.Hkv + g) * (int64_t)kD;
+    const uint16_t *vbase = p.v + (b * p.Skv * p.Hkv + g) * (int64_t)kD;
+    uint32_t loff[4];
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+        const int s = 4 * wave + y;
+        loff[y] = (uint32_t)(s + 16 * (lane >> 5)) * row_bytes +
+                  ((uint32_t)((lane & 31) ^ swz_mask(s)) << 4);
+    }
+    const uint32_t base = lds_addr(buf);
+    auto issue = [&](int c) {
+        const int64_t key0 = (int64_t)fidx[c >> 2] * kTile + (c & 3) * kKeys;
+        const i32x4 rk = rsrc_words(kbase + key0 * p.Hkv * kD, kKeys * row_bytes);
+        const i32x4 rv = rsrc_words(vbase + key0 * p.Hkv * kD, kKeys * row_bytes);
+        const uint32_t dst = base + (uint32_t)((c % kRing) * kBuf);
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+            const uint32_t s = (uint32_t)(4 * wave + y);
+            dma16_asm(rk, dst + s * 1024, loff[y]);
+            dma16_asm(rv, dst + kHalf + s * 1024, loff[y]);
+        }
+    };
+
+    // K and V in the row layout (A operands of S^T = K Q^T and dP^T = V dO^T),
+    // K transposed (A operand of dQ^T = K^T dS^T), addressed as in the forward.
+    const int kmask = swz_mask(col);
+    const int tkey = 4 * quad + (col >> 2);
+    const int tm = swz_mask(tkey);
+    const int tlane = tkey * 1024 + ((((col >> 1) & 1) ^ (tm & 1)) << 4) + (col & 1) * 8;
+    const int txor = tm >> 1;
+    const float c = p.scale * 1.4426950408889634f;
+
+    auto compute = [&](uint32_t cb) {
+        const lds_char *ks = (const lds_char *)(uintptr_t)cb;
+        const lds_char *vs = ks + kHalf;
+        f32x4 st[kVecBlocks][2], pt[kVecBlocks][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            uint4 kr[8], vr[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int o = col * 1024 + 512 * kb + (((4 * t + quad) ^ kmask) << 4);
+                kr[t] = lds_read16(ks + o);
+                vr[t] = lds_read16(vs + o);
+            }
+#pragma unroll
+            for (int x = 0; x < kVecBlocks; ++x) {
+                f32x4 a = {0.f, 0.f, 0.f, 0.f}, d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    a = mfma_16x16x32(as_bf16x8(kr[t]), qf[x][t], a);
+                    d = mfma_16x16x32(as_bf16x8(vr[t]), gf[x][t], d);
+                }
+                st[x][kb] = a;
+                pt[x][kb] = d;
+            }
+        }
+        bf16x8 ds_hi[kVecBlocks], ds_lo[kVecBlocks];
+#pragma unroll
+        for (int x = 0; x < kVecBlocks; ++x) {
+            float ds[8];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float pr = __builtin_amdgcn_exp2f(st[x][kb][e] * c - lse2[x]);
+                    ds[kb * 4 + e] = pr * (pt[x][kb][e] - dlt[x]);
+                }
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) split_bf16x2(ds[2 * k], ds[2 * k + 1], hi[k], lo[k]);
+            ds_hi[x] = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+            ds_lo[x] = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint2 kt[2][8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int o = tlane + (((8 * h + j) ^ txor) << 5);
+                kt[0][j] = lds_read_tr(ks + o);
+                kt[1][j] = lds_read_tr(ks + o + 512);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int db = 8 * h + j;
+                const bf16x8 ka =
+                    as_bf16x8(make_uint4(kt[0][j].x, kt[0][j].y, kt[1][j].x, kt[1][j].y));
+#pragma unroll
+                for (int x = 0; x < kVecBlocks; ++x) {
+                    acc[x][db] = mfma_16x16x32(ka, ds_hi[x], acc[x][db]);
+                    acc[x][db] = mfma_16x16x32(ka, ds_lo[x], acc[x][db]);
+                }
+            }
+        }
+    };
+
+    const int nch = fcnt * (kTile / kKeys);
+    for (int c0 = 0; c0 < kRing - 1 && c0 < nch; ++c0) issue(c0);
+    for (int ch = 0; ch < nch; ++ch) {
+        wait_chunk(ch, nch);
+        __builtin_amdgcn_s_barrier();
+        const uint32_t cb = opaque_u32(base + (uint32_t)((ch % kRing) * kBuf));
+        if (ch + kRing - 1 < nch) issue(ch + kRing - 1);
+        compute(cb);
+    }
+    QSA_WAIT_VM(0);
+
+    // dQ = scale * (dense sums + handed-over sums); lane holds dQ^T[d][vector].
+#pragma unroll
+    for (int x = 0; x < kVecBlocks; ++x) {
+        const float *hp = p.dq_part + vrow[x] * kD + 4 * quad;
+        uint16_t *dqp = p.dq + vrow[x] * kD + 4 * quad;
+#pragma unroll
+        for (int db = 0; db < 16; ++db) {
+            const float4 h = *reinterpret_cast<const float4 *>(hp + 16 * db);
+            const float sc = p.scale;
+            *reinterpret_cast<uint2 *>(dqp + 16 * db) =
+                make_uint2(pack_bf16x2((acc[x][db][0] + h.x) * sc, (acc[x][db][1] + h.y) * sc),
+                           pack_bf16x2((acc[x][db][2] + h.z) * sc, (acc[x][db][3] + h.w) * sc));
+        }
+    }
+}
+
+__global__ __launch_bounds__(64 * kDenseWaves) void k_dq_dense(Problem p)
+{
+    __shared__ __attribute__((aligned(16))) char buf[kRing * kBuf];
+    dq_dense_item(p, (lds_char *)buf);
+}
+
+// dK and dV over full tiles. One work group per (batch, KV head, key tile,
+// half of it): each of the four waves owns 16 keys (K and V rows in
+// registers, dK and dV accumulators for the whole work group) and the work
+// group streams the (row, head) vectors of the key tile's full query tiles in
+// chunks of 32: Q, dO, lse and delta of a chunk are staged once, Q and dO in
+// the forward's K-staging layout (slot j = vector j of the chunk), through the
+// same four-buffer ring. Per chunk a wave computes S = Q K^T and dP = dO V^T
+// for its keys (two 16-vector blocks; lane (key col, quad) holds vectors
+// 16x + 4 quad + i), P and dS, then dV += P^T dO and dK += dS^T Q with the
+// two blocks' vectors as the 32-long contraction, exactly as the gathered
+// pass pairs two rows (P and dS as bf16 high + low); the transposed Q and dO
+// operands are read like V in the forward. The sums go to the last partial
+// slot of the reduce.
+constexpr int kKvStats = 2 * kHalf;          // lse then delta of the chunk's vectors
+constexpr int kKvBuf = kKvStats + 2 * 32 * 4;
+constexpr int kChunksPerTile = kTileVecs / 32;
+
+template <int OPS>
+__device__ __forceinline__ void wait_chunk_ops(int ch, int nch)
+{
+    if (ch + 2 < nch) QSA_WAIT_VM(2 * OPS);
+    else if (ch + 1 < nch) QSA_WAIT_VM(OPS);
+    else QSA_WAIT_VM(0);
+}
+
+__device__ __forceinline__ void dkdv_dense_item(const Problem &p, lds_char *buf)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 15, quad = lane >> 4;
+    const int64_t item = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int64_t per_bg = p.nKT * 2;
+    if (item >= p.B * p.Hkv * per_bg) return;
+    const int64_t bg = item / per_bg;
+    const int64_t rem = item - bg * per_bg;
+    const int64_t b = bg / p.Hkv;
+    const int g = (int)(bg - b * p.Hkv);
+    const int64_t t = rem >> 1;
+    const int64_t key0 = t * kTile + (rem & 1) * 64 + 16 * wave;
+    const int64_t ngroups = p.stride >> 4;
+    uint8_t *flag = p.kv_flag + (bg * p.nslot + p.nseg) * ngroups + (key0 >> 4);
+    const int32_t fcnt = p.rev_f_cnt[b * p.nKT + t];
+    if (fcnt == 0) {  // the same for every wave of the group
+        if (lane == 0) *flag = 0;
+        return;
+    }
+    const __attribute__((address_space(4))) int32_t *ridx =
+        (const __attribute__((address_space(4))) int32_t *)(p.rev_f_idx + (b * p.nKT + t) * p.nQT);
+
+    // K and V of the wave's keys (all exist: full tiles are interior) as the B
+    // operands of S and dP: lane (key col, quad) holds columns 32s + 8quad .. +7.
+    bf16x8 kf[8], vf[8];
+    {
+        const int64_t kr = ((b * p.Skv + key0 + col) * p.Hkv + g) * (int64_t)kD + 8 * quad;
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) {
+            kf[s8] = as_bf16x8(*reinterpret_cast<const uint4 *>(p.k + kr + 32 * s8));
+            vf[s8] = as_bf16x8(*reinterpret_cast<const uint4 *>(p.v + kr + 32 * s8));
+        }
+    }
+    QSA_WAIT_VM(0);  // settle before the staging starts
+    f32x4 adk[16], adv[16];
+#pragma unroll
+    for (int db = 0; db < 16; ++db) {
+        adk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        adv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // Staging of chunk c: query tile ridx[c / 48], vectors 32 (c % 48) + j.
+    // Instruction s puts vectors s (lanes 0..31) and s + 16 (lanes 32..63) at
+    // s * 1024, lane l taking chunk (l & 31) ^ swz_mask(s) of its vector; wave
+    // w issues s = 4w .. 4w+3 for Q and for dO, wave 0 also lse and delta
+    // (lane l < 32: vector l).
+    const uint32_t tile_bytes = (uint32_t)((kTile - 1) * p.Hq * kD * 2 + kGroup * kD * 2);
+    const uint32_t stat_bytes = (uint32_t)(((kGroup - 1) * p.Sq + kTile) * 4);
+    const uint32_t base = lds_addr(buf);
+    const uint32_t chunk16 = (uint32_t)(lane & 31) << 4;
+    auto vec_off = [&](int v) { return (uint32_t)(((v / kGroup) * p.Hq + v % kGroup) * kD * 2); };
+    auto issue = [&](int c) {
+        const int64_t r = ridx[c / kChunksPerTile];
+        const int cc = c % kChunksPerTile;
+        const int64_t tb = ((b * p.Sq + r * kTile) * p.Hq + g * kGroup) * (int64_t)kD;
+        const i32x4 rq = rsrc_words(p.q + tb, tile_bytes);
+        const i32x4 rg = rsrc_words(p.dout + tb, tile_bytes);
+        const uint32_t dst = base + (uint32_t)((c % kRing) * kKvBuf);
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+            const int s = 4 * wave + y;
+            const uint32_t o = vec_off(32 * cc + s + 16 * (lane >> 5)) + (chunk16 ^ ((uint32_t)swz_mask(s) << 4));
+            dma16_asm(rq, dst + (uint32_t)s * 1024, o);
+            dma16_asm(rg, dst + kHalf + (uint32_t)s * 1024, o);
+        }
+        if (wave == 0) {
+            const int64_t sb = (b * p.Hq + g * kGroup) * p.Sq + r * kTile;
+            const i32x4 rl = rsrc_words(p.lse_in + sb, stat_bytes);
+            const i32x4 rd = rsrc_words(p.delta + sb, stat_bytes);
+            const int v = 32 * cc + (lane & 31);
+            const uint32_t so = (uint32_t)(((v % kGroup) * p.Sq + v / kGroup) * 4);
+            if (lane < 32) {
+                dma4_asm(rl, dst + kKvStats, so);
+                dma4_asm(rd, dst + kKvStats + 128, so);
+            }
+        }
+    };
+
+    // Reads: Q and dO in the row layout (A operands of S and dP; lane (vector
+    // col, quad) takes chunk 4t + quad of slot 16x + col) and transposed (B
+    // operands of dK and dV; lane i of group quad names the 8-byte unit of slot
+    // 16x + 4 quad + i/4 holding columns 16db + 4(i%4) .. +3).
+    const int amask = swz_mask(col);
+    const int tvec = 4 * quad + (col >> 2);
+    const int tm = swz_mask(tvec);
+    const int tlane = tvec * 1024 + ((((col >> 1) & 1) ^ (tm & 1)) << 4) + (col & 1) * 8;
+    const int txor = tm >> 1;
+    const float c = p.scale * 1.4426950408889634f;
+
+    auto compute = [&](uint32_t cb) {
+        const lds_char *qs = (const lds_char *)(uintptr_t)cb;
+        const lds_char *gs = qs + kHalf;
+        typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+        float pn[2][4], dn[2][4];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            uint4 qa[8], ga[8];
+#pragma unroll
+            for (int t8 = 0; t8 < 8; ++t8) {
+                const int o = col * 1024 + 512 * x + (((4 * t8 + quad) ^ amask) << 4);
+                qa[t8] = lds_read16(qs + o);
+                ga[t8] = lds_read16(gs + o);
+            }
+            f32x4 sa = {0.f, 0.f, 0.f, 0.f}, pd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t8 = 0; t8 < 8; ++t8) {
+                sa = mfma_16x16x32(as_bf16x8(qa[t8]), kf[t8], sa);
+                pd = mfma_16x16x32(as_bf16x8(ga[t8]), vf[t8], pd);
+            }
+            const f32x4 ls = *reinterpret_cast<const lds_f32x4 *>(qs + kKvStats + (16 * x + 4 * quad) * 4);
+            const f32x4 dl = *reinterpret_cast<const lds_f32x4 *>(qs + kKvStats + 128 + (16 * x + 4 * quad) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float pr = __builtin_amdgcn_exp2f(sa[e] * c - ls[e] * 1.4426950408889634f);
+                pn[x][e] = pr;
+                dn[x][e] = pr * (pd[e] - dl[e]);
+            }
+        }
+        uint32_t ph[4], pl[4], dh[4], dlo[4];
+        split_bf16x2(pn[0][0], pn[0][1], ph[0], pl[0]);
+        split_bf16x2(pn[0][2], pn[0][3], ph[1], pl[1]);
+        split_bf16x2(pn[1][0], pn[1][1], ph[2], pl[2]);
+        split_bf16x2(pn[1][2], pn[1][3], ph[3], pl[3]);
+        split_bf16x2(dn[0][0], dn[0][1], dh[0], dlo[0]);
+        split_bf16x2(dn[0][2], dn[0][3], dh[1], dlo[1]);
+        split_bf16x2(dn[1][0], dn[1][1], dh[2], dlo[2]);
+        split_bf16x2(dn[1][2], dn[1][3], dh[3], dlo[3]);
+        const bf16x8 A_p = as_bf16x8(make_uint4(ph[0], ph[1], ph[2], ph[3]));
+        const bf16x8 A_pl = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
+        const bf16x8 A_d = as_bf16x8(make_uint4(dh[0], dh[1], dh[2], dh[3]));
+        const bf16x8 A_dl = as_bf16x8(make_uint4(dlo[0], dlo[1], dlo[2], dlo[3]));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint2 tq[2][8], tg[2][8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int o = tlane + (((8 * h + j) ^ txor) << 5);
+                tq[0][j] = lds_read_tr(qs + o);
+                tq[1][j] = lds_read_tr(qs + o + 512);
+                tg[0][j] = lds_read_tr(gs + o);
+                tg[1][j] = lds_read_tr(gs + o + 512);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int db = 8 * h + j;
+                const bf16x8 Bg = as_bf16x8(make_uint4(tg[0][j].x, tg[0][j].y, tg[1][j].x, tg[1][j].y));
+                const bf16x8 Bq = as_bf16x8(make_uint4(tq[0][j].x, tq[0][j].y, tq[1][j].x, tq[1][j].y));
+                adv[db] = mfma_16x16x32(A_p, Bg, adv[db]);
+                adv[db] = mfma_16x16x32(A_pl, Bg, adv[db]);
+                adk[db] = mfma_16x16x32(A_d, Bq, adk[db]);
+                adk[db] = mfma_16x16x32(A_dl, Bq, adk[db]);
+            }
+        }
+    };
+
+    const int nch = fcnt * kChunksPerTile;
+    for (int c0 = 0; c0 < kRing - 1 && c0 < nch; ++c0) issue(c0);
+    for (int ch = 0; ch < nch; ++ch) {
+        if (wave == 0) wait_chunk_ops<kChunkOps + 2>(ch, nch);
+        else wait_chunk_ops<kChunkOps>(ch, nch);
+        __builtin_amdgcn_s_barrier();
+        const uint32_t cb = opaque_u32(base + (uint32_t)((ch % kRing) * kKvBuf));
+        if (ch + kRing - 1 < nch) issue(ch + kRing - 1);
+        compute(cb);
+    }
+    QSA_WAIT_VM(0);
+
+    // Lane holds dK/dV[key 4*quad+e][d 16*db + col].
+    float *part = p.kv_part + ((bg * p.nslot + p.nseg) * p.stride + key0) * (int64_t)(2 * kD);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float *pk = part + (4 * quad + e) * (int64_t)(2 * kD) + col;
+#pragma unroll
+        for (int db = 0; db < 16; ++db) {
+            pk[16 * db] = adk[db][e];
+            pk[kD + 16 * db] = adv[db][e];
+        }
+    }
+    if (lane == 0) *flag = 1;
+}
+
+__global__ __launch_bounds__(64 * kDenseWaves) void k_dkdv_dense(Problem p)
+{
+    __shared__ __attribute__((aligned(16))) char buf[kRing * kKvBuf];
+    dkdv_dense_item(p, (lds_char *)buf);
 }
 
 }  // namespace
+
+hipError_t launch_dkdv_dense(const Problem &p, hipStream_t s)
+{
+    const int64_t items = p.B * p.Hkv * p.nKT * 2;
+    hipLaunchKernelGGL(k_dkdv_dense, dim3((unsigned)items), dim3(64 * kDenseWaves), 0, s, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_forward_dense(const Problem &p, hipStream_t s)
 {
@@ -331,9 +747,9 @@ hipError_t launch_forward_dense(const Problem &p, hipStream_t s)
 
 hipError_t launch_dq_dense(const Problem &p, hipStream_t s)
 {
-    (void)p;
-    (void)s;
-    return hipSuccess;
+    const int64_t items = p.B * p.Hkv * p.nQT * kVBlocks;
+    hipLaunchKernelGGL(k_dq_dense, dim3((unsigned)items), dim3(64 * kDenseWaves), 0, s, p);
+    return hipGetLastError();
 }
 
 }  // namespace qsa
