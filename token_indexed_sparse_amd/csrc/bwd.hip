@@ -233,15 +233,19 @@ __global__ __launch_bounds__(64) void k_dq(Problem p)
 }
 
 // ---------------------------------------------------------------- dK, dV
-constexpr int kHitCap = 512;  // LDS hit list entries per batch
-constexpr int kScanWin = 4;   // 64-row windows scanned per step
-constexpr int kSlot = 2 * kGroup * 512;  // Q then dO rows of the group's heads
+constexpr int kHitCap = 384;  // LDS hit list entries per batch
+constexpr int kScanWin = 2;   // 64-row windows scanned per step
+// One staged row: Q then dO of the group's 12 heads (512 bytes each), then lse
+// and delta of heads 0..15 (16 floats each, zero past head 11).
+constexpr int kStatOff = 2 * kGroup * 512;
+constexpr int kSlot = kStatOff + 2 * 16 * 4;
+constexpr int kRingRows = 3;        // staged rows per wave: two fly while one is computed
+constexpr int kRowOps = 2 * 6 + 2;  // direct-to-LDS loads per staged row
 
-// Body of k_dkdv. slots: two staging slots of kSlot bytes; zero: 4 rows of
-// 512 zero bytes read in place of the padding heads 12..15; hrow/hmask: the
-// wave's hit list.
-__device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, lds_char *zero,
-                                          int32_t *hrow, uint32_t *hmask)
+// Body of k_dkdv. slots: kRingRows staging slots of kSlot bytes; hrow/hmask:
+// the wave's hit list.
+__device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int32_t *hrow,
+                                          uint32_t *hmask)
 {
     const int lane = threadIdx.x;
     const int col = lane & 15, quad = lane >> 4;
@@ -287,9 +291,6 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, lds
     if (lane == 0) *flag = nwin > 0 ? 1 : 0;
     if (nwin == 0) return;
 
-    // Padding heads of the transposed operands read zeros.
-    for (int o = lane * 16; o < 4 * 512; o += 64 * 16)
-        *reinterpret_cast<__attribute__((address_space(3))) u32x4 *>(zero + o) = u32x4{0u, 0u, 0u, 0u};
 
     // K and V rows of the 16 keys as B operands of S = Q K^T and dP = dO V^T:
     // lane (key col, quad) holds columns 32t + 8quad .. +7 for step t.
@@ -306,6 +307,10 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, lds
             kf[s] = as_bf16x8(buf_load16(rk, off + 64 * s));
             vf[s] = as_bf16x8(buf_load16(rv, off + 64 * s));
         }
+        // Settle these loads here: the staging below is written in assembly,
+        // which the compiler cannot count, and the counted waits in the loop
+        // are then the only vector memory waits there.
+        QSA_WAIT_VM(0);
     }
     f32x4 adk[16], adv[16];
 #pragma unroll
@@ -318,30 +323,37 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, lds
 
     // Rows of Q and dO of this batch and group (12 heads x 512 bytes each,
     // contiguous), lse and delta of this batch and group.
-    const uint32_t q_bytes = (uint32_t)((p.Sq - 1) * p.Hq * kD * 2 + kGroup * kD * 2);
-    const rsrc_t rq = make_rsrc(p.q + (b * p.Sq * p.Hq + g * kGroup) * (int64_t)kD, q_bytes);
-    const rsrc_t rg = make_rsrc(p.dout + (b * p.Sq * p.Hq + g * kGroup) * (int64_t)kD, q_bytes);
-    const rsrc_t rl = make_rsrc(p.lse_in + (b * p.Hq + g * kGroup) * p.Sq,
-                                (uint32_t)(kGroup * p.Sq * 4));
-    const rsrc_t rd = make_rsrc(p.delta + (b * p.Hq + g * kGroup) * p.Sq,
-                                (uint32_t)(kGroup * p.Sq * 4));
-    // Gather of one row into a slot: instruction x < 6 stages Q heads 2x and
-    // 2x+1, instruction 6+x the same dO heads, in the swizzled layout.
-    auto gather_row = [&](int64_t qi, lds_char *slot) {
-        const uint32_t rb = (uint32_t)(qi * p.Hq * kD * 2);
+    const uint16_t *qbase = p.q + (b * p.Sq * p.Hq + g * kGroup) * (int64_t)kD;
+    const uint16_t *gbase = p.dout + (b * p.Sq * p.Hq + g * kGroup) * (int64_t)kD;
+    const float *lbase = p.lse_in + (b * p.Hq + g * kGroup) * p.Sq;
+    const float *dbase = p.delta + (b * p.Hq + g * kGroup) * p.Sq;
+    // Staging of one row into a slot (direct-to-LDS loads written in
+    // assembly): instruction x < 6 stages Q heads 2x and 2x+1, instruction 6+x
+    // the same dO heads, in the swizzled layout; then lse and delta, lane h < 16
+    // staging head h (heads 12..15 read as zero). The row start goes into the
+    // descriptors, so the lanes' offsets never change.
+    uint32_t lc[6];
+#pragma unroll
+    for (int x = 0; x < 6; ++x)
+        lc[x] = (uint32_t)(x * 1024 + (lane >> 5) * 512 + (dma_chunk(lane, x) << 4));
+    const uint32_t sv = lane < kGroup ? (uint32_t)(lane * p.Sq * 4) : kOutOfRange;
+    const uint32_t slots_addr = lds_addr(slots);
+    auto stage_row = [&](uint32_t qi, int slot) {
+        const int64_t ro = (int64_t)qi * p.Hq * kD;
+        const i32x4 rq = rsrc_words(qbase + ro, (uint32_t)(kGroup * kD * 2));
+        const i32x4 rg = rsrc_words(gbase + ro, (uint32_t)(kGroup * kD * 2));
+        const uint32_t dst = slots_addr + (uint32_t)(slot * kSlot);
 #pragma unroll
         for (int x = 0; x < 6; ++x) {
-            const uint32_t o = rb + (uint32_t)(x * 1024 + (lane >> 5) * 512 + (dma_chunk(lane, x) << 4));
-            dma16(rq, slot + x * 1024, o);
-            dma16(rg, slot + kGroup * 512 + x * 1024, o);
+            dma16_asm(rq, dst + x * 1024, lc[x]);
+            dma16_asm(rg, dst + kGroup * 512 + x * 1024, lc[x]);
         }
-    };
-    auto load_stats = [&](int64_t qi, float (&ls)[4], float (&dl)[4]) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = hq ? (uint32_t)(((4 * quad + e) * p.Sq + qi) * 4) : kOutOfRange;
-            ls[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, lo, 0, 0));
-            dl[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, lo, 0, 0));
+        const uint32_t bytes = (uint32_t)((kGroup * p.Sq - qi) * 4);
+        const i32x4 rl = rsrc_words(lbase + qi, bytes);
+        const i32x4 rd = rsrc_words(dbase + qi, bytes);
+        if (lane < 16) {
+            dma4_asm(rl, dst + kStatOff, sv);
+            dma4_asm(rd, dst + kStatOff + 64, sv);
         }
     };
 
@@ -352,11 +364,11 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, lds
     const int amask = swz_mask(ahead);
     // Transposed read (B operand of dV and dK): lane i of group quad names the
     // 8-byte unit of head 4*quad + i/4 holding columns 16db + 4(i%4) .. +3;
-    // group 3 (heads 12..15) reads the zero rows.
-    const int th = 4 * quad + (col >> 2);
+    // group 3 (padding heads 12..15) reads heads 8..11 of the same row, which
+    // meet exact zeros of P and dS.
+    const int th = (quad < 3 ? 4 * quad : 8) + (col >> 2);
     const int tm = swz_mask(th);
-    const int tlane = (quad < 3 ? th * 512 : (col >> 2) * 512) +
-                      ((((col >> 1) & 1) ^ (tm & 1)) << 4) + (col & 1) * 8;
+    const int tlane = th * 512 + ((((col >> 1) & 1) ^ (tm & 1)) << 4) + (col & 1) * 8;
     const int txor = tm >> 1;
 
     // Pending row of the current pair: its P, dS and transposed operands.
@@ -402,7 +414,6 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, lds
     int64_t w = 0;
     int32_t ip = p_hi - 1, jf = f_hi - 1;
     int32_t cur_tile = -1;
-    float ls_n[4], dl_n[4];
     while (w < nwin) {
         int nh = 0;
         while (w < nwin && nh <= kHitCap - kScanWin * 64) {
@@ -443,39 +454,39 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, lds
         }
         if (nh == 0) continue;
         wave_lds_sync();
-        // Rows of the batch in order; row h is staged in slot h & 1 while the
-        // wave computes row h - 1.
-        int64_t rcur = hrow[0];
-        uint32_t mcur = hmask[0];
-        float ls_c[4], dl_c[4];
-        QSA_WAIT_LDS();
-        gather_row(rcur, slots);
-        load_stats(rcur, ls_c, dl_c);
+        // Rows of the batch in order; row h is staged in slot h % 3, up to two
+        // rows ahead of the one being computed. A row's slot is refilled at the
+        // end of its step, once all its reads have returned.
+        auto hit_row = [&](int h) { return __builtin_amdgcn_readfirstlane((uint32_t)hrow[h]); };
+        for (int r0 = 0; r0 < kRingRows && r0 < nh; ++r0) stage_row(hit_row(r0), r0);
+        int slot = 0;
         for (int h = 0; h < nh; ++h) {
-            lds_char *slot = slots + (h & 1) * kSlot;
-            QSA_WAIT_VM(0);
+            // Row h has landed once at most the rows staged after it are in flight.
+            if (h + 2 < nh) QSA_WAIT_VM(2 * kRowOps);
+            else if (h + 1 < nh) QSA_WAIT_VM(kRowOps);
+            else QSA_WAIT_VM(0);
+            // The reads take their address from this block, so none of them is
+            // moved above the wait.
+            const lds_char *sl = (const lds_char *)(uintptr_t)opaque_u32(slots_addr + (uint32_t)(slot * kSlot));
+            const uint32_t mcur = hmask[h];
             uint4 qa[8], ga[8];
 #pragma unroll
             for (int t8 = 0; t8 < 8; ++t8) {
                 const int o = ahead * 512 + (((4 * t8 + quad) ^ amask) << 4);
-                qa[t8] = lds_read16(slot + o);
-                ga[t8] = lds_read16(slot + kGroup * 512 + o);
+                qa[t8] = lds_read16(sl + o);
+                ga[t8] = lds_read16(sl + kGroup * 512 + o);
             }
             uint2 tq[16], tg[16];
 #pragma unroll
             for (int db = 0; db < 16; ++db) {
                 const int o = tlane + ((db ^ txor) << 5);
-                tq[db] = lds_read_tr((quad < 3 ? slot : zero) + o);
-                tg[db] = lds_read_tr((quad < 3 ? slot + kGroup * 512 : zero) + o);
+                tq[db] = lds_read_tr(sl + o);
+                tg[db] = lds_read_tr(sl + kGroup * 512 + o);
             }
-            const bool more = h + 1 < nh;
-            const int64_t rnext = more ? hrow[h + 1] : 0;
-            const uint32_t mnext = more ? hmask[h + 1] : 0u;
-            QSA_WAIT_LDS();
-            if (more) {
-                gather_row(rnext, slots + ((h + 1) & 1) * kSlot);
-                load_stats(rnext, ls_n, dl_n);
-            }
+            // lse and delta of heads 4*quad .. 4*quad+3
+            typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+            const f32x4 ls_c = *reinterpret_cast<const lds_f32x4 *>(sl + kStatOff + quad * 16);
+            const f32x4 dl_c = *reinterpret_cast<const lds_f32x4 *>(sl + kStatOff + 64 + quad * 16);
 
             f32x4 sa = {0.f, 0.f, 0.f, 0.f}, pd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -509,14 +520,14 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, lds
                 }
                 pending = true;
             }
-            rcur = rnext;
-            mcur = mnext;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                ls_c[e] = ls_n[e];
-                dl_c[e] = dl_n[e];
+            if (h + kRingRows < nh) {
+                const uint32_t qn = hit_row(h + kRingRows);
+                QSA_WAIT_LDS();  // every read of this slot has returned
+                stage_row(qn, slot);
             }
+            slot = slot == kRingRows - 1 ? 0 : slot + 1;
         }
+        QSA_WAIT_VM(0);
         wave_lds_sync();
     }
     if (pending) {
@@ -543,11 +554,10 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, lds
 
 __global__ __launch_bounds__(64) void k_dkdv(Problem p)
 {
-    __shared__ __attribute__((aligned(16))) char slots[2 * kSlot];
-    __shared__ __attribute__((aligned(16))) char zero[4 * 512];
+    __shared__ __attribute__((aligned(16))) char slots[kRingRows * kSlot];
     __shared__ int32_t hrow[kHitCap];
     __shared__ uint32_t hmask[kHitCap];
-    dkdv_item(p, (lds_char *)slots, (lds_char *)zero, hrow, hmask);
+    dkdv_item(p, (lds_char *)slots, hrow, hmask);
 }
 
 // dK = scale * sum of the partials, dV = sum, in slot order (the segments,
