@@ -64,8 +64,11 @@ Layout layout(const qsa_dims *d, int which)
         return at;
     };
     const size_t none = (size_t)-1;
-    L.memb = which == 2 ? none : take((size_t)(rows * stride));
-    L.has = which == 2 ? none : take((size_t)rows);
+    // The byte membership table and has_routes are outputs of qsa_preprocess
+    // only (caller buffers): no forward or backward kernel reads them, so those
+    // calls do not materialise them.
+    L.memb = none;
+    L.has = none;
     L.mbits = which == 1 ? take((size_t)(rows * (stride / 32)) * 4) : none;
     L.row_keys = take((size_t)(rows * d->W) * 4);
     L.row_cnt = take((size_t)rows * 4);

@@ -190,13 +190,23 @@ __global__ __launch_bounds__(256) void k_partial_keys(Problem p)
     int32_t *out = p.pkeys + row * p.W;
     const int n = p.row_cnt[row];
     int cnt = 0;
-    for (int s0 = 0; s0 < n; s0 += 64) {
-        const int s = s0 + lane;
-        const int32_t key = s < n ? keys[s] : 0;
-        const bool keep = s < n && kd[key >> 7] != 2;
-        const uint64_t ball = __ballot(keep);
-        if (keep) out[cnt + __popcll(ball & below)] = key;
-        cnt += __popcll(ball);
+    // Four 64-key groups per round, so that their loads are in flight together.
+    for (int s0 = 0; s0 < n; s0 += 256) {
+        int32_t key[4];
+        bool keep[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int s = s0 + 64 * u + lane;
+            key[u] = s < n ? keys[s] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) keep[u] = s0 + 64 * u + lane < n && kd[key[u] >> 7] != 2;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint64_t ball = __ballot(keep[u]);
+            if (keep[u]) out[cnt + __popcll(ball & below)] = key[u];
+            cnt += __popcll(ball);
+        }
     }
     if (lane == 0) p.pcnt[row] = cnt;
 }
