@@ -499,7 +499,8 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
             float pn[4], dn[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float pr = on ? exp2f(sa[e] * c - ls_c[e] * 1.4426950408889634f) : 0.f;
+                const float pr =
+                    on ? __builtin_amdgcn_exp2f(sa[e] * c - ls_c[e] * 1.4426950408889634f) : 0.f;
                 pn[e] = pr;
                 // select, never multiply: an unselected key's dP may be non-finite
                 dn[e] = on ? pr * (pd[e] - dl_c[e]) : 0.f;
