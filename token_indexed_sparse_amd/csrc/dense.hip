@@ -8,17 +8,17 @@
 // ("fa4_qsa" page, `_block_kinds`: count == 128 * 128); such pairs are
 // exactly the keys the partial key lists leave out.
 //
-// Design (one work group of four waves per query tile, KV head and block of
-// 128 (row, head) vectors):
+// Design (one work group of eight waves, two per SIMD, per query tile, KV
+// head and block of 128 (row, head) vectors):
 //  * Inside a full tile every (row, head) vector of the tile sees the same
 //    keys, so the MFMA blocks take 16 consecutive vectors of the tile (rows
 //    and heads mixed) instead of the 12 heads of one row: no padding lanes.
-//    A wave owns two such blocks (32 vectors), a work group 128, and the 12
+//    A wave owns one such block (16 vectors), a work group 128, and the 12
 //    work groups of a query tile are consecutive blocks, which the XCD-aware
 //    mapping keeps on one XCD so the key tiles they share stay in its L2.
 //  * Keys come in chunks of 32 from the tile row's full key tiles. A chunk's
 //    K and V rows are contiguous, staged once per work group into LDS by
-//    direct-to-LDS loads (each wave issues a quarter) in the swizzled layout
+//    direct-to-LDS loads (each wave issues an eighth) in the swizzled layout
 //    of the gathered forward, into a ring of four chunk buffers: three chunks
 //    fly while one is computed. A wave waits (counted) for its own loads of
 //    the chunk, then the work-group barrier makes every wave's loads visible
@@ -36,8 +36,8 @@ namespace qsa {
 
 namespace {
 
-constexpr int kDenseWaves = 4;
-constexpr int kVecBlocks = 2;                                  // 16-vector blocks per wave
+constexpr int kDenseWaves = 8;  // two waves per SIMD
+constexpr int kVecBlocks = 1;                                  // 16-vector blocks per wave
 constexpr int kGroupVecs = kDenseWaves * 16 * kVecBlocks;      // vectors per work group
 constexpr int kTileVecs = kTile * kGroup;                      // vectors of a query tile
 constexpr int kVBlocks = kTileVecs / kGroupVecs;               // work groups per query tile
@@ -45,10 +45,11 @@ constexpr int kKeys = 32;                                      // keys per stage
 constexpr int kHalf = kKeys * 512;                             // K (or V) bytes of a chunk
 constexpr int kBuf = 2 * kHalf;                                // K then V
 constexpr int kRing = 4;        // chunk buffers: three chunks in flight ahead
-constexpr int kChunkOps = 8;    // direct-to-LDS loads a wave issues per chunk
+constexpr int kStage = 16 / kDenseWaves;  // staging instructions per wave and tensor
+constexpr int kChunkOps = 2 * kStage;     // direct-to-LDS loads a wave issues per chunk
 constexpr float kSlack = 64.f;  // log2 of the largest unnormalised P
 static_assert(kTileVecs % kGroupVecs == 0, "work groups must tile the query tile");
-static_assert(kDenseWaves * 4 == 16, "each wave stages four of the 16 row pairs");
+static_assert(kDenseWaves * kStage == 16, "the waves share the 16 row pairs of a chunk");
 
 // This wave's loads of chunk ch have landed once at most the loads of the
 // chunks issued after it (up to kRing - 2 of them) are in flight.
@@ -136,16 +137,16 @@ __device__ __forceinline__ void forward_dense_item(const Problem &p, lds_char *b
 
     // Staging: instruction s (0..15) puts key slot s (lanes 0..31) and s + 16
     // (lanes 32..63) of a chunk at s * 1024, lane l taking chunk
-    // (l & 31) ^ swz_mask(s) of its row; wave w issues s = 4w .. 4w+3 for K
+    // (l & 31) ^ swz_mask(s) of its row; wave w issues s = 2w, 2w+1 for K
     // and for V. The chunk's first key goes into the descriptors, so the lane
     // offsets never change.
     const uint32_t row_bytes = (uint32_t)(p.Hkv * kD * 2);
     const uint16_t *kbase = p.k + (b * p.Skv * p.Hkv + g) * (int64_t)kD;
     const uint16_t *vbase = p.v + (b * p.Skv * p.Hkv + g) * (int64_t)kD;
-    uint32_t loff[4];
+    uint32_t loff[kStage];
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-        const int s = 4 * wave + y;
+    for (int y = 0; y < kStage; ++y) {
+        const int s = kStage * wave + y;
         loff[y] = (uint32_t)(s + 16 * (lane >> 5)) * row_bytes +
                   ((uint32_t)((lane & 31) ^ swz_mask(s)) << 4);
     }
@@ -156,8 +157,8 @@ __device__ __forceinline__ void forward_dense_item(const Problem &p, lds_char *b
         const i32x4 rv = rsrc_words(vbase + key0 * p.Hkv * kD, kKeys * row_bytes);
         const uint32_t dst = base + (uint32_t)((c % kRing) * kBuf);
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-            const uint32_t s = (uint32_t)(4 * wave + y);
+        for (int y = 0; y < kStage; ++y) {
+            const uint32_t s = (uint32_t)(kStage * wave + y);
             dma16_asm(rk, dst + s * 1024, loff[y]);
             dma16_asm(rv, dst + kHalf + s * 1024, loff[y]);
         }
@@ -387,10 +388,10 @@ __device__ __forceinline__ void dq_dense_item(const Problem &p, lds_char *buf)
     const uint32_t row_bytes = (uint32_t)(p.Hkv * kD * 2);
     const uint16_t *kbase = p.k + (b * p.Skv * p.Hkv + g) * (int64_t)kD;
     const uint16_t *vbase = p.v + (b * p.Skv * p.Hkv + g) * (int64_t)kD;
-    uint32_t loff[4];
+    uint32_t loff[kStage];
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-        const int s = 4 * wave + y;
+    for (int y = 0; y < kStage; ++y) {
+        const int s = kStage * wave + y;
         loff[y] = (uint32_t)(s + 16 * (lane >> 5)) * row_bytes +
                   ((uint32_t)((lane & 31) ^ swz_mask(s)) << 4);
     }
@@ -401,8 +402,8 @@ __device__ __forceinline__ void dq_dense_item(const Problem &p, lds_char *buf)
         const i32x4 rv = rsrc_words(vbase + key0 * p.Hkv * kD, kKeys * row_bytes);
         const uint32_t dst = base + (uint32_t)((c % kRing) * kBuf);
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-            const uint32_t s = (uint32_t)(4 * wave + y);
+        for (int y = 0; y < kStage; ++y) {
+            const uint32_t s = (uint32_t)(kStage * wave + y);
             dma16_asm(rk, dst + s * 1024, loff[y]);
             dma16_asm(rv, dst + kHalf + s * 1024, loff[y]);
         }
@@ -531,6 +532,11 @@ __global__ __launch_bounds__(64 * kDenseWaves) void k_dq_dense(Problem p)
 constexpr int kKvStats = 2 * kHalf;          // lse then delta of the chunk's vectors
 constexpr int kKvBuf = kKvStats + 2 * 32 * 4;
 constexpr int kChunksPerTile = kTileVecs / 32;
+constexpr int kKvWaves = 4;                       // waves of a dK/dV work group, 16 keys each
+constexpr int kKvStage = 16 / kKvWaves;           // Q (and dO) staging instructions per wave
+constexpr int kKvChunkOps = 2 * kKvStage;         // direct-to-LDS loads a wave issues per chunk
+constexpr int kKvParts = kTile / (16 * kKvWaves);  // work groups per key tile
+static_assert(kKvParts * 16 * kKvWaves == kTile, "waves of 16 keys must tile the key tile");
 
 template <int OPS>
 __device__ __forceinline__ void wait_chunk_ops(int ch, int nch)
@@ -546,14 +552,14 @@ __device__ __forceinline__ void dkdv_dense_item(const Problem &p, lds_char *buf)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15, quad = lane >> 4;
     const int64_t item = xcd_logical_block(blockIdx.x, gridDim.x);
-    const int64_t per_bg = p.nKT * 2;
+    const int64_t per_bg = p.nKT * kKvParts;
     if (item >= p.B * p.Hkv * per_bg) return;
     const int64_t bg = item / per_bg;
     const int64_t rem = item - bg * per_bg;
     const int64_t b = bg / p.Hkv;
     const int g = (int)(bg - b * p.Hkv);
-    const int64_t t = rem >> 1;
-    const int64_t key0 = t * kTile + (rem & 1) * 64 + 16 * wave;
+    const int64_t t = rem / kKvParts;
+    const int64_t key0 = t * kTile + (rem - t * kKvParts) * (16 * kKvWaves) + 16 * wave;
     const int64_t ngroups = p.stride >> 4;
     uint8_t *flag = p.kv_flag + (bg * p.nslot + p.nseg) * ngroups + (key0 >> 4);
     const int32_t fcnt = p.rev_f_cnt[b * p.nKT + t];
@@ -601,8 +607,8 @@ __device__ __forceinline__ void dkdv_dense_item(const Problem &p, lds_char *buf)
         const i32x4 rg = rsrc_words(p.dout + tb, tile_bytes);
         const uint32_t dst = base + (uint32_t)((c % kRing) * kKvBuf);
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-            const int s = 4 * wave + y;
+        for (int y = 0; y < kKvStage; ++y) {
+            const int s = kKvStage * wave + y;
             const uint32_t o = vec_off(32 * cc + s + 16 * (lane >> 5)) + (chunk16 ^ ((uint32_t)swz_mask(s) << 4));
             dma16_asm(rq, dst + (uint32_t)s * 1024, o);
             dma16_asm(rg, dst + kHalf + (uint32_t)s * 1024, o);
@@ -700,8 +706,8 @@ __device__ __forceinline__ void dkdv_dense_item(const Problem &p, lds_char *buf)
     const int nch = fcnt * kChunksPerTile;
     for (int c0 = 0; c0 < kRing - 1 && c0 < nch; ++c0) issue(c0);
     for (int ch = 0; ch < nch; ++ch) {
-        if (wave == 0) wait_chunk_ops<kChunkOps + 2>(ch, nch);
-        else wait_chunk_ops<kChunkOps>(ch, nch);
+        if (wave == 0) wait_chunk_ops<kKvChunkOps + 2>(ch, nch);
+        else wait_chunk_ops<kKvChunkOps>(ch, nch);
         __builtin_amdgcn_s_barrier();
         const uint32_t cb = opaque_u32(base + (uint32_t)((ch % kRing) * kKvBuf));
         if (ch + kRing - 1 < nch) issue(ch + kRing - 1);
@@ -723,7 +729,7 @@ __device__ __forceinline__ void dkdv_dense_item(const Problem &p, lds_char *buf)
     if (lane == 0) *flag = 1;
 }
 
-__global__ __launch_bounds__(64 * kDenseWaves) void k_dkdv_dense(Problem p)
+__global__ __launch_bounds__(64 * kKvWaves) void k_dkdv_dense(Problem p)
 {
     __shared__ __attribute__((aligned(16))) char buf[kRing * kKvBuf];
     dkdv_dense_item(p, (lds_char *)buf);
@@ -733,8 +739,8 @@ __global__ __launch_bounds__(64 * kDenseWaves) void k_dkdv_dense(Problem p)
 
 hipError_t launch_dkdv_dense(const Problem &p, hipStream_t s)
 {
-    const int64_t items = p.B * p.Hkv * p.nKT * 2;
-    hipLaunchKernelGGL(k_dkdv_dense, dim3((unsigned)items), dim3(64 * kDenseWaves), 0, s, p);
+    const int64_t items = p.B * p.Hkv * p.nKT * kKvParts;
+    hipLaunchKernelGGL(k_dkdv_dense, dim3((unsigned)items), dim3(64 * kKvWaves), 0, s, p);
     return hipGetLastError();
 }
 
