@@ -18,6 +18,22 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Query tiles per dK/dV segment: short segments keep the rows that the
+// concurrent work items stage close together (more L2 hits), at the cost of
+// more partial sums, which are bounded by kPartialBudget.
+int64_t seg_tiles_for(const qsa_dims *d)
+{
+    const int64_t nQT = (d->Sq + kTile - 1) / kTile;
+    const int64_t stride = (d->Skv + kTile - 1) / kTile * kTile;
+    int64_t seg = kSegTilesMin;
+    for (;;) {
+        const int64_t nseg = (nQT + seg - 1) / seg;
+        const int64_t bytes = d->B * d->Hkv * (nseg + 1) * stride * 2 * kD * 4;
+        if (bytes <= kPartialBudget || seg >= nQT) return seg;
+        seg *= 2;
+    }
+}
+
 qsa_status check_dims(const qsa_dims *d)
 {
     if (!d) return QSA_ERR_NULL;
@@ -34,7 +50,8 @@ qsa_status check_dims(const qsa_dims *d)
     const int64_t stride = (d->Skv + kTile - 1) / kTile * kTile;
     if (d->B * d->Hkv * stride > (int64_t(1) << 30)) return QSA_ERR_SHAPE;
     // dK/dV work items: one per query segment and 16-key group.
-    const int64_t nseg = ((d->Sq + kTile - 1) / kTile + kSegTiles - 1) / kSegTiles;
+    const int64_t seg = seg_tiles_for(d);
+    const int64_t nseg = ((d->Sq + kTile - 1) / kTile + seg - 1) / seg;
     if (nseg * d->B * d->Hkv * (stride / 16) >= (int64_t(1) << 31)) return QSA_ERR_SHAPE;
     // Gathers use 32-bit buffer offsets within one batch row of K/V or Q/dO.
     if (d->Skv * d->Hkv * kD * 2 >= (int64_t(1) << 31)) return QSA_ERR_SHAPE;
@@ -90,7 +107,8 @@ Layout layout(const qsa_dims *d, int which)
     }
     L.fstate = which == 0 ? take((size_t)(d->B * d->Hq * d->Sq) * 8) : none;
     L.delta = which == 1 ? take((size_t)(d->B * d->Hq * d->Sq) * 4) : none;
-    const int64_t nseg = (nQT + kSegTiles - 1) / kSegTiles;
+    const int64_t seg = seg_tiles_for(d);
+    const int64_t nseg = (nQT + seg - 1) / seg;
     // The dK/dV partial sums and the dQ hand-over are never live together
     // (dQ finishes before dK/dV starts), so they share one region.
     const size_t kv_bytes = (size_t)(d->B * d->Hkv * (nseg + 1) * stride) * 2 * kD * 4;
@@ -139,7 +157,8 @@ void fill_common(Problem &p, const qsa_dims *d, const void *routes, float scale)
     p.nQT = (d->Sq + kTile - 1) / kTile;
     p.nKT = (d->Skv + kTile - 1) / kTile;
     p.stride = p.nKT * kTile;
-    p.nseg = (p.nQT + kSegTiles - 1) / kSegTiles;
+    p.seg_tiles = seg_tiles_for(d);
+    p.nseg = (p.nQT + p.seg_tiles - 1) / p.seg_tiles;
     p.nslot = p.nseg + 1;
     p.scale = scale;
     p.routes = routes;

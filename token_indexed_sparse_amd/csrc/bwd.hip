@@ -271,8 +271,8 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
     // that fall in [t_lo, t_hi).
     const int64_t t = key0 >> 7;
     const int64_t bt = b * p.nKT + t;
-    const int32_t t_lo = (int32_t)(seg * kSegTiles);
-    const int32_t t_hi = (int32_t)((seg + 1) * kSegTiles);
+    const int32_t t_lo = (int32_t)(seg * p.seg_tiles);
+    const int32_t t_hi = (int32_t)((seg + 1) * p.seg_tiles);
     const int32_t *idx_p = p.rev_p_idx + bt * p.nQT, *idx_f = p.rev_f_idx + bt * p.nQT;
     auto lower_bound = [&](const int32_t *a, int32_t cnt, int32_t x) {
         int32_t lo = 0, hi = cnt;

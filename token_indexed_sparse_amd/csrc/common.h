@@ -11,7 +11,10 @@ namespace qsa {
 constexpr int kD = 256;     // head dimension (QSA page, "Support and execution")
 constexpr int kGroup = 12;  // query heads per KV head
 constexpr int kTile = 128;  // query and key tile edge of the membership table
-constexpr int kSegTiles = 32;  // query tiles per dK/dV work segment
+// dK/dV work segments: kSegTilesMin query tiles, doubled while the FP32
+// partial sums of all segments would exceed kPartialBudget bytes.
+constexpr int kSegTilesMin = 8;
+constexpr int64_t kPartialBudget = int64_t(4) << 30;
 constexpr int kMaxSkvLog2 = 19;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -54,7 +57,8 @@ struct Problem {
     float *kv_part;
     uint8_t *kv_flag;
     int64_t nseg;
-    int64_t nslot;  // nseg + 1 partial-sum slots per (batch, KV head)
+    int64_t nslot;      // nseg + 1 partial-sum slots per (batch, KV head)
+    int64_t seg_tiles;  // query tiles per segment
     // Hand-off from the gathered to the dense dQ: unscaled FP32 sums
     // [B, Sq, Hq, 256] of the rows whose tile row has full tiles.
     float *dq_part;
