@@ -9,7 +9,7 @@
 // Three kernels, no floating-point atomics anywhere:
 //  * k_delta: one wave per (row, head) reduces dO . out_fp32.
 //  * k_dq: query-major like the forward (one wave per row and KV head walks
-//    the row's sorted key list in 32-slot chunks; each chunk's K and V rows
+//    the row's sorted key list in 16-slot chunks, two waves per SIMD; each chunk's K and V rows
 //    are gathered straight into LDS by direct-to-LDS loads, read out, and the
 //    next chunk's gathers fly while this chunk is computed). S^T = K Q^T and
 //    dP^T = V dO^T take K and V in the row layout; dS^T stays in the
@@ -61,9 +61,9 @@ __global__ __launch_bounds__(256) void k_delta(Problem p)
 }
 
 // ---------------------------------------------------------------- dQ
-constexpr int kChunk = 32;  // key slots per step
+constexpr int kChunk = 16;  // key slots per step (one 16-slot MFMA block)
 
-// Body of k_dq; ks and vs are the wave's K and V staging regions (32 rows of
+// Body of k_dq; ks and vs are the wave's K and V staging regions (16 rows of
 // 512 bytes each, swizzled as described with swz()).
 __device__ __forceinline__ void dq_row(const Problem &p, lds_char *ks, lds_char *vs)
 {
@@ -115,23 +115,23 @@ __device__ __forceinline__ void dq_row(const Problem &p, lds_char *ks, lds_char 
         const float c = p.scale * 1.4426950408889634f;
         const rsrc_t rkeys = make_rsrc(p.pkeys + row * p.W, (uint32_t)(p.W * 4));
         auto fetch_key = [&](int ch) -> int {
-            const int slot = ch * kChunk + (lane & 31);
+            const int slot = ch * kChunk + (lane & 15);
             const int kk = (int)__builtin_amdgcn_raw_buffer_load_b32(
                 rkeys, slot < n ? (uint32_t)slot * 4 : kOutOfRange, 0, 0);
             return slot < n ? kk : -1;
         };
-        auto offsets = [&](int kk, uint32_t (&off)[16]) {
+        auto offsets = [&](int kk, uint32_t (&off)[8]) {
             const uint32_t mine = kk >= 0 ? (uint32_t)kk * row_bytes : kOutOfRange;
 #pragma unroll
-            for (int s = 0; s < 16; ++s) {
+            for (int s = 0; s < 8; ++s) {
                 const uint32_t e = __builtin_amdgcn_readlane(mine, 2 * s);
                 const uint32_t o = __builtin_amdgcn_readlane(mine, 2 * s + 1);
                 off[s] = ((lane >> 5) ? o : e) + ((uint32_t)dma_chunk(lane, s) << 4);
             }
         };
-        auto gather = [&](rsrc_t r, lds_char *dst, const uint32_t (&off)[16]) {
+        auto gather = [&](rsrc_t r, lds_char *dst, const uint32_t (&off)[8]) {
 #pragma unroll
-            for (int s = 0; s < 16; ++s) dma16(r, dst + s * 1024, off[s]);
+            for (int s = 0; s < 8; ++s) dma16(r, dst + s * 1024, off[s]);
         };
         // Row-layout reads (A operands of S^T = K Q^T and dP^T = V dO^T) and
         // the transposed read of K (A operand of dQ^T = K^T dS^T), as in the
@@ -144,7 +144,7 @@ __device__ __forceinline__ void dq_row(const Problem &p, lds_char *ks, lds_char 
 
         const int nchunks = (n + kChunk - 1) / kChunk;
         int knext = fetch_key(1);
-        uint32_t off[16];
+        uint32_t off[8];
         offsets(fetch_key(0), off);
         gather(rk, ks, off);
         gather(rv, vs, off);
@@ -154,54 +154,46 @@ __device__ __forceinline__ void dq_row(const Problem &p, lds_char *ks, lds_char 
             QSA_WAIT_VM(0);
             offsets(knext, off);
             knext = fetch_key(ch + 2);
-            uint4 kr[2][8], vr[2][8];
-            uint2 kt[2][16];
+            uint4 kr[8], vr[8];
+            uint2 kt[16];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const int o = (kb * 16 + col) * 512 + (((4 * t + quad) ^ kmask) << 4);
-                    kr[kb][t] = lds_read16(ks + o);
-                    vr[kb][t] = lds_read16(vs + o);
-                }
-#pragma unroll
-            for (int db = 0; db < 16; ++db) {
-                const int o = tbase + ((db ^ txor) << 5);
-                kt[0][db] = lds_read_tr(ks + o);
-                kt[1][db] = lds_read_tr(ks + o + 16 * 512);
+            for (int t = 0; t < 8; ++t) {
+                const int o = col * 512 + (((4 * t + quad) ^ kmask) << 4);
+                kr[t] = lds_read16(ks + o);
+                vr[t] = lds_read16(vs + o);
             }
+#pragma unroll
+            for (int db = 0; db < 16; ++db) kt[db] = lds_read_tr(ks + tbase + ((db ^ txor) << 5));
             QSA_WAIT_LDS();
             gather(rk, ks, off);
             gather(rv, vs, off);
 
-            float ds[8];
+            f32x4 sa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                f32x4 sa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    sa = mfma_16x16x32(as_bf16x8(kr[kb][t]), qf[t], sa);
-                    pa = mfma_16x16x32(as_bf16x8(vr[kb][t]), gf[t], pa);
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool valid = hv && (ch * kChunk + kb * 16 + 4 * quad + e < n);
-                    const float pr = valid ? exp2f(sa[e] * c - lse2) : 0.f;
-                    // select, never multiply: a padding slot's dP is not used
-                    ds[kb * 4 + e] = valid ? pr * (pa[e] - dlt) : 0.f;
-                }
+            for (int t = 0; t < 8; ++t) {
+                sa = mfma_16x16x32(as_bf16x8(kr[t]), qf[t], sa);
+                pa = mfma_16x16x32(as_bf16x8(vr[t]), gf[t], pa);
             }
-            uint32_t dsh[4], dsl[4];
+            float ds[4];
 #pragma unroll
-            for (int x = 0; x < 4; ++x) split_bf16x2(ds[2 * x], ds[2 * x + 1], dsh[x], dsl[x]);
-            const bf16x8 dsv_hi = as_bf16x8(make_uint4(dsh[0], dsh[1], dsh[2], dsh[3]));
-            const bf16x8 dsv_lo = as_bf16x8(make_uint4(dsl[0], dsl[1], dsl[2], dsl[3]));
+            for (int e = 0; e < 4; ++e) {
+                const bool valid = hv && (ch * kChunk + 4 * quad + e < n);
+                const float pr = valid ? exp2f(sa[e] * c - lse2) : 0.f;
+                // select, never multiply: a padding slot's dP is not used
+                ds[e] = valid ? pr * (pa[e] - dlt) : 0.f;
+            }
+            // B operand dS^T of the 16x16x16 product: slot j of lane group
+            // quad is key 4*quad + j, the lane's own accumulator values.
+            uint32_t dsh[2], dsl[2];
+            split_bf16x2(ds[0], ds[1], dsh[0], dsl[0]);
+            split_bf16x2(ds[2], ds[3], dsh[1], dsl[1]);
+            const bf16x4 dsv_hi = __builtin_bit_cast(bf16x4, make_uint2(dsh[0], dsh[1]));
+            const bf16x4 dsv_lo = __builtin_bit_cast(bf16x4, make_uint2(dsl[0], dsl[1]));
 #pragma unroll
             for (int db = 0; db < 16; ++db) {
-                const bf16x8 ka =
-                    as_bf16x8(make_uint4(kt[0][db].x, kt[0][db].y, kt[1][db].x, kt[1][db].y));
-                acc[db] = mfma_16x16x32(ka, dsv_hi, acc[db]);
-                acc[db] = mfma_16x16x32(ka, dsv_lo, acc[db]);
+                const bf16x4 ka = __builtin_bit_cast(bf16x4, kt[db]);
+                acc[db] = mfma_16x16x16(ka, dsv_hi, acc[db]);
+                acc[db] = mfma_16x16x16(ka, dsv_lo, acc[db]);
             }
         }
         QSA_WAIT_VM(0);  // no gather may outlive the wave's LDS

@@ -9,19 +9,23 @@
 //  * The 12 query heads that share one K/V row are the dense contraction: the
 //    wave computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (M = 16 key slots,
 //    N = 12 heads padded to 16, K = 256 in eight steps).
-//  * The row's sorted key list is walked in 32-slot chunks. A chunk's K and V
+//  * The row's sorted key list is walked in 16-slot chunks. A chunk's K and V
 //    rows are gathered straight into LDS with direct-to-LDS buffer loads, two
 //    512-byte rows per instruction, so the vector memory path sees whole
 //    contiguous rows instead of one row per lane. Slots past the end of the
 //    list read as zero without a branch. Once a chunk has been read out of
 //    LDS into registers, the next chunk's gathers are issued into the same
 //    regions and fly while the current chunk's products and softmax run.
+//    16-slot chunks keep the wave under 256 registers and 16 KB of LDS, so
+//    two waves share each SIMD and one's gathers hide behind the other's
+//    products (32-slot chunks at one wave per SIMD were 9 % slower).
 //  * K is read back in the MFMA operand layout with 16-byte reads, V with the
 //    transposing ds_read_b64_tr_b16 as the A operand of O^T = V^T P^T; a
 //    per-row swizzle of the 16-byte chunks keeps both reads free of bank
 //    conflicts.
 //  * The accumulator layout of S^T puts four key slots of one head in a lane,
-//    which is exactly the B operand layout of O^T = V^T P^T, so P never leaves
+//    which is exactly the B operand layout of O^T = V^T P^T in the
+//    v_mfma_f32_16x16x16_bf16 form (K = 16 key slots), so P never leaves
 //    registers. Each lane owns one head: the running maximum and sum are per
 //    lane and the rescale of O is a per-lane scalar.
 //  * The first chunk fixes each head's reference maximum. P = exp2(s - ref)
@@ -43,7 +47,7 @@ namespace qsa {
 
 namespace {
 
-constexpr int kChunk = 32;            // key slots per step (two 16-slot MFMA blocks)
+constexpr int kChunk = 16;            // key slots per step (one 16-slot MFMA block)
 constexpr float kSlack = 64.f;        // log2 of the largest unnormalised P
 
 // Body of k_forward; ks and vs are the wave's K and V staging regions.
@@ -108,43 +112,43 @@ __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_
         QSA_WAIT_VM(0);
     }
 
-    // Gather instruction s stages key slot s (lanes 0..31) and slot s + 16
-    // (lanes 32..63), each lane one 16-byte chunk of the row, so every
-    // instruction reads two whole rows. A lane's 16 keys per chunk (slots
-    // 16h .. 16h+15 for its half h) are fetched one chunk ahead with four
-    // 16-byte loads; slots at or past n read as zero.
+    // Gather instruction s (0..7) stages key slot s (lanes 0..31) and slot
+    // s + 8 (lanes 32..63), each lane one 16-byte chunk of the row. A lane's 8
+    // keys per chunk (slots 8h .. 8h+7 for its half h) are fetched one chunk
+    // ahead with two 16-byte loads; slots at or past n read as zero.
     const int half = lane >> 5;
     const rsrc_t rkeys = make_rsrc(p.pkeys + row * p.W, (uint32_t)(p.W * 4));
-    auto fetch_keys = [&](int ch, uint4 (&kk)[4]) {
-        const int base = ch * kChunk + 16 * half;
+    auto fetch_keys = [&](int ch, uint4 (&kk)[2]) {
+        const int base = ch * kChunk + 8 * half;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 2; ++q)
             kk[q] = buf_load16(rkeys, base + 4 * q < n ? (uint32_t)(base + 4 * q) * 4 : kOutOfRange);
     };
-    // Row slot j sits at rowbase(j) = (j & 15) * 1024 + (j >> 4) * 512 with
-    // its chunks swizzled by swz_mask(j & 15); lane l of instruction s holds
-    // chunk (l & 31) ^ swz_mask(s) of slot s + 16h.
+    // Row slot j sits at rowbase(j) = (j & 7) * 1024 + (j >> 3) * 512 with its
+    // chunks swizzled by swz_mask(j); lane l of instruction s holds chunk
+    // (l & 31) ^ swz_mask(s + 8h) of slot s + 8h.
     const uint32_t lane16 = (uint32_t)((lane & 31) << 4);
-    auto offsets = [&](const uint4 (&kk)[4], int ch, uint32_t (&off)[16]) {
+    auto offsets = [&](const uint4 (&kk)[2], int ch, uint32_t (&off)[8]) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < 2; ++q) {
             const uint32_t k4[4] = {kk[q].x, kk[q].y, kk[q].z, kk[q].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int s2 = 4 * q + e;
+                const uint32_t m = (uint32_t)swz_mask(s2 + 8 * half) << 4;
                 // key < 2^19 and row_bytes < 2^21: the 24-bit multiply-add is exact
-                off[s2] = __umul24(k4[e], row_bytes) + (lane16 ^ (uint32_t)(swz_mask(s2) << 4));
+                off[s2] = __umul24(k4[e], row_bytes) + (lane16 ^ m);
             }
         }
         if ((ch + 1) * kChunk > n) {  // the last chunk: slots past n read zeros
-            const int rem = n - ch * kChunk - 16 * half;
+            const int rem = n - ch * kChunk - 8 * half;
 #pragma unroll
-            for (int s2 = 0; s2 < 16; ++s2) off[s2] = s2 < rem ? off[s2] : kOutOfRange;
+            for (int s2 = 0; s2 < 8; ++s2) off[s2] = s2 < rem ? off[s2] : kOutOfRange;
         }
     };
-    auto gather = [&](rsrc_t r, lds_char *dst, const uint32_t (&off)[16]) {
+    auto gather = [&](rsrc_t r, lds_char *dst, const uint32_t (&off)[8]) {
 #pragma unroll
-        for (int s2 = 0; s2 < 16; ++s2) dma16(r, dst + s2 * 1024, off[s2]);
+        for (int s2 = 0; s2 < 8; ++s2) dma16(r, dst + s2 * 1024, off[s2]);
     };
 
     const float c = p.scale * 1.4426950408889634f;  // scores in log2 units
@@ -160,16 +164,18 @@ __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_
     // chunk's slot is 2 (db ^ (m >> 1)) + (((i >> 1) & 1) ^ (m & 1)) for the
     // row's mask m. Slot kb*16 + j lies 512 kb above slot j.
     const int kmask = swz_mask(col);
+    const int kbase_lane = (col & 7) * 1024 + (col >> 3) * 512;
     const int vkey = 4 * quad + (col >> 2);
     const int vm = swz_mask(vkey);
-    const int vbase_lane = vkey * 1024 + ((((col >> 1) & 1) ^ (vm & 1)) << 4) + (col & 1) * 8;
+    const int vbase_lane = (vkey & 7) * 1024 + (vkey >> 3) * 512 +
+                           ((((col >> 1) & 1) ^ (vm & 1)) << 4) + (col & 1) * 8;
     const int vxor = vm >> 1;
 
     const int nchunks = (n + kChunk - 1) / kChunk;
     bool restart = false;
     for (;;) {
-        uint4 kn[4];
-        uint32_t off[16];
+        uint4 kn[2];
+        uint32_t off[8];
         fetch_keys(0, kn);
         offsets(kn, 0, off);
         fetch_keys(1, kn);
@@ -177,66 +183,43 @@ __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_
         gather(rv, vs, off);
 
         for (int ch = 0; ch < nchunks; ++ch) {
-            // The compiler orders every LDS read after all direct-to-LDS loads
-            // issued before it, so a chunk's K and V are read out whole, and
-            // the next chunk is gathered only then, overlapping this chunk's
-            // products and softmax.
             QSA_WAIT_VM(0);
             offsets(kn, ch + 1, off);  // next chunk
             fetch_keys(ch + 2, kn);
-            uint4 kr[2][8];
+            uint4 kr[8];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int t = 0; t < 8; ++t)
+                kr[t] = lds_read16(ks + kbase_lane + (((4 * t + quad) ^ kmask) << 4));
+            uint2 va[16];
 #pragma unroll
-                for (int t = 0; t < 8; ++t)
-                    kr[kb][t] = lds_read16(ks + col * 1024 + 512 * kb + (((4 * t + quad) ^ kmask) << 4));
-            uint2 va[2][16];
-#pragma unroll
-            for (int db = 0; db < 16; ++db) {
-                const int o = vbase_lane + ((db ^ vxor) << 5);
-                va[0][db] = lds_read_tr(vs + o);
-                va[1][db] = lds_read_tr(vs + o + 512);
-            }
+            for (int db = 0; db < 16; ++db) va[db] = lds_read_tr(vs + vbase_lane + ((db ^ vxor) << 5));
             QSA_WAIT_LDS();  // both regions are free
             gather(rk, ks, off);
             gather(rv, vs, off);
 
-            f32x4 st[2];
+            f32x4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int t = 0; t < 8; ++t) a = mfma_16x16x32(as_bf16x8(kr[kb][t]), qf[t], a);
-                st[kb] = a;
-            }
+            for (int t = 0; t < 8; ++t) st = mfma_16x16x32(as_bf16x8(kr[t]), qf[t], st);
 
-            // Softmax numerators; lane holds key slots kb*16 + 4*quad + e of head col.
-            float t[2][4];
+            // Softmax numerators; lane holds key slots 4*quad + e of head col.
+            float t4[4];
             float mx = -INFINITY;
             if ((ch + 1) * kChunk <= n) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        t[kb][e] = st[kb][e] * c;
-                        mx = fmaxf(mx, t[kb][e]);
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    t4[e] = st[e] * c;
+                    mx = fmaxf(mx, t4[e]);
+                }
             } else {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const bool valid = ch * kChunk + kb * 16 + 4 * quad + e < n;
-                        t[kb][e] = valid ? st[kb][e] * c : -INFINITY;
-                        mx = fmaxf(mx, t[kb][e]);
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    const bool valid = ch * kChunk + 4 * quad + e < n;
+                    t4[e] = valid ? st[e] * c : -INFINITY;
+                    mx = fmaxf(mx, t4[e]);
+                }
             }
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            // The first chunk fixes each head's reference maximum (O and the
-            // sum are still zero). A later chunk more than 2^kSlack above it
-            // raises the reference and has the whole row recomputed, so O is
-            // never rescaled inside the loop.
             if (ch == 0) {
                 m_run = fmaxf(m_run, mx);
             } else if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0) {
@@ -244,28 +227,24 @@ __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_
                 restart = true;
                 break;
             }
-            float pr[8];
+            float pr[4];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float pv = __builtin_amdgcn_exp2f(t[kb][e] - m_run);
-                    pr[kb * 4 + e] = pv;
-                    l_part += pv;
-                }
-            // B operand P^T: slot j of lane group quad is key 4*quad+j (j<4) or
-            // 16+4*quad+j-4 (j>=4): the lane's own accumulator values.
-            uint32_t hi[4], lo[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) split_bf16x2(pr[2 * x], pr[2 * x + 1], hi[x], lo[x]);
-            const bf16x8 pb_hi = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
-            const bf16x8 pb_lo = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+            for (int e = 0; e < 4; ++e) {
+                pr[e] = __builtin_amdgcn_exp2f(t4[e] - m_run);
+                l_part += pr[e];
+            }
+            // B operand P^T of the 16x16x16 product: slot j of lane group quad
+            // is key 4*quad + j, the lane's own accumulator values.
+            uint32_t hi[2], lo[2];
+            split_bf16x2(pr[0], pr[1], hi[0], lo[0]);
+            split_bf16x2(pr[2], pr[3], hi[1], lo[1]);
+            const bf16x4 pb_hi = __builtin_bit_cast(bf16x4, make_uint2(hi[0], hi[1]));
+            const bf16x4 pb_lo = __builtin_bit_cast(bf16x4, make_uint2(lo[0], lo[1]));
 #pragma unroll
             for (int db = 0; db < 16; ++db) {
-                const bf16x8 v8 =
-                    as_bf16x8(make_uint4(va[0][db].x, va[0][db].y, va[1][db].x, va[1][db].y));
-                acc[db] = mfma_16x16x32(v8, pb_hi, acc[db]);
-                acc[db] = mfma_16x16x32(v8, pb_lo, acc[db]);
+                const bf16x4 v4 = __builtin_bit_cast(bf16x4, va[db]);
+                acc[db] = mfma_16x16x16(v4, pb_hi, acc[db]);
+                acc[db] = mfma_16x16x16(v4, pb_lo, acc[db]);
             }
         }
         QSA_WAIT_VM(0);  // no gather may outlive this pass or the wave's LDS
