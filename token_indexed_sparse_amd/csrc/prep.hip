@@ -21,6 +21,19 @@ namespace qsa {
 namespace {
 
 constexpr int kPrepThreads = 256;
+constexpr int kRouteUnroll = 8;  // route loads in flight per thread
+constexpr int kFullWords = 256;
+
+// LDS bytes of k_prep_rows without and with the staged key list; the list is
+// staged when the whole fits in 64 KB.
+__host__ __device__ inline size_t prep_lds_base(const Problem &p)
+{
+    return (size_t)(p.stride / 32) * 4 + (kPrepThreads + 1) * 4;
+}
+__host__ __device__ inline bool prep_stage_keys(const Problem &p)
+{
+    return prep_lds_base(p) + (size_t)p.W * 4 <= 65536;
+}  // full-tile bits per tile row kept in LDS (8192 key tiles)
 
 __global__ void k_fill_i32(int32_t *__restrict__ p, int64_t n, int32_t value)
 {
@@ -38,15 +51,24 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_rows(Problem p)
     const int tid = threadIdx.x;
     const int64_t nwords = p.stride >> 5;
     uint32_t *bm = lds;
-    uint32_t *scan = lds + nwords;  // kPrepThreads + 1 entries
+    uint32_t *scan = lds + nwords;  // one total per wave
 
     for (int64_t w = tid; w < nwords; w += kPrepThreads) bm[w] = 0u;
     __syncthreads();
 
+    // The loads of a round are all issued before its LDS atomics, so a row
+    // waits for one or two memory latencies, not one per route.
     const RouteT *routes = static_cast<const RouteT *>(p.routes) + row * p.W;
-    for (int64_t s = tid; s < p.W; s += kPrepThreads) {
-        const int64_t r = (int64_t)routes[s];  // range test on the full width
-        if (r >= 0 && r < p.Skv) atomicOr(&bm[r >> 5], 1u << (r & 31));
+    for (int64_t s0 = 0; s0 < p.W; s0 += (int64_t)kPrepThreads * kRouteUnroll) {
+        int64_t r[kRouteUnroll];
+#pragma unroll
+        for (int u = 0; u < kRouteUnroll; ++u) {
+            const int64_t s = s0 + u * kPrepThreads + tid;
+            r[u] = s < p.W ? (int64_t)routes[s] : -1;  // range test on the full width
+        }
+#pragma unroll
+        for (int u = 0; u < kRouteUnroll; ++u)
+            if (r[u] >= 0 && r[u] < p.Skv) atomicOr(&bm[r[u] >> 5], 1u << (r[u] & 31));
     }
     __syncthreads();
 
@@ -76,26 +98,51 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_rows(Problem p)
     const int64_t w0 = tid * per, w1 = (w0 + per < nwords) ? w0 + per : nwords;
     int cnt = 0;
     for (int64_t w = w0; w < w1; ++w) cnt += __popc(bm[w]);
-    scan[tid] = cnt;
+    // Exclusive prefix of the counts: inclusive scan inside each wave, then
+    // the wave totals.
+    const int lane = tid & 63, wv = tid >> 6;
+    int inc = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(inc, off);
+        if (lane >= off) inc += t;
+    }
+    if (lane == 63) scan[wv] = inc;
     __syncthreads();
-    for (int off = 1; off < kPrepThreads; off <<= 1) {
-        const int add = tid >= off ? scan[tid - off] : 0;
-        __syncthreads();
-        scan[tid] += add;
-        __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int v = 0; v < kPrepThreads / 64; ++v) {
+        const int tv = scan[v];
+        before += v < wv ? tv : 0;
+        total += tv;
     }
-    const int total = scan[kPrepThreads - 1];
-    int pos = scan[tid] - cnt;
+    int pos = before + inc - cnt;
     int32_t *keys = p.row_keys + row * p.W;
-    for (int64_t w = w0; w < w1; ++w) {
-        uint32_t bits = bm[w];
-        while (bits) {
-            const int bit = __ffs(bits) - 1;
-            bits &= bits - 1;
-            keys[pos++] = (int32_t)(w * 32 + bit);
+    if (prep_stage_keys(p)) {
+        // Through LDS, so that the list leaves in coalesced stores (each
+        // thread's run of keys would otherwise be one scattered store per key).
+        int32_t *sk = reinterpret_cast<int32_t *>(scan + kPrepThreads + 1);
+        for (int64_t w = w0; w < w1; ++w) {
+            uint32_t bits = bm[w];
+            while (bits) {
+                const int bit = __ffs(bits) - 1;
+                bits &= bits - 1;
+                sk[pos++] = (int32_t)(w * 32 + bit);
+            }
         }
+        __syncthreads();
+        for (int64_t s = tid; s < p.W; s += kPrepThreads) keys[s] = s < total ? sk[s] : -1;
+    } else {
+        for (int64_t w = w0; w < w1; ++w) {
+            uint32_t bits = bm[w];
+            while (bits) {
+                const int bit = __ffs(bits) - 1;
+                bits &= bits - 1;
+                keys[pos++] = (int32_t)(w * 32 + bit);
+            }
+        }
+        for (int64_t s = total + tid; s < p.W; s += kPrepThreads) keys[s] = -1;
     }
-    for (int64_t s = total + tid; s < p.W; s += kPrepThreads) keys[s] = -1;
     if (tid == 0) {
         p.row_cnt[row] = total;
         if (p.has_routes) p.has_routes[row] = total > 0 ? 1 : 0;
@@ -180,6 +227,7 @@ __global__ __launch_bounds__(64) void k_lists_rev(Problem p)
 // stays on the gathered path.
 __global__ __launch_bounds__(256) void k_partial_keys(Problem p)
 {
+    __shared__ uint32_t fullbits[4][kFullWords];
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= p.B * p.Sq) return;
     const int lane = threadIdx.x & 63;
@@ -189,20 +237,40 @@ __global__ __launch_bounds__(256) void k_partial_keys(Problem p)
     const int32_t *keys = p.row_keys + row * p.W;
     int32_t *out = p.pkeys + row * p.W;
     const int n = p.row_cnt[row];
+    // Full-tile bits of the row's tile row in LDS (one bit per key tile), so
+    // that a key's test needs no dependent load. Rows on tile rows longer than
+    // the bit set test the kinds in memory.
+    uint32_t *full = fullbits[threadIdx.x >> 6];
+    const bool in_lds = p.nKT <= 32 * kFullWords;
+    if (in_lds) {
+        for (int64_t t0 = 0; t0 < p.nKT; t0 += 64) {
+            const int64_t t = t0 + lane;
+            const uint64_t f = __ballot(t < p.nKT && kd[t] == 2);
+            if (lane == 0) {
+                full[t0 >> 5] = (uint32_t)f;
+                if ((t0 >> 5) + 1 < kFullWords) full[(t0 >> 5) + 1] = (uint32_t)(f >> 32);
+            }
+        }
+    }
+    wave_lds_sync();
+    auto is_full = [&](int32_t key) {
+        const int32_t t = key >> 7;
+        return in_lds ? ((full[t >> 5] >> (t & 31)) & 1u) != 0u : kd[t] == 2;
+    };
     int cnt = 0;
-    // Four 64-key groups per round, so that their loads are in flight together.
-    for (int s0 = 0; s0 < n; s0 += 256) {
-        int32_t key[4];
-        bool keep[4];
+    // Eight 64-key groups per round, so that their loads are in flight together.
+    for (int s0 = 0; s0 < n; s0 += 512) {
+        int32_t key[8];
+        bool keep[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
             const int s = s0 + 64 * u + lane;
             key[u] = s < n ? keys[s] : 0;
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) keep[u] = s0 + 64 * u + lane < n && kd[key[u] >> 7] != 2;
+        for (int u = 0; u < 8; ++u) keep[u] = s0 + 64 * u + lane < n && !is_full(key[u]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
             const uint64_t ball = __ballot(keep[u]);
             if (keep[u]) out[cnt + __popcll(ball & below)] = key[u];
             cnt += __popcll(ball);
@@ -226,7 +294,7 @@ hipError_t launch_preprocess(const Problem &p, hipStream_t s)
     int blocks = (int)((ntiles + 255) / 256);
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL(k_fill_i32, dim3(blocks), dim3(256), 0, s, p.tile_cnt, ntiles, 0);
-    const size_t lds = (size_t)(p.stride / 32) * 4 + (kPrepThreads + 1) * 4;
+    const size_t lds = prep_lds_base(p) + (prep_stage_keys(p) ? (size_t)p.W * 4 : 0);
     if (p.route_is_i64)
         hipLaunchKernelGGL(k_prep_rows<int64_t>, dim3((unsigned)(p.B * p.Sq)), dim3(kPrepThreads),
                            lds, s, p);
