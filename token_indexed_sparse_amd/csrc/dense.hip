@@ -8,21 +8,24 @@
 // ("fa4_qsa" page, `_block_kinds`: count == 128 * 128); such pairs are
 // exactly the keys the partial key lists leave out.
 //
-// Design (one work group of eight waves, two per SIMD, per query tile, KV
-// head and block of 128 (row, head) vectors):
+// Design (one work group of four waves per query tile, KV head and block of
+// 64 (row, head) vectors; two work groups share a CU, so one's set-up and
+// final stores overlap the other's products):
 //  * Inside a full tile every (row, head) vector of the tile sees the same
 //    keys, so the MFMA blocks take 16 consecutive vectors of the tile (rows
 //    and heads mixed) instead of the 12 heads of one row: no padding lanes.
-//    A wave owns one such block (16 vectors), a work group 128, and the 12
+//    A wave owns one such block (16 vectors), a work group 64, and the 24
 //    work groups of a query tile are consecutive blocks, which the XCD-aware
 //    mapping keeps on one XCD so the key tiles they share stay in its L2.
 //  * Keys come in chunks of 32 from the tile row's full key tiles. A chunk's
 //    K and V rows are contiguous, staged once per work group into LDS by
-//    direct-to-LDS loads (each wave issues an eighth) in the swizzled layout
-//    of the gathered forward, into a ring of four chunk buffers: three chunks
-//    fly while one is computed. A wave waits (counted) for its own loads of
-//    the chunk, then the work-group barrier makes every wave's loads visible
-//    and frees the buffer of the previous chunk for the next load.
+//    direct-to-LDS loads (each wave issues a quarter) in the swizzled layout
+//    of the gathered forward, into two chunk buffers: the next chunk flies
+//    while one is computed. A wave waits (counted) for its own loads of the
+//    chunk, then the work-group barrier makes every wave's loads visible and
+//    frees the buffer of the previous chunk for the next load. With one work
+//    group per CU (eight waves, four buffers) the set-up and the final
+//    stores of every work group were exposed: 8-11 % slower.
 //  * S^T = K Q^T and O^T = V^T P^T exactly as in the gathered forward (K in
 //    the row layout, V through the transposing read, P^T straight from the
 //    accumulators, P as bf16 high + low), per vector block.
@@ -36,7 +39,7 @@ namespace qsa {
 
 namespace {
 
-constexpr int kDenseWaves = 8;  // two waves per SIMD
+constexpr int kDenseWaves = 4;  // one wave per SIMD; two work groups share a CU
 constexpr int kVecBlocks = 1;                                  // 16-vector blocks per wave
 constexpr int kGroupVecs = kDenseWaves * 16 * kVecBlocks;      // vectors per work group
 constexpr int kTileVecs = kTile * kGroup;                      // vectors of a query tile
@@ -44,7 +47,7 @@ constexpr int kVBlocks = kTileVecs / kGroupVecs;               // work groups pe
 constexpr int kKeys = 32;                                      // keys per staged chunk
 constexpr int kHalf = kKeys * 512;                             // K (or V) bytes of a chunk
 constexpr int kBuf = 2 * kHalf;                                // K then V
-constexpr int kRing = 4;        // chunk buffers: three chunks in flight ahead
+constexpr int kRing = 2;        // chunk buffers: one chunk in flight ahead
 constexpr int kStage = 16 / kDenseWaves;  // staging instructions per wave and tensor
 constexpr int kChunkOps = 2 * kStage;     // direct-to-LDS loads a wave issues per chunk
 constexpr float kSlack = 64.f;  // log2 of the largest unnormalised P
@@ -55,9 +58,9 @@ static_assert(kDenseWaves * kStage == 16, "the waves share the 16 row pairs of a
 // chunks issued after it (up to kRing - 2 of them) are in flight.
 __device__ __forceinline__ void wait_chunk(int ch, int nch)
 {
-    static_assert(kRing == 4, "the counted waits assume three chunks in flight");
-    if (ch + 2 < nch) QSA_WAIT_VM(2 * kChunkOps);
-    else if (ch + 1 < nch) QSA_WAIT_VM(kChunkOps);
+    static_assert(kRing == 2 || kRing == 4, "counted waits for one or three chunks in flight");
+    if (kRing == 4 && ch + 2 < nch) QSA_WAIT_VM(2 * kChunkOps);
+    else if (kRing == 4 && ch + 1 < nch) QSA_WAIT_VM(kChunkOps);
     else QSA_WAIT_VM(0);
 }
 
@@ -175,7 +178,7 @@ __device__ __forceinline__ void forward_dense_item(const Problem &p, lds_char *b
     const int vxor = vm >> 1;
     const float c = p.scale * 1.4426950408889634f;  // scores in log2 units
 
-    auto compute = [&](uint32_t cb, bool first, auto rescale_tag) {
+    auto compute = [&](uint32_t cb, bool first, lds_flag *flag, auto rescale_tag) {
         constexpr bool kRescale = decltype(rescale_tag)::value;
         const lds_char *ks = (const lds_char *)(uintptr_t)cb;
         const lds_char *vs = ks + kHalf;
@@ -227,7 +230,7 @@ __device__ __forceinline__ void forward_dense_item(const Problem &p, lds_char *b
                     // (an empty hand-over has -inf). This pass's sums are
                     // discarded, so P may keep using the raised reference.
                     m_ref[x] = fmaxf(m_ref[x], mx);
-                    if (lane == 0) *redo_flag = 1;
+                    if (lane == 0) *flag = 1;
                 }
             }
             float pr[8];
@@ -278,26 +281,29 @@ __device__ __forceinline__ void forward_dense_item(const Problem &p, lds_char *b
         }
     };
     // One pass over the full tiles. Without rescaling, a wave that needs it
-    // raises the flag; every wave reads the flag between the same two
-    // barriers, so all leave together and the pass reports it.
+    // raises the flag of its chunk's parity; every wave reads that flag after
+    // the next barrier, before any wave can write it again, so all leave
+    // together and the pass reports it.
     auto pass = [&](auto rescale_tag) {
         constexpr bool kRescale = decltype(rescale_tag)::value;
         for (int c0 = 0; c0 < kRing - 1 && c0 < nch; ++c0) issue(c0);
         bool redo = false;
         for (int ch = 0; ch < nch; ++ch) {
             wait_chunk(ch, nch);
-            __builtin_amdgcn_s_barrier();
-            if (!kRescale && opaque_u32(__builtin_amdgcn_readfirstlane(*redo_flag)) != 0u) {
+            asm volatile("s_waitcnt lgkmcnt(0)\n s_barrier" ::: "memory");
+            if (!kRescale && ch > 0 &&
+                opaque_u32(__builtin_amdgcn_readfirstlane(redo_flag[(ch - 1) & 1])) != 0u) {
                 redo = true;
                 break;
             }
             const uint32_t cb = opaque_u32(base + (uint32_t)((ch % kRing) * kBuf));
             if (ch + kRing - 1 < nch) issue(ch + kRing - 1);
-            compute(cb, !kRescale && ch == 0, rescale_tag);
+            compute(cb, !kRescale && ch == 0, redo_flag + (ch & 1), rescale_tag);
         }
         QSA_WAIT_VM(0);
-        __builtin_amdgcn_s_barrier();
-        if (!kRescale && !redo) redo = opaque_u32(__builtin_amdgcn_readfirstlane(*redo_flag)) != 0u;
+        asm volatile("s_waitcnt lgkmcnt(0)\n s_barrier" ::: "memory");
+        if (!kRescale && !redo)
+            redo = opaque_u32(__builtin_amdgcn_readfirstlane(redo_flag[0] | redo_flag[1])) != 0u;
         return redo;
     };
     init();
@@ -333,10 +339,10 @@ __device__ __forceinline__ void forward_dense_item(const Problem &p, lds_char *b
 __global__ __launch_bounds__(64 * kDenseWaves) void k_forward_dense(Problem p)
 {
     __shared__ __attribute__((aligned(16))) char buf[kRing * kBuf];
-    __shared__ uint32_t redo_flag;
-    if (threadIdx.x == 0) redo_flag = 0;
+    __shared__ uint32_t redo_flag[2];
+    if (threadIdx.x < 2) redo_flag[threadIdx.x] = 0;
     __syncthreads();
-    forward_dense_item(p, (lds_char *)buf, (lds_flag *)&redo_flag);
+    forward_dense_item(p, (lds_char *)buf, (lds_flag *)redo_flag);
 }
 
 // dQ over full tiles: same tiling and staging as the forward. P = 2^(S c -
@@ -521,8 +527,9 @@ __global__ __launch_bounds__(64 * kDenseWaves) void k_dq_dense(Problem p)
 // registers, dK and dV accumulators for the whole work group) and the work
 // group streams the (row, head) vectors of the key tile's full query tiles in
 // chunks of 32: Q, dO, lse and delta of a chunk are staged once, Q and dO in
-// the forward's K-staging layout (slot j = vector j of the chunk), through the
-// same four-buffer ring. Per chunk a wave computes S = Q K^T and dP = dO V^T
+// the forward's K-staging layout (slot j = vector j of the chunk), through two
+// buffers; the kernel is held to 256 registers so that two work groups share
+// a CU (15 % faster than one with four buffers). Per chunk a wave computes S = Q K^T and dP = dO V^T
 // for its keys (two 16-vector blocks; lane (key col, quad) holds vectors
 // 16x + 4 quad + i), P and dS, then dV += P^T dO and dK += dS^T Q with the
 // two blocks' vectors as the 32-long contraction, exactly as the gathered
@@ -538,11 +545,14 @@ constexpr int kKvChunkOps = 2 * kKvStage;         // direct-to-LDS loads a wave 
 constexpr int kKvParts = kTile / (16 * kKvWaves);  // work groups per key tile
 static_assert(kKvParts * 16 * kKvWaves == kTile, "waves of 16 keys must tile the key tile");
 
+constexpr int kKvRing = 2;  // dK/dV chunk buffers: one chunk in flight ahead
+
 template <int OPS>
 __device__ __forceinline__ void wait_chunk_ops(int ch, int nch)
 {
-    if (ch + 2 < nch) QSA_WAIT_VM(2 * OPS);
-    else if (ch + 1 < nch) QSA_WAIT_VM(OPS);
+    static_assert(kKvRing == 2 || kKvRing == 4, "counted waits for one or three chunks in flight");
+    if (kKvRing == 4 && ch + 2 < nch) QSA_WAIT_VM(2 * OPS);
+    else if (kKvRing == 4 && ch + 1 < nch) QSA_WAIT_VM(OPS);
     else QSA_WAIT_VM(0);
 }
 
@@ -605,7 +615,7 @@ __device__ __forceinline__ void dkdv_dense_item(const Problem &p, lds_char *buf)
         const int64_t tb = ((b * p.Sq + r * kTile) * p.Hq + g * kGroup) * (int64_t)kD;
         const i32x4 rq = rsrc_words(p.q + tb, tile_bytes);
         const i32x4 rg = rsrc_words(p.dout + tb, tile_bytes);
-        const uint32_t dst = base + (uint32_t)((c % kRing) * kKvBuf);
+        const uint32_t dst = base + (uint32_t)((c % kKvRing) * kKvBuf);
 #pragma unroll
         for (int y = 0; y < kKvStage; ++y) {
             const int s = kKvStage * wave + y;
@@ -615,8 +625,14 @@ __device__ __forceinline__ void dkdv_dense_item(const Problem &p, lds_char *buf)
         }
         if (wave == 0) {
             const int64_t sb = (b * p.Hq + g * kGroup) * p.Sq + r * kTile;
-            const i32x4 rl = rsrc_words(p.lse_in + sb, stat_bytes);
-            const i32x4 rd = rsrc_words(p.delta + sb, stat_bytes);
+            i32x4 rl = rsrc_words(p.lse_in + sb, stat_bytes);
+            i32x4 rd = rsrc_words(p.delta + sb, stat_bytes);
+            // Keep the descriptors in scalar registers for the loads below.
+#pragma unroll
+            for (int w4 = 0; w4 < 4; ++w4) {
+                rl[w4] = __builtin_amdgcn_readfirstlane(rl[w4]);
+                rd[w4] = __builtin_amdgcn_readfirstlane(rd[w4]);
+            }
             const int v = 32 * cc + (lane & 31);
             const uint32_t so = (uint32_t)(((v % kGroup) * p.Sq + v / kGroup) * 4);
             if (lane < 32) {
@@ -644,18 +660,22 @@ __device__ __forceinline__ void dkdv_dense_item(const Problem &p, lds_char *buf)
         float pn[2][4], dn[2][4];
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-            uint4 qa[8], ga[8];
-#pragma unroll
-            for (int t8 = 0; t8 < 8; ++t8) {
-                const int o = col * 1024 + 512 * x + (((4 * t8 + quad) ^ amask) << 4);
-                qa[t8] = lds_read16(qs + o);
-                ga[t8] = lds_read16(gs + o);
-            }
             f32x4 sa = {0.f, 0.f, 0.f, 0.f}, pd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int t8 = 0; t8 < 8; ++t8) {
-                sa = mfma_16x16x32(as_bf16x8(qa[t8]), kf[t8], sa);
-                pd = mfma_16x16x32(as_bf16x8(ga[t8]), vf[t8], pd);
+            for (int hh = 0; hh < 2; ++hh) {  // four column steps at a time
+                uint4 qa[4], ga[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int t8 = 4 * hh + u;
+                    const int o = col * 1024 + 512 * x + (((4 * t8 + quad) ^ amask) << 4);
+                    qa[u] = lds_read16(qs + o);
+                    ga[u] = lds_read16(gs + o);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    sa = mfma_16x16x32(as_bf16x8(qa[u]), kf[4 * hh + u], sa);
+                    pd = mfma_16x16x32(as_bf16x8(ga[u]), vf[4 * hh + u], pd);
+                }
             }
             const f32x4 ls = *reinterpret_cast<const lds_f32x4 *>(qs + kKvStats + (16 * x + 4 * quad) * 4);
             const f32x4 dl = *reinterpret_cast<const lds_f32x4 *>(qs + kKvStats + 128 + (16 * x + 4 * quad) * 4);
@@ -680,19 +700,19 @@ __device__ __forceinline__ void dkdv_dense_item(const Problem &p, lds_char *buf)
         const bf16x8 A_d = as_bf16x8(make_uint4(dh[0], dh[1], dh[2], dh[3]));
         const bf16x8 A_dl = as_bf16x8(make_uint4(dlo[0], dlo[1], dlo[2], dlo[3]));
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            uint2 tq[2][8], tg[2][8];
+        for (int h = 0; h < 4; ++h) {
+            uint2 tq[2][4], tg[2][4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int o = tlane + (((8 * h + j) ^ txor) << 5);
+            for (int j = 0; j < 4; ++j) {
+                const int o = tlane + (((4 * h + j) ^ txor) << 5);
                 tq[0][j] = lds_read_tr(qs + o);
                 tq[1][j] = lds_read_tr(qs + o + 512);
                 tg[0][j] = lds_read_tr(gs + o);
                 tg[1][j] = lds_read_tr(gs + o + 512);
             }
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int db = 8 * h + j;
+            for (int j = 0; j < 4; ++j) {
+                const int db = 4 * h + j;
                 const bf16x8 Bg = as_bf16x8(make_uint4(tg[0][j].x, tg[0][j].y, tg[1][j].x, tg[1][j].y));
                 const bf16x8 Bq = as_bf16x8(make_uint4(tq[0][j].x, tq[0][j].y, tq[1][j].x, tq[1][j].y));
                 adv[db] = mfma_16x16x32(A_p, Bg, adv[db]);
@@ -704,13 +724,13 @@ __device__ __forceinline__ void dkdv_dense_item(const Problem &p, lds_char *buf)
     };
 
     const int nch = fcnt * kChunksPerTile;
-    for (int c0 = 0; c0 < kRing - 1 && c0 < nch; ++c0) issue(c0);
+    for (int c0 = 0; c0 < kKvRing - 1 && c0 < nch; ++c0) issue(c0);
     for (int ch = 0; ch < nch; ++ch) {
         if (wave == 0) wait_chunk_ops<kKvChunkOps + 2>(ch, nch);
         else wait_chunk_ops<kKvChunkOps>(ch, nch);
         __builtin_amdgcn_s_barrier();
-        const uint32_t cb = opaque_u32(base + (uint32_t)((ch % kRing) * kKvBuf));
-        if (ch + kRing - 1 < nch) issue(ch + kRing - 1);
+        const uint32_t cb = opaque_u32(base + (uint32_t)((ch % kKvRing) * kKvBuf));
+        if (ch + kKvRing - 1 < nch) issue(ch + kKvRing - 1);
         compute(cb);
     }
     QSA_WAIT_VM(0);
@@ -729,9 +749,9 @@ __device__ __forceinline__ void dkdv_dense_item(const Problem &p, lds_char *buf)
     if (lane == 0) *flag = 1;
 }
 
-__global__ __launch_bounds__(64 * kKvWaves) void k_dkdv_dense(Problem p)
+__global__ __launch_bounds__(64 * kKvWaves, 2) void k_dkdv_dense(Problem p)
 {
-    __shared__ __attribute__((aligned(16))) char buf[kRing * kKvBuf];
+    __shared__ __attribute__((aligned(16))) char buf[kKvRing * kKvBuf];
     dkdv_dense_item(p, (lds_char *)buf);
 }
 
