@@ -66,14 +66,18 @@ def test_small_cases_full_parity(case):
 # Full 128 x 128 tiles (the dense path) next to gathered keys: the hand-over
 # between the two forward passes, rows with no gathered keys, causal-complete
 # and all-full tile rows, edge tiles that are chosen whole but cannot be full,
-# and large scores in a full key tile that make the dense pass raise its
-# reference maximum.
+# moderately large scores in the first full key tile (seed 54), and very large
+# scores in the last one (seed 56), which make the dense pass redo its tiles
+# with a raised reference maximum and the gathered pass restart rows (a CPU
+# test checks that the case does force both).
 TILED = [
     dict(seed=51, B=1, Sq=384, Skv=384, Hq=12, Hkv=1, p_full=0.5, extra=30),
     dict(seed=52, B=2, Sq=300, Skv=520, Hq=24, Hkv=2, p_full=0.6, extra=10, bare_rows=True),
     dict(seed=53, B=1, Sq=384, Skv=384, Hq=12, Hkv=1, causal=True, extra=0),
     dict(seed=54, B=1, Sq=256, Skv=384, Hq=12, Hkv=1, p_full=0.5, extra=20, loud_keys=8.0),
     dict(seed=55, B=1, Sq=256, Skv=256, Hq=12, Hkv=1, all_keys=True, extra=0),
+    dict(seed=56, B=1, Sq=384, Skv=512, Hq=12, Hkv=1, p_full=0.6, extra=20, loud_keys=48.0,
+         loud_last=True),
 ]
 
 

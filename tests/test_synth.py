@@ -125,3 +125,38 @@ def test_tiled_cases_have_full_and_partial_tiles():
         keys = np.unique(row[(row >= 0) & (row < 520)])
         for t in np.unique(keys // 128):
             assert np.isin(np.arange(128 * t, min(128 * t + 128, 520)), keys).all()
+
+
+def test_loud_last_case_forces_both_rescale_paths():
+    """The loud-last tiled case has rows whose later keys score far above the
+    first ones: in the dense pass (full tiles after the first, above the
+    hand-over and the first 32 keys by more than 2^64) and in the gathered
+    pass (partial keys after the first 16, in ascending key order). Scores are
+    taken in log2 units, exactly as the kernels compare them."""
+    Sq, Skv = 384, 512
+    inp = synth.tiled_case(seed=56, B=1, Sq=Sq, Skv=Skv, Hq=12, Hkv=1, p_full=0.6, extra=20,
+                           loud_keys=48.0, loud_last=True)
+    q = synth.bf16_to_f32(inp.q)[0].astype(np.float64)
+    k = synth.bf16_to_f32(inp.k)[0, :, 0].astype(np.float64)
+    memb = np.zeros((Sq, Skv), bool)
+    for i in range(Sq):
+        v = inp.routes[0, i]
+        memb[i, v[(v >= 0) & (v < Skv)]] = True
+    full = memb.reshape(Sq // 128, 128, Skv // 128, 128).sum(axis=(1, 3)) == 128 * 128
+    c = 0.0625 / np.log(2.0)
+    dense_raise = gathered_restart = 0
+    for i in range(Sq):
+        s = q[i] @ k.T * c
+        ft = np.nonzero(full[i // 128])[0]
+        part = memb[i].copy()
+        for t in ft:
+            part[128 * t:128 * t + 128] = False
+        if len(ft) >= 2:
+            m_hand = s[:, part].max(axis=1) if part.any() else np.full(12, -np.inf)
+            ref = np.maximum(m_hand, s[:, 128 * ft[0]:128 * ft[0] + 32].max(axis=1))
+            later = np.concatenate([s[:, 128 * t:128 * t + 128] for t in ft], axis=1).max(axis=1)
+            dense_raise += int((later > ref + 64).any())
+        keys = np.nonzero(part)[0]
+        if len(keys) > 16:
+            gathered_restart += int((s[:, keys].max(axis=1) > s[:, keys[:16]].max(axis=1) + 64).any())
+    assert dense_raise > 0 and gathered_restart > 0, (dense_raise, gathered_restart)

@@ -224,7 +224,7 @@ def random_case(seed: int, B: int, Sq: int, Skv: int, Hq: int, Hkv: int, W: int,
 
 def tiled_case(seed: int, B: int, Sq: int, Skv: int, Hq: int, Hkv: int, p_full: float = 0.5,
                extra: int = 16, D: int = 256, bare_rows: bool = False, loud_keys: float = 0.0,
-               all_keys: bool = False, causal: bool = False) -> Inputs:
+               all_keys: bool = False, causal: bool = False, loud_last: bool = False) -> Inputs:
     """Routes that select whole 128 x 128 tiles, so that full tiles occur.
 
     Each (batch, query tile, key tile) is chosen with probability ``p_full``
@@ -234,7 +234,9 @@ def tiled_case(seed: int, B: int, Sq: int, Skv: int, Hq: int, Hkv: int, p_full: 
     ``bare_rows`` the odd query tiles of batch 0 get no extra keys. Route slots
     are shuffled; spare slots hold -1, a duplicate and an out-of-range value.
     ``loud_keys`` > 0 multiplies the K rows of the first chosen key tile of
-    batch 0 by that factor (large scores there).
+    batch 0 by that factor (large scores there); with ``loud_last`` the last
+    chosen key tile instead, so that the large scores come after smaller ones
+    in every row's key order.
     """
     rng = np.random.default_rng(seed)
     nQT, nKT = -(-Sq // 128), -(-Skv // 128)
@@ -272,7 +274,8 @@ def tiled_case(seed: int, B: int, Sq: int, Skv: int, Hq: int, Hkv: int, p_full: 
     if loud_keys > 0:
         t0 = np.nonzero(chosen[0].any(axis=0))[0]
         if len(t0):
-            kf[0, 128 * t0[0]:128 * t0[0] + 128] *= loud_keys
+            tl = t0[-1] if loud_last else t0[0]
+            kf[0, 128 * tl:128 * tl + 128] *= loud_keys
     k = bf16_bits(kf)
     v = bf16_bits(rng.standard_normal((B, Skv, Hkv, D), dtype=np.float32))
     go = bf16_bits(rng.standard_normal((B, Sq, Hq, D), dtype=np.float32))
