@@ -13,9 +13,11 @@
 //    rows are gathered straight into LDS with direct-to-LDS buffer loads, two
 //    512-byte rows per instruction, so the vector memory path sees whole
 //    contiguous rows instead of one row per lane. Slots past the end of the
-//    list read as zero without a branch. Once a chunk has been read out of
-//    LDS into registers, the next chunk's gathers are issued into the same
-//    regions and fly while the current chunk's products and softmax run.
+//    list read as zero without a branch. Once a chunk's K rows have been read
+//    out of LDS into registers, the next chunk's K gathers are issued into the
+//    same region and fly while the scores and softmax run; the V region is
+//    read and refilled the same way just before the PV products (refilling
+//    both regions together, after both reads, was 4 % slower).
 //    16-slot chunks keep the wave under 256 registers and 16 KB of LDS, so
 //    two waves share each SIMD and one's gathers hide behind the other's
 //    products (32-slot chunks at one wave per SIMD were 9 % slower).
@@ -186,20 +188,17 @@ __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_
             QSA_WAIT_VM(0);
             offsets(kn, ch + 1, off);  // next chunk
             fetch_keys(ch + 2, kn);
-            uint4 kr[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-                kr[t] = lds_read16(ks + kbase_lane + (((4 * t + quad) ^ kmask) << 4));
-            uint2 va[16];
-#pragma unroll
-            for (int db = 0; db < 16; ++db) va[db] = lds_read_tr(vs + vbase_lane + ((db ^ vxor) << 5));
-            QSA_WAIT_LDS();  // both regions are free
-            gather(rk, ks, off);
-            gather(rv, vs, off);
-
             f32x4 st = {0.f, 0.f, 0.f, 0.f};
+            {
+                uint4 kr[8];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) st = mfma_16x16x32(as_bf16x8(kr[t]), qf[t], st);
+                for (int t = 0; t < 8; ++t)
+                    kr[t] = lds_read16(ks + kbase_lane + (((4 * t + quad) ^ kmask) << 4));
+                QSA_WAIT_LDS();  // the K region is free
+                gather(rk, ks, off);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) st = mfma_16x16x32(as_bf16x8(kr[t]), qf[t], st);
+            }
 
             // Softmax numerators; lane holds key slots 4*quad + e of head col.
             float t4[4];
@@ -240,6 +239,15 @@ __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_
             split_bf16x2(pr[2], pr[3], hi[1], lo[1]);
             const bf16x4 pb_hi = __builtin_bit_cast(bf16x4, make_uint2(hi[0], hi[1]));
             const bf16x4 pb_lo = __builtin_bit_cast(bf16x4, make_uint2(lo[0], lo[1]));
+            uint2 va[16];
+            {
+                const lds_char *vsr = (const lds_char *)(uintptr_t)opaque_u32(lds_addr(vs));
+#pragma unroll
+                for (int db = 0; db < 16; ++db)
+                    va[db] = lds_read_tr(vsr + vbase_lane + ((db ^ vxor) << 5));
+            }
+            QSA_WAIT_LDS();  // the V region is free
+            gather(rv, vs, off);
 #pragma unroll
             for (int db = 0; db < 16; ++db) {
                 const bf16x4 v4 = __builtin_bit_cast(bf16x4, va[db]);
