@@ -10,20 +10,23 @@
 //  * k_delta: one wave per (row, head) reduces dO . out_fp32.
 //  * k_dq: query-major like the forward (one wave per row and KV head walks
 //    the row's sorted key list in 16-slot chunks, two waves per SIMD; each chunk's K and V rows
-//    are gathered straight into LDS by direct-to-LDS loads, read out, and the
-//    next chunk's gathers fly while this chunk is computed). S^T = K Q^T and
+//    are gathered straight into LDS by direct-to-LDS loads; the V region is
+//    refilled with the next chunk's rows once its rows are read, the K region
+//    once the transposed K read for dQ is done). S^T = K Q^T and
 //    dP^T = V dO^T take K and V in the row layout; dS^T stays in the
 //    accumulator layout and is the B operand of dQ^T = K^T dS^T, whose K^T
 //    operand is the transposed read of the same staged K rows.
 //  * k_dkdv: key-major. One wave owns 16 consecutive keys of one KV head and
-//    one segment of 32 query tiles, keeps the 16 K and V rows in registers and
+//    one segment of query tiles (8 by default, more when the partial sums
+//    would not fit the workspace budget), keeps the 16 K and V rows in registers and
 //    their dK, dV accumulators for the whole item. It walks the partial
 //    entries of the reverse tile list of its 128-key tile column inside the
 //    segment from the last query tile down (full tiles are summed by the dense
 //    pass), reads a 16-bit slice of the bit-packed membership row of every
 //    query in those tiles, and lists the rows that select one of its keys in
-//    LDS. Each listed row's Q and dO (12 heads x 512 bytes each) are gathered
-//    into a 2-slot LDS ring by direct-to-LDS loads, one row ahead, then read
+//    LDS. Each listed row's Q and dO (12 heads x 512 bytes each), lse and
+//    delta are gathered into a 3-slot LDS ring by direct-to-LDS loads, two
+//    rows ahead, then read
 //    in the row layout (A operands of S = Q K^T and dP = dO V^T, M = heads)
 //    and transposed (B operands of dV += P^T dO and dK += dS^T Q, where two
 //    rows' heads form the 32-long contraction). P and dS enter these products
@@ -154,26 +157,31 @@ __device__ __forceinline__ void dq_row(const Problem &p, lds_char *ks, lds_char 
             QSA_WAIT_VM(0);
             offsets(knext, off);
             knext = fetch_key(ch + 2);
-            uint4 kr[8], vr[8];
-            uint2 kt[16];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int o = col * 512 + (((4 * t + quad) ^ kmask) << 4);
-                kr[t] = lds_read16(ks + o);
-                vr[t] = lds_read16(vs + o);
-            }
-#pragma unroll
-            for (int db = 0; db < 16; ++db) kt[db] = lds_read_tr(ks + tbase + ((db ^ txor) << 5));
-            QSA_WAIT_LDS();
-            gather(rk, ks, off);
-            gather(rv, vs, off);
-
             f32x4 sa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
+            {
+                uint4 kr[8], vr[8];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                sa = mfma_16x16x32(as_bf16x8(kr[t]), qf[t], sa);
-                pa = mfma_16x16x32(as_bf16x8(vr[t]), gf[t], pa);
+                for (int t = 0; t < 8; ++t) {
+                    const int o = col * 512 + (((4 * t + quad) ^ kmask) << 4);
+                    kr[t] = lds_read16(ks + o);
+                    vr[t] = lds_read16(vs + o);
+                }
+                QSA_WAIT_LDS();  // the V region is free
+                gather(rv, vs, off);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    sa = mfma_16x16x32(as_bf16x8(kr[t]), qf[t], sa);
+                    pa = mfma_16x16x32(as_bf16x8(vr[t]), gf[t], pa);
+                }
             }
+            uint2 kt[16];
+            {
+                const lds_char *ksr = (const lds_char *)(uintptr_t)opaque_u32(lds_addr(ks));
+#pragma unroll
+                for (int db = 0; db < 16; ++db) kt[db] = lds_read_tr(ksr + tbase + ((db ^ txor) << 5));
+            }
+            QSA_WAIT_LDS();  // the K region is free
+            gather(rk, ks, off);
             float ds[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
