@@ -51,6 +51,9 @@ SMALL = [
     dict(seed=35, B=1, Sq=200, Skv=200, Hq=12, Hkv=1, W=200, causal=True),
     # more query rows than one dK/dV query-range phase holds: accumulators carry over
     dict(seed=36, B=2, Sq=2300, Skv=200, Hq=24, Hkv=2, W=10),
+    # rows too wide for the row's key list to be staged in LDS (over 64 KB):
+    # the preprocessing writes it straight from its bitmap
+    dict(seed=37, B=1, Sq=40, Skv=3000, Hq=12, Hkv=1, W=17000),
 ]
 
 
