@@ -57,12 +57,15 @@ def check_close(name: str, x: np.ndarray, ref: np.ndarray, tol: float) -> dict:
     ref = np.asarray(ref, np.float64)
     assert x.shape == ref.shape, (name, x.shape, ref.shape)
     same_inf = np.isinf(ref) & (x == ref)
-    err = np.abs(x - ref)
-    ok = same_inf | (err <= tol + tol * np.abs(ref))
     fin = np.isfinite(ref)
+    # differences only where the reference is finite (-inf lse of empty rows
+    # compares by equality above)
+    diff = np.subtract(x, ref, out=np.zeros_like(ref), where=fin)
+    err = np.where(fin, np.abs(diff), np.inf)
+    ok = same_inf | (err <= tol + tol * np.abs(np.where(fin, ref, 0.0)))
     stats = {
         "max_abs": float(np.max(np.where(fin, err, 0.0))) if x.size else 0.0,
-        "norm_rel": float(np.linalg.norm(np.where(fin, x - ref, 0)) /
+        "norm_rel": float(np.linalg.norm(diff) /
                           max(np.linalg.norm(np.where(fin, ref, 0)), 1e-300)) if x.size else 0.0,
     }
     if not ok.all():
