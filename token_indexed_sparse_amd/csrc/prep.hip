@@ -59,16 +59,50 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_rows(Problem p)
     // The loads of a round are all issued before its LDS atomics, so a row
     // waits for one or two memory latencies, not one per route.
     const RouteT *routes = static_cast<const RouteT *>(p.routes) + row * p.W;
-    for (int64_t s0 = 0; s0 < p.W; s0 += (int64_t)kPrepThreads * kRouteUnroll) {
-        int64_t r[kRouteUnroll];
+    if (sizeof(RouteT) == 4 && (p.W & 3) == 0 && ((uintptr_t)p.routes & 15) == 0) {
+        // Four consecutive slots per thread in one 16-byte load; the bits of
+        // slots that fall in the same word are merged before the atomic, so
+        // runs of consecutive keys cost one atomic per word and thread.
+        const int4 *r4 = reinterpret_cast<const int4 *>(routes);
+        const int64_t n4 = p.W >> 2;
+        for (int64_t s0 = 0; s0 < n4; s0 += (int64_t)kPrepThreads * kRouteUnroll) {
+            int4 r[kRouteUnroll];
 #pragma unroll
-        for (int u = 0; u < kRouteUnroll; ++u) {
-            const int64_t s = s0 + u * kPrepThreads + tid;
-            r[u] = s < p.W ? (int64_t)routes[s] : -1;  // range test on the full width
+            for (int u = 0; u < kRouteUnroll; ++u) {
+                const int64_t s = s0 + u * kPrepThreads + tid;
+                r[u] = s < n4 ? r4[s] : make_int4(-1, -1, -1, -1);
+            }
+#pragma unroll
+            for (int u = 0; u < kRouteUnroll; ++u) {
+                const int32_t v[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
+                int32_t word = -1;
+                uint32_t bits = 0u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (v[e] < 0 || v[e] >= p.Skv) continue;
+                    const int32_t wv = v[e] >> 5;
+                    if (wv != word) {
+                        if (bits) atomicOr(&bm[word], bits);
+                        word = wv;
+                        bits = 0u;
+                    }
+                    bits |= 1u << (v[e] & 31);
+                }
+                if (bits) atomicOr(&bm[word], bits);
+            }
         }
+    } else {
+        for (int64_t s0 = 0; s0 < p.W; s0 += (int64_t)kPrepThreads * kRouteUnroll) {
+            int64_t r[kRouteUnroll];
 #pragma unroll
-        for (int u = 0; u < kRouteUnroll; ++u)
-            if (r[u] >= 0 && r[u] < p.Skv) atomicOr(&bm[r[u] >> 5], 1u << (r[u] & 31));
+            for (int u = 0; u < kRouteUnroll; ++u) {
+                const int64_t s = s0 + u * kPrepThreads + tid;
+                r[u] = s < p.W ? (int64_t)routes[s] : -1;  // range test on the full width
+            }
+#pragma unroll
+            for (int u = 0; u < kRouteUnroll; ++u)
+                if (r[u] >= 0 && r[u] < p.Skv) atomicOr(&bm[r[u] >> 5], 1u << (r[u] & 31));
+        }
     }
     __syncthreads();
 
@@ -93,21 +127,21 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_rows(Problem p)
         for (int64_t w = tid; w < nwords; w += kPrepThreads) dst[w] = bm[w];
     }
 
-    // Ascending key list: each thread owns a contiguous run of words.
-    const int64_t per = (nwords + kPrepThreads - 1) / kPrepThreads;
-    const int64_t w0 = tid * per, w1 = (w0 + per < nwords) ? w0 + per : nwords;
-    int cnt = 0;
-    for (int64_t w = w0; w < w1; ++w) cnt += __popc(bm[w]);
-    // Exclusive prefix of the counts: inclusive scan inside each wave, then
-    // the wave totals.
+    // Ascending key list. Wave v owns a contiguous quarter of the words, and
+    // inside it lane l owns words l, l + 64, ..., so a run of dense words (a
+    // window of consecutive keys) spreads over the lanes instead of falling on
+    // one thread. Positions: the words before the wave's quarter (wave totals
+    // through LDS), then, inside the quarter, the earlier 64-word blocks and
+    // the earlier lanes of the word's own block (wave scans).
     const int lane = tid & 63, wv = tid >> 6;
-    int inc = cnt;
+    const int64_t qw = (nwords + kPrepThreads / 64 - 1) / (kPrepThreads / 64);
+    const int64_t wbeg = wv * qw, wend = (wbeg + qw < nwords) ? wbeg + qw : nwords;
+    int mine = 0;
+    for (int64_t w = wbeg + lane; w < wend; w += 64) mine += __popc(bm[w]);
+    int wave_total = mine;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(inc, off);
-        if (lane >= off) inc += t;
-    }
-    if (lane == 63) scan[wv] = inc;
+    for (int off = 32; off > 0; off >>= 1) wave_total += __shfl_xor(wave_total, off);
+    if (lane == 0) scan[wv] = wave_total;
     __syncthreads();
     int before = 0, total = 0;
 #pragma unroll
@@ -116,31 +150,34 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_rows(Problem p)
         before += v < wv ? tv : 0;
         total += tv;
     }
-    int pos = before + inc - cnt;
     int32_t *keys = p.row_keys + row * p.W;
-    if (prep_stage_keys(p)) {
-        // Through LDS, so that the list leaves in coalesced stores (each
-        // thread's run of keys would otherwise be one scattered store per key).
-        int32_t *sk = reinterpret_cast<int32_t *>(scan + kPrepThreads + 1);
-        for (int64_t w = w0; w < w1; ++w) {
-            uint32_t bits = bm[w];
-            while (bits) {
-                const int bit = __ffs(bits) - 1;
-                bits &= bits - 1;
-                sk[pos++] = (int32_t)(w * 32 + bit);
-            }
+    const bool staged = prep_stage_keys(p);
+    int32_t *sk = reinterpret_cast<int32_t *>(scan + kPrepThreads + 1);
+    int run = before;  // keys before the current 64-word block
+    for (int64_t w0 = wbeg; w0 < wend; w0 += 64) {
+        const int64_t w = w0 + lane;
+        uint32_t bits = w < wend ? bm[w] : 0u;
+        const int c = __popc(bits);
+        int inc = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(inc, off);
+            if (lane >= off) inc += t;
         }
+        int pos = run + inc - c;
+        while (bits) {
+            const int bit = __ffs(bits) - 1;
+            bits &= bits - 1;
+            const int32_t key = (int32_t)(w * 32 + bit);
+            if (staged) sk[pos++] = key;  // through LDS: the list leaves in coalesced stores
+            else keys[pos++] = key;
+        }
+        run += __shfl(inc, 63);
+    }
+    if (staged) {
         __syncthreads();
         for (int64_t s = tid; s < p.W; s += kPrepThreads) keys[s] = s < total ? sk[s] : -1;
     } else {
-        for (int64_t w = w0; w < w1; ++w) {
-            uint32_t bits = bm[w];
-            while (bits) {
-                const int bit = __ffs(bits) - 1;
-                bits &= bits - 1;
-                keys[pos++] = (int32_t)(w * 32 + bit);
-            }
-        }
         for (int64_t s = total + tid; s < p.W; s += kPrepThreads) keys[s] = -1;
     }
     if (tid == 0) {
