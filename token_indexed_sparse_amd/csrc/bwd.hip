@@ -274,19 +274,32 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
     const int32_t t_lo = (int32_t)(seg * p.seg_tiles);
     const int32_t t_hi = (int32_t)((seg + 1) * p.seg_tiles);
     const int32_t *idx_p = p.rev_p_idx + bt * p.nQT, *idx_f = p.rev_f_idx + bt * p.nQT;
-    auto lower_bound = [&](const int32_t *a, int32_t cnt, int32_t x) {
-        int32_t lo = 0, hi = cnt;
-        while (lo < hi) {
-            const int32_t mid = (lo + hi) >> 1;
-            if (a[mid] < x) lo = mid + 1;
-            else hi = mid;
+    // Entries of an ascending list below t_lo and below t_hi, counted by the
+    // whole wave at once: one memory latency per 256 entries instead of a
+    // chain of dependent loads.
+    auto count_below = [&](const int32_t *a, int32_t cnt, int32_t &c_lo, int32_t &c_hi) {
+        int32_t n_lo = 0, n_hi = 0;
+        for (int32_t b0 = 0; b0 < cnt; b0 += 256) {
+            int32_t v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int32_t x = b0 + 64 * u + lane;
+                v[u] = x < cnt ? a[x] : INT32_MAX;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                n_lo += __popcll(__ballot(v[u] < t_lo));
+                n_hi += __popcll(__ballot(v[u] < t_hi));
+            }
         }
-        return lo;
+        c_lo = n_lo;
+        c_hi = n_hi;
     };
     // Partial tiles only: the full ones are summed by the dense pass.
-    const int32_t cnt_p = p.rev_p_cnt[bt], cnt_f = 0;
-    const int32_t p_lo = lower_bound(idx_p, cnt_p, t_lo), p_hi = lower_bound(idx_p, cnt_p, t_hi);
-    const int32_t f_lo = lower_bound(idx_f, cnt_f, t_lo), f_hi = lower_bound(idx_f, cnt_f, t_hi);
+    const int32_t cnt_p = p.rev_p_cnt[bt];
+    int32_t p_lo, p_hi;
+    count_below(idx_p, cnt_p, p_lo, p_hi);
+    const int32_t f_lo = 0, f_hi = 0;
     const int64_t nwin = 2 * ((int64_t)(p_hi - p_lo) + (f_hi - f_lo));
     if (lane == 0) *flag = nwin > 0 ? 1 : 0;
     if (nwin == 0) return;
