@@ -267,13 +267,14 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
         return;
     }
 
-    // This item's query tiles: the entries of the tile column's reverse lists
-    // that fall in [t_lo, t_hi).
+    // This item's query tiles: the entries of the tile column's reverse list
+    // of partial tiles that fall in [t_lo, t_hi) (the full tiles are summed by
+    // the dense pass).
     const int64_t t = key0 >> 7;
     const int64_t bt = b * p.nKT + t;
     const int32_t t_lo = (int32_t)(seg * p.seg_tiles);
     const int32_t t_hi = (int32_t)((seg + 1) * p.seg_tiles);
-    const int32_t *idx_p = p.rev_p_idx + bt * p.nQT, *idx_f = p.rev_f_idx + bt * p.nQT;
+    const int32_t *idx_p = p.rev_p_idx + bt * p.nQT;
     // Entries of an ascending list below t_lo and below t_hi, counted by the
     // whole wave at once: one memory latency per 256 entries instead of a
     // chain of dependent loads.
@@ -295,12 +296,10 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
         c_lo = n_lo;
         c_hi = n_hi;
     };
-    // Partial tiles only: the full ones are summed by the dense pass.
     const int32_t cnt_p = p.rev_p_cnt[bt];
     int32_t p_lo, p_hi;
     count_below(idx_p, cnt_p, p_lo, p_hi);
-    const int32_t f_lo = 0, f_hi = 0;
-    const int64_t nwin = 2 * ((int64_t)(p_hi - p_lo) + (f_hi - f_lo));
+    const int64_t nwin = 2 * (int64_t)(p_hi - p_lo);  // 64-row windows
     if (lane == 0) *flag = nwin > 0 ? 1 : 0;
     if (nwin == 0) return;
 
@@ -417,16 +416,21 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
     };
 
     // Hits are visited in DESCENDING query order (tiles from the top of the
-    // merged reverse lists, the upper 64 rows of a tile first): all items of a
+    // reverse list of partial tiles, the upper 64 rows of a tile first): all items of a
     // segment sweep its rows at about the same rate, so the rows they read
     // stay in the caches.
     const int64_t mstride = p.stride >> 5;
     const uint32_t *mrow = p.mbits + (b * p.Sq) * mstride + (key0 >> 5);
     const int shift = (int)(key0 & 16);
     const uint64_t above = (lane == 63) ? 0ull : (~0ull << (lane + 1));
+    // The segment's tiles, read once: lane j holds entry p_lo + j (segments of
+    // more than 64 tiles read the list in memory).
+    const int32_t nt = p_hi - p_lo;
+    const int32_t tl = lane < nt ? idx_p[p_lo + lane] : -1;
+    auto seg_tile = [&](int32_t j) {
+        return nt <= 64 ? __builtin_amdgcn_readlane(tl, j) : idx_p[p_lo + j];
+    };
     int64_t w = 0;
-    int32_t ip = p_hi - 1, jf = f_hi - 1;
-    int32_t cur_tile = -1;
     while (w < nwin) {
         int nh = 0;
         while (w < nwin && nh <= kHitCap - kScanWin * 64) {
@@ -437,18 +441,8 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
                 m[x] = 0u;
                 rbase[x] = 0;
                 if (w + x < nwin) {
-                    if (((w + x) & 1) == 0) {
-                        const int32_t vp = ip >= p_lo ? idx_p[ip] : -1;
-                        const int32_t vq = jf >= f_lo ? idx_f[jf] : -1;
-                        if (vp > vq) {
-                            cur_tile = vp;
-                            --ip;
-                        } else {
-                            cur_tile = vq;
-                            --jf;
-                        }
-                    }
-                    rbase[x] = (int64_t)cur_tile * kTile + (((w + x) & 1) ? 0 : 64);
+                    const int32_t tile = seg_tile(nt - 1 - (int32_t)((w + x) >> 1));
+                    rbase[x] = (int64_t)tile * kTile + (((w + x) & 1) ? 0 : 64);
                     const int64_t qi = rbase[x] + lane;
                     if (qi < p.Sq) m[x] = (mrow[qi * mstride] >> shift) & 0xffffu;
                 }
