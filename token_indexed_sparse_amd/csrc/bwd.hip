@@ -15,7 +15,9 @@
 //    once the transposed K read for dQ is done). S^T = K Q^T and
 //    dP^T = V dO^T take K and V in the row layout; dS^T stays in the
 //    accumulator layout and is the B operand of dQ^T = K^T dS^T, whose K^T
-//    operand is the transposed read of the same staged K rows.
+//    operand is the transposed read of the same staged K rows. The high and
+//    low bf16 parts of dS go through one 16x16x32 MFMA whose K = 32 covers
+//    the 16 key slots twice, as the forward does with P.
 //  * k_dkdv: key-major. One wave owns 16 consecutive keys of one KV head and
 //    one segment of query tiles (8 by default, more when the partial sums
 //    would not fit the workspace budget), keeps the 16 K and V rows in registers and
@@ -170,6 +172,11 @@ __device__ __forceinline__ void dq_row(const Problem &p, lds_char *ks, lds_char 
                 gather(rv, vs, off);
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
+                    hold_after(kr[t]);
+                    hold_after(vr[t]);
+                }
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
                     sa = mfma_16x16x32(as_bf16x8(kr[t]), qf[t], sa);
                     pa = mfma_16x16x32(as_bf16x8(vr[t]), gf[t], pa);
                 }
@@ -190,18 +197,19 @@ __device__ __forceinline__ void dq_row(const Problem &p, lds_char *ks, lds_char 
                 // select, never multiply: a padding slot's dP is not used
                 ds[e] = valid ? pr * (pa[e] - dlt) : 0.f;
             }
-            // B operand dS^T of the 16x16x16 product: slot j of lane group
-            // quad is key 4*quad + j, the lane's own accumulator values.
+            // B operand dS^T of a 16x16x32 product whose K = 32 runs over the
+            // 16 keys twice: slots 0..3 of lane group quad hold the high bf16
+            // parts of keys 4*quad .. +3 (the lane's own accumulator values),
+            // slots 4..7 their low parts; the A operand repeats K^T's four
+            // keys in both halves.
             uint32_t dsh[2], dsl[2];
             split_bf16x2(ds[0], ds[1], dsh[0], dsl[0]);
             split_bf16x2(ds[2], ds[3], dsh[1], dsl[1]);
-            const bf16x4 dsv_hi = __builtin_bit_cast(bf16x4, make_uint2(dsh[0], dsh[1]));
-            const bf16x4 dsv_lo = __builtin_bit_cast(bf16x4, make_uint2(dsl[0], dsl[1]));
+            const bf16x8 dsv = __builtin_bit_cast(bf16x8, make_uint4(dsh[0], dsh[1], dsl[0], dsl[1]));
 #pragma unroll
             for (int db = 0; db < 16; ++db) {
-                const bf16x4 ka = __builtin_bit_cast(bf16x4, kt[db]);
-                acc[db] = mfma_16x16x16(ka, dsv_hi, acc[db]);
-                acc[db] = mfma_16x16x16(ka, dsv_lo, acc[db]);
+                const uint4 k8 = make_uint4(kt[db].x, kt[db].y, kt[db].x, kt[db].y);
+                acc[db] = mfma_16x16x32(as_bf16x8(k8), dsv, acc[db]);
             }
         }
         QSA_WAIT_VM(0);  // no gather may outlive the wave's LDS

@@ -353,6 +353,17 @@ __device__ __forceinline__ uint32_t opaque_u32(uint32_t x)
     return x;
 }
 
+// The compiler takes x as rewritten here, so arithmetic that reads it stays
+// after this point and after the volatile asm before it (a wait, the issue of
+// direct-to-LDS loads) instead of being interleaved with the reads that
+// produced it.
+__device__ __forceinline__ void hold_after(uint4 &x)
+{
+    u32x4 v = __builtin_bit_cast(u32x4, x);
+    asm volatile("" : "+v"(v));
+    x = __builtin_bit_cast(uint4, v);
+}
+
 __device__ __forceinline__ int64_t xcd_logical_block(int64_t b, int64_t n)
 {
     const int64_t x = b & 7, y = b >> 3;

@@ -26,19 +26,21 @@
 //    per-row swizzle of the 16-byte chunks keeps both reads free of bank
 //    conflicts.
 //  * The accumulator layout of S^T puts four key slots of one head in a lane,
-//    which is exactly the B operand layout of O^T = V^T P^T in the
-//    v_mfma_f32_16x16x16_bf16 form (K = 16 key slots), so P never leaves
-//    registers. Each lane owns one head: the running maximum and sum are per
-//    lane and the rescale of O is a per-lane scalar.
+//    which is the B operand layout of O^T = V^T P^T over 16 key slots, so P
+//    never leaves registers. Each lane owns one head: the running maximum and
+//    sum are per lane and the rescale of O is a per-lane scalar.
 //  * The first chunk fixes each head's reference maximum. P = exp2(s - ref)
 //    may then grow up to 2^64, which FP32 and the bf16 split carry exactly as
 //    well; a chunk further above the reference raises it and has the row
 //    recomputed from its first chunk (the result is the same, only the work
 //    repeats). O is therefore never rescaled inside the loop, and its
 //    accumulators stay in the matrix-core registers.
-//  * P is split into bf16 high and low parts (two MFMAs) so that the FP32
-//    output keeps about 16 mantissa bits of P; the normaliser is summed from
-//    the FP32 P.
+//  * P is split into bf16 high and low parts so that the FP32 output keeps
+//    about 16 mantissa bits of P; the normaliser is summed from the FP32 P.
+//    Both parts go through one v_mfma_f32_16x16x32_bf16 whose K = 32 covers
+//    the 16 key slots twice (high parts, then low parts, against the same V
+//    values repeated): on gfx950 the 16x16x16 form takes as many cycles as
+//    the 16x16x32 one, so two 16x16x16 products would cost twice as much.
 //  * Padding slots are zero operands with P = 0 by selection, so no unused
 //    K/V value ever enters the arithmetic.
 //  * Blocks are mapped XCD-aware: each XCD walks a contiguous range of rows,
@@ -197,6 +199,8 @@ __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_
                 QSA_WAIT_LDS();  // the K region is free
                 gather(rk, ks, off);
 #pragma unroll
+                for (int t = 0; t < 8; ++t) hold_after(kr[t]);
+#pragma unroll
                 for (int t = 0; t < 8; ++t) st = mfma_16x16x32(as_bf16x8(kr[t]), qf[t], st);
             }
 
@@ -232,13 +236,15 @@ __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_
                 pr[e] = __builtin_amdgcn_exp2f(t4[e] - m_run);
                 l_part += pr[e];
             }
-            // B operand P^T of the 16x16x16 product: slot j of lane group quad
-            // is key 4*quad + j, the lane's own accumulator values.
+            // B operand P^T of a 16x16x32 product whose K = 32 runs over the
+            // 16 keys twice: slots 0..3 of lane group quad hold the high bf16
+            // parts of keys 4*quad .. +3 (the lane's own accumulator values),
+            // slots 4..7 their low parts. The A operand repeats V^T's four
+            // keys in both halves, so one MFMA adds V^T (P_hi + P_lo)^T.
             uint32_t hi[2], lo[2];
             split_bf16x2(pr[0], pr[1], hi[0], lo[0]);
             split_bf16x2(pr[2], pr[3], hi[1], lo[1]);
-            const bf16x4 pb_hi = __builtin_bit_cast(bf16x4, make_uint2(hi[0], hi[1]));
-            const bf16x4 pb_lo = __builtin_bit_cast(bf16x4, make_uint2(lo[0], lo[1]));
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(hi[0], hi[1], lo[0], lo[1]));
             uint2 va[16];
             {
                 const lds_char *vsr = (const lds_char *)(uintptr_t)opaque_u32(lds_addr(vs));
@@ -250,9 +256,8 @@ __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_
             gather(rv, vs, off);
 #pragma unroll
             for (int db = 0; db < 16; ++db) {
-                const bf16x4 v4 = __builtin_bit_cast(bf16x4, va[db]);
-                acc[db] = mfma_16x16x16(v4, pb_hi, acc[db]);
-                acc[db] = mfma_16x16x16(v4, pb_lo, acc[db]);
+                const uint4 v8 = make_uint4(va[db].x, va[db].y, va[db].x, va[db].y);
+                acc[db] = mfma_16x16x32(as_bf16x8(v8), pb, acc[db]);
             }
         }
         QSA_WAIT_VM(0);  // no gather may outlive this pass or the wave's LDS
