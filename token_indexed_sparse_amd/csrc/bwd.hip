@@ -259,12 +259,16 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
     const int col = lane & 15, quad = lane >> 4;
     const int64_t ngroups = p.stride >> 4;
     const int64_t per_seg = p.B * p.Hkv * ngroups;
-    // item = (nseg - 1 - seg) * per_seg + (b * Hkv + g) * ngroups + kg: all key
-    // groups of one query segment run side by side and read the same rows.
+    // item = seg * per_seg + (b * Hkv + g) * ngroups + kg: all key groups of
+    // one query segment run side by side and read the same rows. Segments go
+    // in ascending order: under a causal route budget the early segments have
+    // the fewest candidate keys, so each of their key groups is hit by the
+    // most rows, and their long items start first instead of trailing at the
+    // end of the launch.
     const int64_t item = blockIdx.x;
     if (item >= p.nseg * per_seg) return;
-    const int64_t seg = p.nseg - 1 - item / per_seg;
-    const int64_t rem = item - (p.nseg - 1 - seg) * per_seg;
+    const int64_t seg = item / per_seg;
+    const int64_t rem = item - seg * per_seg;
     const int64_t kg = rem % ngroups, bg = rem / ngroups;
     const int g = (int)(bg % p.Hkv);
     const int64_t b = bg / p.Hkv;
@@ -474,23 +478,31 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
         // end of its step, once all its reads have returned.
         auto hit_row = [&](int h) { return __builtin_amdgcn_readfirstlane((uint32_t)hrow[h]); };
         for (int r0 = 0; r0 < kRingRows && r0 < nh; ++r0) stage_row(hit_row(r0), r0);
-        int slot = 0;
-        for (int h = 0; h < nh; ++h) {
-            // Row h has landed once at most the rows staged after it are in flight.
-            if (h + 2 < nh) QSA_WAIT_VM(2 * kRowOps);
-            else if (h + 1 < nh) QSA_WAIT_VM(kRowOps);
-            else QSA_WAIT_VM(0);
-            // The reads take their address from this block, so none of them is
-            // moved above the wait.
-            const lds_char *sl = (const lds_char *)(uintptr_t)opaque_u32(slots_addr + (uint32_t)(slot * kSlot));
-            const uint32_t mcur = hmask[h];
-            uint4 qa[8], ga[8];
+        // Row-layout reads of one slot (A operands of S and dP). The address
+        // is made opaque after the wait that precedes the call, so none of
+        // the reads is moved above that wait.
+        uint4 qa[8], ga[8];
+        auto read_rows = [&](int sl_idx) {
+            const lds_char *sr =
+                (const lds_char *)(uintptr_t)opaque_u32(slots_addr + (uint32_t)(sl_idx * kSlot));
 #pragma unroll
             for (int t8 = 0; t8 < 8; ++t8) {
                 const int o = ahead * 512 + (((4 * t8 + quad) ^ amask) << 4);
-                qa[t8] = lds_read16(sl + o);
-                ga[t8] = lds_read16(sl + kGroup * 512 + o);
+                qa[t8] = lds_read16(sr + o);
+                ga[t8] = lds_read16(sr + kGroup * 512 + o);
             }
+        };
+        // Row 0 has landed once at most the rows staged after it are in flight.
+        if (nh > 2) QSA_WAIT_VM(2 * kRowOps);
+        else if (nh > 1) QSA_WAIT_VM(kRowOps);
+        else QSA_WAIT_VM(0);
+        read_rows(0);
+        int slot = 0;
+        for (int h = 0; h < nh; ++h) {
+            // Row h has landed (waited for before its row-layout reads, which
+            // were issued during the previous row's products).
+            const lds_char *sl = (const lds_char *)(uintptr_t)opaque_u32(slots_addr + (uint32_t)(slot * kSlot));
+            const uint32_t mcur = hmask[h];
             uint2 tq[16], tg[16];
 #pragma unroll
             for (int db = 0; db < 16; ++db) {
@@ -519,6 +531,14 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
                 pn[e] = pr;
                 // select, never multiply: an unselected key's dP may be non-finite
                 dn[e] = on ? pr * (pd[e] - dl_c[e]) : 0.f;
+            }
+            // The next row's row-layout reads fly during this row's dV/dK
+            // products. Rows h+1 and h+2 are the ones in flight here; row h+1
+            // has landed once at most h+2's loads remain.
+            if (h + 1 < nh) {
+                if (h + 2 < nh) QSA_WAIT_VM(kRowOps);
+                else QSA_WAIT_VM(0);
+                read_rows(slot == kRingRows - 1 ? 0 : slot + 1);
             }
             if (pending) {
                 flush(pn, dn, tq, tg);
