@@ -30,10 +30,11 @@
 //    delta are gathered into a 3-slot LDS ring by direct-to-LDS loads, two
 //    rows ahead, then read
 //    in the row layout (A operands of S = Q K^T and dP = dO V^T, M = heads)
-//    and transposed (B operands of dV += P^T dO and dK += dS^T Q, where two
-//    rows' heads form the 32-long contraction). P and dS enter these products
-//    (and dS the dQ product) as bf16 high + low parts, so that sums over
-//    thousands of query heads keep FP32-level error.
+//    and transposed (B operands of dV += P^T dO and dK += dS^T Q, whose
+//    32-long contraction takes the row's heads twice: high parts, then low
+//    parts). P and dS enter these products (and dS the dQ product) as bf16
+//    high + low parts, so that sums over thousands of query heads keep
+//    FP32-level error.
 //  * k_dkdv_reduce: the FP32 partial sums of the segments and then of the
 //    dense full-tile pass are added in that fixed order (deterministic, no
 //    atomics) and written as bf16 dK, dV.
@@ -395,35 +396,25 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
     const int tlane = th * 512 + ((((col >> 1) & 1) ^ (tm & 1)) << 4) + (col & 1) * 8;
     const int txor = tm >> 1;
 
-    // Pending row of the current pair: its P, dS and transposed operands.
-    float pa[4] = {0.f, 0.f, 0.f, 0.f}, da[4] = {0.f, 0.f, 0.f, 0.f};
-    uint2 pq[16], pg[16];
-    bool pending = false;
-
-    // dV += P^T dO and dK += dS^T Q for the pending row (k slots 0..3 of each
-    // lane group) and a second row (slots 4..7); P and dS as bf16 high + low.
-    auto flush = [&](const float *pb, const float *db_, const uint2 *bq, const uint2 *bg_) {
-        uint32_t ph[4], pl[4], dh[4], dl[4];
-        split_bf16x2(pa[0], pa[1], ph[0], pl[0]);
-        split_bf16x2(pa[2], pa[3], ph[1], pl[1]);
-        split_bf16x2(pb[0], pb[1], ph[2], pl[2]);
-        split_bf16x2(pb[2], pb[3], ph[3], pl[3]);
-        split_bf16x2(da[0], da[1], dh[0], dl[0]);
-        split_bf16x2(da[2], da[3], dh[1], dl[1]);
-        split_bf16x2(db_[0], db_[1], dh[2], dl[2]);
-        split_bf16x2(db_[2], db_[3], dh[3], dl[3]);
-        const bf16x8 A_p = as_bf16x8(make_uint4(ph[0], ph[1], ph[2], ph[3]));
-        const bf16x8 A_pl = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
-        const bf16x8 A_d = as_bf16x8(make_uint4(dh[0], dh[1], dh[2], dh[3]));
-        const bf16x8 A_dl = as_bf16x8(make_uint4(dl[0], dl[1], dl[2], dl[3]));
+    // dV += P^T dO and dK += dS^T Q for one row. The 32-long contraction
+    // covers the row's 16 head slots twice: k slots 0..3 of lane group quad
+    // hold the high bf16 parts of P (or dS) for heads 4*quad .. +3 (the lane's
+    // own accumulator values of S), slots 4..7 their low parts, and the B
+    // operand repeats the transposed dO (or Q) values of the same four heads.
+    auto flush = [&](const float *pn, const float *dn, const uint2 *bq, const uint2 *bg_) {
+        uint32_t ph[2], pl[2], dh[2], dl[2];
+        split_bf16x2(pn[0], pn[1], ph[0], pl[0]);
+        split_bf16x2(pn[2], pn[3], ph[1], pl[1]);
+        split_bf16x2(dn[0], dn[1], dh[0], dl[0]);
+        split_bf16x2(dn[2], dn[3], dh[1], dl[1]);
+        const bf16x8 A_p = as_bf16x8(make_uint4(ph[0], ph[1], pl[0], pl[1]));
+        const bf16x8 A_d = as_bf16x8(make_uint4(dh[0], dh[1], dl[0], dl[1]));
 #pragma unroll
         for (int db = 0; db < 16; ++db) {
-            const bf16x8 Bg = as_bf16x8(make_uint4(pg[db].x, pg[db].y, bg_[db].x, bg_[db].y));
-            const bf16x8 Bq = as_bf16x8(make_uint4(pq[db].x, pq[db].y, bq[db].x, bq[db].y));
+            const bf16x8 Bg = as_bf16x8(make_uint4(bg_[db].x, bg_[db].y, bg_[db].x, bg_[db].y));
+            const bf16x8 Bq = as_bf16x8(make_uint4(bq[db].x, bq[db].y, bq[db].x, bq[db].y));
             adv[db] = mfma_16x16x32(A_p, Bg, adv[db]);
-            adv[db] = mfma_16x16x32(A_pl, Bg, adv[db]);
             adk[db] = mfma_16x16x32(A_d, Bq, adk[db]);
-            adk[db] = mfma_16x16x32(A_dl, Bq, adk[db]);
         }
     };
 
@@ -540,22 +531,7 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
                 else QSA_WAIT_VM(0);
                 read_rows(slot == kRingRows - 1 ? 0 : slot + 1);
             }
-            if (pending) {
-                flush(pn, dn, tq, tg);
-                pending = false;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    pa[e] = pn[e];
-                    da[e] = dn[e];
-                }
-#pragma unroll
-                for (int db = 0; db < 16; ++db) {
-                    pq[db] = tq[db];
-                    pg[db] = tg[db];
-                }
-                pending = true;
-            }
+            flush(pn, dn, tq, tg);
             if (h + kRingRows < nh) {
                 const uint32_t qn = hit_row(h + kRingRows);
                 QSA_WAIT_LDS();  // every read of this slot has returned
@@ -566,14 +542,6 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
         QSA_WAIT_VM(0);
         wave_lds_sync();
     }
-    if (pending) {
-        const float zero4[4] = {0.f, 0.f, 0.f, 0.f};
-        uint2 z[16];
-#pragma unroll
-        for (int db = 0; db < 16; ++db) z[db] = make_uint2(0u, 0u);
-        flush(zero4, zero4, z, z);
-    }
-
     // Lane holds dK/dV[key 4*quad+e][d 16*db + col]; the partial sums of this
     // segment go to its slice of the workspace, dK first, then dV.
     float *part = p.kv_part + ((bg * p.nslot + seg) * p.stride + key0) * (int64_t)(2 * kD);
