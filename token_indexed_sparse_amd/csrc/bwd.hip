@@ -464,9 +464,10 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
         }
         if (nh == 0) continue;
         wave_lds_sync();
-        // Rows of the batch in order; row h is staged in slot h % 3, up to two
-        // rows ahead of the one being computed. A row's slot is refilled at the
-        // end of its step, once all its reads have returned.
+        // Rows of the batch in order; row h is staged in slot h % 3. A row's
+        // slot is refilled with row h+3 as soon as all its reads have returned
+        // (before its softmax and products), so up to three rows are in flight
+        // while one is computed.
         auto hit_row = [&](int h) { return __builtin_amdgcn_readfirstlane((uint32_t)hrow[h]); };
         for (int r0 = 0; r0 < kRingRows && r0 < nh; ++r0) stage_row(hit_row(r0), r0);
         // Row-layout reads of one slot (A operands of S and dP). The address
@@ -512,6 +513,14 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
                 sa = mfma_16x16x32(as_bf16x8(qa[t8]), kf[t8], sa);
                 pd = mfma_16x16x32(as_bf16x8(ga[t8]), vf[t8], pd);
             }
+            // Every read of this slot is issued; once they have returned the
+            // slot takes row h+3, whose loads then fly during this row's
+            // softmax and products as well.
+            if (h + kRingRows < nh) {
+                const uint32_t qn = hit_row(h + kRingRows);
+                QSA_WAIT_LDS();
+                stage_row(qn, slot);
+            }
             // Lane holds S[head 4*quad+e][key col].
             const bool on = hq && ((mcur >> col) & 1u);
             float pn[4], dn[4];
@@ -524,19 +533,16 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
                 dn[e] = on ? pr * (pd[e] - dl_c[e]) : 0.f;
             }
             // The next row's row-layout reads fly during this row's dV/dK
-            // products. Rows h+1 and h+2 are the ones in flight here; row h+1
-            // has landed once at most h+2's loads remain.
+            // products. Rows h+1 .. h+3 are the ones in flight here (staged in
+            // order); row h+1 has landed once at most the later rows' loads
+            // remain.
             if (h + 1 < nh) {
-                if (h + 2 < nh) QSA_WAIT_VM(kRowOps);
+                if (h + 3 < nh) QSA_WAIT_VM(2 * kRowOps);
+                else if (h + 2 < nh) QSA_WAIT_VM(kRowOps);
                 else QSA_WAIT_VM(0);
                 read_rows(slot == kRingRows - 1 ? 0 : slot + 1);
             }
             flush(pn, dn, tq, tg);
-            if (h + kRingRows < nh) {
-                const uint32_t qn = hit_row(h + kRingRows);
-                QSA_WAIT_LDS();  // every read of this slot has returned
-                stage_row(qn, slot);
-            }
             slot = slot == kRingRows - 1 ? 0 : slot + 1;
         }
         QSA_WAIT_VM(0);
