@@ -27,8 +27,8 @@
 //    pass), reads a 16-bit slice of the bit-packed membership row of every
 //    query in those tiles, and lists the rows that select one of its keys in
 //    LDS. Each listed row's Q and dO (12 heads x 512 bytes each), lse and
-//    delta are gathered into a 3-slot LDS ring by direct-to-LDS loads, two
-//    rows ahead, then read
+//    delta are gathered into a 3-slot LDS ring by direct-to-LDS loads (a
+//    slot takes the row three ahead once its reads have returned), then read
 //    in the row layout (A operands of S = Q K^T and dP = dO V^T, M = heads)
 //    and transposed (B operands of dV += P^T dO and dK += dS^T Q, whose
 //    32-long contraction takes the row's heads twice: high parts, then low
