@@ -297,11 +297,6 @@ __device__ __forceinline__ void lds_read_tr_x8(u32x2 (&d)[8], const uint32_t (&a
         : "memory");
 }
 
-__device__ __forceinline__ f32x4 mfma_16x16x16(bf16x4 a, bf16x4 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
 // Explicit waits for direct-to-LDS loads, which produce no register the
 // compiler could track. The s_waitcnt immediate of this architecture holds
 // vmcnt in bits 3..0 and 15..14, expcnt in 6..4 and lgkmcnt in 11..8; a
