@@ -75,16 +75,26 @@ typedef enum qsa_status {
     QSA_ERR_HEADDIM = 4,     /* D != 256 */
     QSA_ERR_SCALE = 5,       /* scale not finite or not > 0 */
     QSA_ERR_ALIGN = 6,       /* a pointer is not aligned as stated above */
-    QSA_ERR_ROUTE_DTYPE = 7, /* route_is_i64 not 0 or 1, or reserved != 0 */
+    QSA_ERR_ROUTE_DTYPE = 7, /* route_is_i64 not 0 or 1, or an unknown flags bit */
     QSA_ERR_WORKSPACE = 8,   /* workspace NULL or smaller than required */
     QSA_ERR_DEVICE = 9,      /* no gfx950 device current, or a HIP runtime error */
     QSA_ERR_LAUNCH = 10      /* a kernel launch failed */
 } qsa_status;
 
+/* Bits of qsa_dims.flags.
+ * QSA_FLAG_DETERMINISTIC: the same inputs give bitwise the same outputs on
+ *   every call. Without it (the default) the gathered forward and dQ passes
+ *   start each query row's walk over its key list at the point that the rows
+ *   running beside it on the same XCD have reached, so that rows in flight
+ *   share the key rows in L2; the sums are the same sums taken in another
+ *   order, so out_fp32, lse and dq (and through them dk, dv) can differ in
+ *   the last bits between calls, with the same accuracy. */
+#define QSA_FLAG_DETERMINISTIC 1
+
 typedef struct qsa_dims {
     int64_t B, Sq, Skv, Hq, Hkv, D, W;
     int32_t route_is_i64; /* 0: routes are int32, 1: int64 */
-    int32_t reserved;     /* must be 0 */
+    int32_t flags;        /* QSA_FLAG_* bits; every other bit must be 0 */
 } qsa_dims;
 
 /* Sizes of the workspace each call needs (0 if `dims` is invalid). */

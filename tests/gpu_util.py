@@ -37,7 +37,7 @@ class GpuRun:
     """Inputs on the GPU and the outputs of one forward + backward."""
 
     def __init__(self, inp: synth.Inputs, scale: float, routes: np.ndarray = None,
-                 backward: bool = True):
+                 backward: bool = True, deterministic: bool = False):
         r = inp.routes if routes is None else routes
         self.q = to_gpu_bf16(inp.q)
         self.k = to_gpu_bf16(inp.k)
@@ -45,10 +45,12 @@ class GpuRun:
         self.g = to_gpu_bf16(inp.grad_out) if inp.grad_out is not None else None
         self.routes = torch.from_numpy(np.ascontiguousarray(r)).cuda()
         self.scale = scale
-        self.out, self.out32, self.lse = qsa.forward(self.q, self.k, self.v, self.routes, scale)
+        self.out, self.out32, self.lse = qsa.forward(self.q, self.k, self.v, self.routes, scale,
+                                                     deterministic=deterministic)
         if backward and self.g is not None:
             self.dq, self.dk, self.dv = qsa.backward(self.g, self.q, self.k, self.v, self.out32,
-                                                     self.lse, self.routes, scale)
+                                                     self.lse, self.routes, scale,
+                                                     deterministic=deterministic)
         torch.cuda.synchronize()
 
 

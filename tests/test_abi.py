@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def _dims(**kw):
     from token_indexed_sparse_amd import qsa
-    base = dict(B=1, Sq=256, Skv=256, Hq=12, Hkv=1, D=256, W=36, route_is_i64=0, reserved=0)
+    base = dict(B=1, Sq=256, Skv=256, Hq=12, Hkv=1, D=256, W=36, route_is_i64=0, flags=0)
     base.update(kw)
     return qsa.Dims(**base)
 
@@ -66,7 +66,7 @@ def test_workspace_sizes(lib):
 @pytest.mark.parametrize("kw,status", [
     (dict(D=128), 4), (dict(Hq=16), 3), (dict(Hq=24, Hkv=1), 3), (dict(Hkv=0, Hq=0), 3),
     (dict(B=0), 2), (dict(Sq=0), 2), (dict(Skv=0), 2), (dict(W=0), 2),
-    (dict(Skv=(1 << 19) + 1), 2), (dict(route_is_i64=2), 7), (dict(reserved=1), 7),
+    (dict(Skv=(1 << 19) + 1), 2), (dict(route_is_i64=2), 7), (dict(flags=2), 7),
 ])
 def test_validation_errors_before_any_launch(lib, kw, status):
     d = _dims(**kw)

@@ -37,7 +37,7 @@ int64_t seg_tiles_for(const qsa_dims *d)
 qsa_status check_dims(const qsa_dims *d)
 {
     if (!d) return QSA_ERR_NULL;
-    if ((d->route_is_i64 != 0 && d->route_is_i64 != 1) || d->reserved != 0)
+    if ((d->route_is_i64 != 0 && d->route_is_i64 != 1) || (d->flags & ~QSA_FLAG_DETERMINISTIC) != 0)
         return QSA_ERR_ROUTE_DTYPE;
     if (d->B < 1 || d->Sq < 1 || d->Skv < 1 || d->W < 1) return QSA_ERR_SHAPE;
     if (d->D != kD) return QSA_ERR_HEADDIM;
@@ -62,7 +62,7 @@ qsa_status check_dims(const qsa_dims *d)
 
 struct Layout {
     size_t memb, has, mbits, row_keys, row_cnt, pkeys, pcnt, tile_cnt, kinds, fpc, fpi, ffc, ffi,
-        rpc, rpi, rfc, rfi, fstate, delta, kv_part, kv_flag, total;
+        rpc, rpi, rfc, rfi, fstate, delta, kv_part, kv_flag, walk, total;
 };
 
 // which: 0 forward, 1 backward, 2 preprocess (only tile counts and, if the
@@ -115,6 +115,7 @@ Layout layout(const qsa_dims *d, int which)
     const size_t dq_bytes = (size_t)(rows * d->Hq) * kD * 4;
     L.kv_part = which == 1 ? take(kv_bytes > dq_bytes ? kv_bytes : dq_bytes) : none;
     L.kv_flag = which == 1 ? take((size_t)(d->B * d->Hkv * (nseg + 1) * (stride / 16))) : none;
+    L.walk = which == 2 ? none : take(16 * 4);
     L.total = off;
     return L;
 }
@@ -154,6 +155,7 @@ void fill_common(Problem &p, const qsa_dims *d, const void *routes, float scale)
     p.Hkv = d->Hkv;
     p.W = d->W;
     p.route_is_i64 = d->route_is_i64;
+    p.flags = d->flags;
     p.nQT = (d->Sq + kTile - 1) / kTile;
     p.nKT = (d->Skv + kTile - 1) / kTile;
     p.stride = p.nKT * kTile;
@@ -196,6 +198,9 @@ void carve(Problem &p, const Layout &L, void *ws)
         p.dq_part = p.kv_part;
     }
     if (L.kv_flag != none) p.kv_flag = reinterpret_cast<uint8_t *>(w + L.kv_flag);
+    // Deterministic calls walk every key list from its start (no walk clocks).
+    if (L.walk != none && !(p.flags & QSA_FLAG_DETERMINISTIC))
+        p.walk = reinterpret_cast<uint32_t *>(w + L.walk);
 }
 
 qsa_status check_scale(float scale)
@@ -393,7 +398,7 @@ const char *qsa_status_string(qsa_status status)
     case QSA_ERR_HEADDIM: return "head dimension must be 256";
     case QSA_ERR_SCALE: return "scale must be finite and > 0";
     case QSA_ERR_ALIGN: return "a pointer is not aligned (16 bytes for tensors, 4/8 for lse and routes)";
-    case QSA_ERR_ROUTE_DTYPE: return "routes must be int32 or int64 (route_is_i64 0 or 1, reserved 0)";
+    case QSA_ERR_ROUTE_DTYPE: return "routes must be int32 or int64 (route_is_i64 0 or 1), and flags only QSA_FLAG_* bits";
     case QSA_ERR_WORKSPACE: return "workspace is NULL or smaller than the size query returned";
     case QSA_ERR_DEVICE: return "no gfx950 device is current, or the HIP runtime failed";
     case QSA_ERR_LAUNCH: return "a kernel launch failed";

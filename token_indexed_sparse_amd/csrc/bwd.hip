@@ -149,9 +149,20 @@ __device__ __forceinline__ void dq_row(const Problem &p, lds_char *ks, lds_char 
         const int txor = tm >> 1;
 
         const int nchunks = (n + kChunk - 1) / kChunk;
-        int knext = fetch_key(1);
+        // Walk rotation aligned with the rows in flight, as in the forward
+        // (its own clock).
+        uint32_t *const clk = p.walk ? p.walk + 8 : nullptr;
+        int rot = 0;
+        if (clk && nchunks > 1) {
+            const uint32_t done = __hip_atomic_fetch_add(clk, opaque_u32(0u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            rot = (int)__builtin_amdgcn_readfirstlane((done / kWalkSlots) % (uint32_t)nchunks);
+        }
+        auto phys = [&](int x) {
+            return x >= nchunks ? x : (x + rot >= nchunks ? x + rot - nchunks : x + rot);
+        };
+        int knext = fetch_key(phys(1));
         uint32_t off[8];
-        offsets(fetch_key(0), off);
+        offsets(fetch_key(phys(0)), off);
         gather(rk, ks, off);
         gather(rv, vs, off);
         for (int ch = 0; ch < nchunks; ++ch) {
@@ -159,7 +170,8 @@ __device__ __forceinline__ void dq_row(const Problem &p, lds_char *ks, lds_char 
             // compiler orders LDS reads after all earlier direct-to-LDS loads).
             QSA_WAIT_VM(0);
             offsets(knext, off);
-            knext = fetch_key(ch + 2);
+            knext = fetch_key(phys(ch + 2));
+            const int pc = phys(ch);  // the chunk's place in the list
             f32x4 sa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
             {
                 uint4 kr[8], vr[8];
@@ -193,7 +205,7 @@ __device__ __forceinline__ void dq_row(const Problem &p, lds_char *ks, lds_char 
             float ds[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const bool valid = hv && (ch * kChunk + 4 * quad + e < n);
+                const bool valid = hv && (pc * kChunk + 4 * quad + e < n);
                 const float pr = valid ? exp2f(sa[e] * c - lse2) : 0.f;
                 // select, never multiply: a padding slot's dP is not used
                 ds[e] = valid ? pr * (pa[e] - dlt) : 0.f;
@@ -214,6 +226,8 @@ __device__ __forceinline__ void dq_row(const Problem &p, lds_char *ks, lds_char 
             }
         }
         QSA_WAIT_VM(0);  // no gather may outlive the wave's LDS
+        if (clk && lane == 0)
+            __hip_atomic_fetch_add(clk, (uint32_t)nchunks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (!hv) return;
     if (handoff) {

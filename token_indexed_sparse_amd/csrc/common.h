@@ -24,6 +24,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 struct Problem {
     int64_t B, Sq, Skv, Hq, Hkv, W;
     int32_t route_is_i64;
+    int32_t flags;  // QSA_FLAG_* bits of the call
     int64_t stride;  // membership row stride = nKT * 128
     int64_t nQT, nKT;
     float scale;
@@ -62,7 +63,15 @@ struct Problem {
     // Hand-off from the gathered to the dense dQ: unscaled FP32 sums
     // [B, Sq, Hq, 256] of the rows whose tile row has full tiles.
     float *dq_part;
+    // Walk clocks of the gathered forward (word 0) and dQ (word 8) passes,
+    // zeroed by the preprocessing: the key chunks of the rows finished so far.
+    // Null when the call asks for deterministic results.
+    uint32_t *walk;
 };
+
+// Resident waves of a gathered pass (256 CUs x 4 SIMDs x 2 waves): the walk
+// clock divided by this is how many chunks a wave slot has walked so far.
+constexpr uint32_t kWalkSlots = 2048;
 
 hipError_t launch_preprocess(const Problem &p, hipStream_t s);
 hipError_t launch_partial_keys(const Problem &p, hipStream_t s);

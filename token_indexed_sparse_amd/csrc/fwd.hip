@@ -176,20 +176,38 @@ __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_
     const int vxor = vm >> 1;
 
     const int nchunks = (n + kChunk - 1) / kChunk;
+    // Walk rotation. Rows start whenever a slot frees up, so without it the
+    // rows in flight sit at scattered points of their (similar) ascending key
+    // lists and share little of the caches. A row starts instead at the chunk
+    // that the wave slots have reached on average (the chunks of all finished
+    // rows over the resident slots, modulo the row's chunk count) and wraps
+    // around, so the rows in flight walk the same part of their lists. Any
+    // walk order gives the same result up to FP32 rounding order.
+    uint32_t *const clk = p.walk;
+    int rot = 0;
+    if (clk && nchunks > 1) {
+        const uint32_t done = __hip_atomic_fetch_add(clk, opaque_u32(0u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        rot = (int)__builtin_amdgcn_readfirstlane((done / kWalkSlots) % (uint32_t)nchunks);
+    }
+    // Chunk x of the walk; positions past the list stay past it.
+    auto phys = [&](int x) {
+        return x >= nchunks ? x : (x + rot >= nchunks ? x + rot - nchunks : x + rot);
+    };
     bool restart = false;
     for (;;) {
         uint4 kn[2];
         uint32_t off[8];
-        fetch_keys(0, kn);
-        offsets(kn, 0, off);
-        fetch_keys(1, kn);
+        fetch_keys(phys(0), kn);
+        offsets(kn, phys(0), off);
+        fetch_keys(phys(1), kn);
         gather(rk, ks, off);
         gather(rv, vs, off);
 
         for (int ch = 0; ch < nchunks; ++ch) {
             QSA_WAIT_VM(0);
-            offsets(kn, ch + 1, off);  // next chunk
-            fetch_keys(ch + 2, kn);
+            offsets(kn, phys(ch + 1), off);  // next chunk
+            fetch_keys(phys(ch + 2), kn);
+            const int pc = phys(ch);  // the chunk's place in the list
             f32x4 st = {0.f, 0.f, 0.f, 0.f};
             {
                 uint4 kr[8];
@@ -207,7 +225,7 @@ __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_
             // Softmax numerators; lane holds key slots 4*quad + e of head col.
             float t4[4];
             float mx = -INFINITY;
-            if ((ch + 1) * kChunk <= n) {
+            if ((pc + 1) * kChunk <= n) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     t4[e] = st[e] * c;
@@ -216,7 +234,7 @@ __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const bool valid = ch * kChunk + 4 * quad + e < n;
+                    const bool valid = pc * kChunk + 4 * quad + e < n;
                     t4[e] = valid ? st[e] * c : -INFINITY;
                     mx = fmaxf(mx, t4[e]);
                 }
@@ -267,6 +285,8 @@ __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_
         for (int db = 0; db < 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
         l_part = 0.f;
     }
+    if (clk && lane == 0)
+        __hip_atomic_fetch_add(clk, (uint32_t)nchunks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     float l = l_part + __shfl_xor(l_part, 16);
     l += __shfl_xor(l, 32);

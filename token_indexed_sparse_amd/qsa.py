@@ -37,7 +37,7 @@ class Dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("Sq", ctypes.c_int64), ("Skv", ctypes.c_int64),
                 ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64), ("D", ctypes.c_int64),
                 ("W", ctypes.c_int64), ("route_is_i64", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("flags", ctypes.c_int32)]
 
 
 def library() -> ctypes.CDLL:
@@ -78,11 +78,15 @@ def _raise(status: int) -> None:
     raise QSAError(status, msg)
 
 
-def make_dims(B, Sq, Skv, Hq, Hkv, D, W, route_is_i64=False) -> Dims:
-    return Dims(B, Sq, Skv, Hq, Hkv, D, W, 1 if route_is_i64 else 0, 0)
+FLAG_DETERMINISTIC = 1  # QSA_FLAG_DETERMINISTIC
 
 
-def _dims(q: torch.Tensor, k: torch.Tensor, routes: torch.Tensor) -> Dims:
+def make_dims(B, Sq, Skv, Hq, Hkv, D, W, route_is_i64=False, deterministic=False) -> Dims:
+    return Dims(B, Sq, Skv, Hq, Hkv, D, W, 1 if route_is_i64 else 0,
+                FLAG_DETERMINISTIC if deterministic else 0)
+
+
+def _dims(q: torch.Tensor, k: torch.Tensor, routes: torch.Tensor, deterministic=False) -> Dims:
     if q.dim() != 4 or k.dim() != 4 or routes.dim() != 3:
         raise ValueError("q, k must be [B, S, H, 256] and routes [B, Sq, W]")
     B, Sq, Hq, D = q.shape
@@ -91,7 +95,8 @@ def _dims(q: torch.Tensor, k: torch.Tensor, routes: torch.Tensor) -> Dims:
         raise ValueError("inconsistent shapes")
     if routes.dtype not in (torch.int32, torch.int64):
         raise TypeError("routes must be int32 or int64")
-    return make_dims(B, Sq, Skv, Hq, Hkv, D, routes.shape[2], routes.dtype == torch.int64)
+    return make_dims(B, Sq, Skv, Hq, Hkv, D, routes.shape[2], routes.dtype == torch.int64,
+                     deterministic)
 
 
 def _check(t: torch.Tensor, dtype, name: str) -> torch.Tensor:
@@ -129,15 +134,17 @@ def preprocess_workspace_bytes(dims: Dims) -> int:
 
 
 def forward(q, k, v, routes, scale: Optional[float] = None, *, out=None, out_fp32=None, lse=None,
-            workspace=None):
-    """QSA forward. Returns ``(out bf16, out_fp32, lse [B, Hq, Sq])``."""
+            workspace=None, deterministic: bool = False):
+    """QSA forward. Returns ``(out bf16, out_fp32, lse [B, Hq, Sq])``.
+
+    ``deterministic`` sets QSA_FLAG_DETERMINISTIC (bitwise reproducible)."""
     q = _check(q, torch.bfloat16, "q")
     k = _check(k, torch.bfloat16, "k")
     v = _check(v, torch.bfloat16, "v")
     routes = routes.contiguous()
     if not routes.is_cuda:
         raise ValueError("routes must be a GPU tensor")
-    dims = _dims(q, k, routes)
+    dims = _dims(q, k, routes, deterministic)
     if v.shape != k.shape:
         raise ValueError("v must have k's shape")
     if scale is None:
@@ -164,8 +171,10 @@ def forward(q, k, v, routes, scale: Optional[float] = None, *, out=None, out_fp3
 
 
 def backward(grad_out, q, k, v, out_fp32, lse, routes, scale: Optional[float] = None, *,
-             dq=None, dk=None, dv=None, workspace=None):
-    """QSA backward. Returns ``(dq, dk, dv)`` in bf16."""
+             dq=None, dk=None, dv=None, workspace=None, deterministic: bool = False):
+    """QSA backward. Returns ``(dq, dk, dv)`` in bf16.
+
+    ``deterministic`` sets QSA_FLAG_DETERMINISTIC (bitwise reproducible)."""
     grad_out = _check(grad_out, torch.bfloat16, "grad_out")
     q = _check(q, torch.bfloat16, "q")
     k = _check(k, torch.bfloat16, "k")
@@ -173,7 +182,7 @@ def backward(grad_out, q, k, v, out_fp32, lse, routes, scale: Optional[float] = 
     out_fp32 = _check(out_fp32, torch.float32, "out_fp32")
     lse = _check(lse, torch.float32, "lse")
     routes = routes.contiguous()
-    dims = _dims(q, k, routes)
+    dims = _dims(q, k, routes, deterministic)
     if scale is None:
         scale = 1.0 / (q.shape[-1] ** 0.5)
     if grad_out.shape != q.shape or out_fp32.shape != q.shape:
