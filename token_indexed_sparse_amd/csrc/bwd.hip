@@ -75,7 +75,7 @@ __device__ __forceinline__ void dq_row(const Problem &p, lds_char *ks, lds_char 
 {
     const int lane = threadIdx.x;
     const int col = lane & 15, quad = lane >> 4;
-    const int64_t item = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int64_t item = (int64_t)blockIdx.x;
     if (item >= p.B * p.Sq * p.Hkv) return;
     const int64_t row = item / p.Hkv;
     const int g = (int)(item - row * p.Hkv);
