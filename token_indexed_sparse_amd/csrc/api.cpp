@@ -123,6 +123,7 @@ Layout layout(const qsa_dims *d, int which)
 struct DeviceInfo {
     bool checked = false, ok = false;
     size_t max_lds = 0;
+    uint32_t cus = 0;
 };
 DeviceInfo g_dev[64];
 
@@ -136,13 +137,23 @@ qsa_status check_device(const qsa_dims *d)
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return QSA_ERR_DEVICE;
         info.ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
         info.max_lds = prop.sharedMemPerBlock;
+        info.cus = (uint32_t)prop.multiProcessorCount;
         info.checked = true;
     }
-    if (!info.ok) return QSA_ERR_DEVICE;
+    if (!info.ok || info.cus == 0) return QSA_ERR_DEVICE;
     const int64_t stride = (d->Skv + kTile - 1) / kTile * kTile;
     const size_t lds = (size_t)(stride / 32) * 4 + 257 * 4;
     if (lds > info.max_lds) return QSA_ERR_SHAPE;
     return QSA_OK;
+}
+
+// Resident waves of the gathered forward and dQ passes: two per SIMD, four
+// SIMDs per CU (their register use keeps two waves per SIMD).
+uint32_t walk_slots()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+    return g_dev[dev].cus * 8u;
 }
 
 void fill_common(Problem &p, const qsa_dims *d, const void *routes, float scale)
@@ -199,8 +210,10 @@ void carve(Problem &p, const Layout &L, void *ws)
     }
     if (L.kv_flag != none) p.kv_flag = reinterpret_cast<uint8_t *>(w + L.kv_flag);
     // Deterministic calls walk every key list from its start (no walk clocks).
-    if (L.walk != none && !(p.flags & QSA_FLAG_DETERMINISTIC))
+    if (L.walk != none && !(p.flags & QSA_FLAG_DETERMINISTIC)) {
         p.walk = reinterpret_cast<uint32_t *>(w + L.walk);
+        p.walk_slots = walk_slots();
+    }
 }
 
 qsa_status check_scale(float scale)

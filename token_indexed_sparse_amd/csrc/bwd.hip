@@ -155,7 +155,7 @@ __device__ __forceinline__ void dq_row(const Problem &p, lds_char *ks, lds_char 
         int rot = 0;
         if (clk && nchunks > 1) {
             const uint32_t done = __hip_atomic_fetch_add(clk, opaque_u32(0u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            rot = (int)__builtin_amdgcn_readfirstlane((done / kWalkSlots) % (uint32_t)nchunks);
+            rot = (int)__builtin_amdgcn_readfirstlane((done / p.walk_slots) % (uint32_t)nchunks);
         }
         auto phys = [&](int x) {
             return x >= nchunks ? x : (x + rot >= nchunks ? x + rot - nchunks : x + rot);

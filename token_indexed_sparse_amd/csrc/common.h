@@ -67,11 +67,10 @@ struct Problem {
     // zeroed by the preprocessing: the key chunks of the rows finished so far.
     // Null when the call asks for deterministic results.
     uint32_t *walk;
+    // Resident waves of those passes (CUs x 4 SIMDs x 2 waves): the walk
+    // clock divided by this is how many chunks a wave slot has walked so far.
+    uint32_t walk_slots;
 };
-
-// Resident waves of a gathered pass (256 CUs x 4 SIMDs x 2 waves): the walk
-// clock divided by this is how many chunks a wave slot has walked so far.
-constexpr uint32_t kWalkSlots = 2048;
 
 hipError_t launch_preprocess(const Problem &p, hipStream_t s);
 hipError_t launch_partial_keys(const Problem &p, hipStream_t s);

@@ -189,7 +189,7 @@ __device__ __forceinline__ void forward_row(const Problem &p, lds_char *ks, lds_
     int rot = 0;
     if (clk && nchunks > 1) {
         const uint32_t done = __hip_atomic_fetch_add(clk, opaque_u32(0u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        rot = (int)__builtin_amdgcn_readfirstlane((done / kWalkSlots) % (uint32_t)nchunks);
+        rot = (int)__builtin_amdgcn_readfirstlane((done / p.walk_slots) % (uint32_t)nchunks);
     }
     // Chunk x of the walk; positions past the list stay past it.
     auto phys = [&](int x) {
