@@ -176,6 +176,8 @@ def main() -> int:
                     help="workload name or index 1-5 (default: the 32k-token long-context one)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="set QSA_FLAG_DETERMINISTIC (head-first key walks, bitwise reproducible)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -220,7 +222,8 @@ def main() -> int:
     out32 = torch.empty(q.shape, dtype=torch.float32, device=dev)
     lse = torch.empty((wl.B, wl.Hq, wl.Sq), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dims = qsa.make_dims(wl.B, wl.Sq, wl.Skv, wl.Hq, wl.Hkv, wl.D, wl.W)
+    dims = qsa.make_dims(wl.B, wl.Sq, wl.Skv, wl.Hq, wl.Hkv, wl.D, wl.W,
+                         deterministic=args.deterministic)
     ws_f = torch.empty(qsa.forward_workspace_bytes(dims), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(qsa.backward_workspace_bytes(dims), dtype=torch.uint8, device=dev)
     lib = qsa.library()
@@ -301,7 +304,8 @@ def main() -> int:
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "Sq": wl.Sq, "Skv": wl.Skv, "Hq": wl.Hq,
                    "Hkv": wl.Hkv, "D": wl.D, "W": wl.W, "nnz_pairs": nnz, "full_tile_pairs": nnz_full,
-                   "flop_per_step": flop_fwd + flop_bwd, "parallelism": "single GPU"},
+                   "flop_per_step": flop_fwd + flop_bwd, "parallelism": "single GPU",
+                   "deterministic": bool(args.deterministic)},
         "mfma_peak_frac": value / PEAK_BF16_TFLOPS,
         "forward_tflops": flop_fwd / (fwd_ms * 1e-3) / 1e12,
         "backward_tflops": flop_bwd / (bwd_ms * 1e-3) / 1e12,

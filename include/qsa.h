@@ -83,12 +83,14 @@ typedef enum qsa_status {
 
 /* Bits of qsa_dims.flags.
  * QSA_FLAG_DETERMINISTIC: the same inputs give bitwise the same outputs on
- *   every call. Without it (the default) the gathered forward and dQ passes
- *   start each query row's walk over its key list at the point that the rows
- *   running beside it on the same XCD have reached, so that rows in flight
- *   share the key rows in L2; the sums are the same sums taken in another
- *   order, so out_fp32, lse and dq (and through them dk, dv) can differ in
- *   the last bits between calls, with the same accuracy. */
+ *   every call. Without it (the default), on calls with at least eight
+ *   query rows per resident wave of the device (B * Sq * Hkv >= 64 * CUs),
+ *   the gathered forward and dQ passes start each query row's walk over its
+ *   key list at the point that the rows in flight have reached, so that they
+ *   read the same key rows at about the same time; the sums are the same sums
+ *   taken in another order, so out_fp32, lse and dq (and through them dk, dv)
+ *   can differ in the last bits between calls, with the same accuracy.
+ *   Smaller calls are bitwise reproducible either way. */
 #define QSA_FLAG_DETERMINISTIC 1
 
 typedef struct qsa_dims {

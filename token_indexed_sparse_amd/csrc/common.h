@@ -72,6 +72,9 @@ struct Problem {
     uint32_t walk_slots;
 };
 
+// Rows per wave slot from which the gathered passes rotate their key walks.
+constexpr int kWalkRounds = 8;
+
 hipError_t launch_preprocess(const Problem &p, hipStream_t s);
 hipError_t launch_partial_keys(const Problem &p, hipStream_t s);
 hipError_t launch_forward(const Problem &p, hipStream_t s);
