@@ -33,7 +33,7 @@ def bf16_bits_of(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-class GpuRun:
+class DeviceRun:
     """Inputs on the GPU and the outputs of one forward + backward."""
 
     def __init__(self, inp: synth.Inputs, scale: float, routes: np.ndarray = None,

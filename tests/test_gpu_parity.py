@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import (TOL_BF16, TOL_FP32, GpuRun, bf16_bits_of, check_close,
+from gpu_util import (TOL_BF16, TOL_FP32, DeviceRun, bf16_bits_of, check_close,
                       check_preprocess_exact, log, to_np)
 from token_indexed_sparse_amd import qsa, synth
 
@@ -26,7 +26,7 @@ def _gpu():
 
 
 def _full_compare(inp, scale, run=None):
-    run = run or GpuRun(inp, scale)
+    run = run or DeviceRun(inp, scale)
     P = oracle.Problem(inp.q, inp.k, inp.v, inp.routes, scale, inp.grad_out)
     o_ref, l_ref = P.forward_full()
     check_close("out_fp32", to_np(run.out32), o_ref, TOL_FP32)
@@ -61,7 +61,7 @@ SMALL = [
 def test_small_cases_full_parity(case):
     log(f"case {case}")
     inp = synth.random_case(**case)
-    run = GpuRun(inp, 0.0625)
+    run = DeviceRun(inp, 0.0625)
     check_preprocess_exact(inp.routes, case["Skv"], run.routes)
     _full_compare(inp, 0.0625, run)
 
@@ -88,7 +88,7 @@ TILED = [
 def test_full_tile_cases_parity(case):
     log(f"case {case}")
     inp = synth.tiled_case(**case)
-    run = GpuRun(inp, 0.0625)
+    run = DeviceRun(inp, 0.0625)
     check_preprocess_exact(inp.routes, case["Skv"], run.routes)
     _full_compare(inp, 0.0625, run)
 
@@ -96,11 +96,11 @@ def test_full_tile_cases_parity(case):
 def test_int64_routes_huge_values_match_int32():
     inp = synth.random_case(41, 1, 150, 140, 12, 1, 30, route_dtype=np.int64)
     log("int64 routes with values beyond 2^31")
-    run = GpuRun(inp, 0.1)
+    run = DeviceRun(inp, 0.1)
     check_preprocess_exact(inp.routes, 140, run.routes)
     _full_compare(inp, 0.1, run)
     r32 = np.where((inp.routes >= 0) & (inp.routes < 140), inp.routes, -1).astype(np.int32)
-    run32 = GpuRun(inp, 0.1, routes=r32)
+    run32 = DeviceRun(inp, 0.1, routes=r32)
     for a, b in ((run.out32, run32.out32), (run.lse, run32.lse), (run.dq, run32.dq),
                  (run.dk, run32.dk), (run.dv, run32.dv)):
         assert torch.equal(a, b)
@@ -110,7 +110,7 @@ def test_tiny_workload_full_parity():
     wl = synth.WORKLOADS[1]
     log(f"workload {wl.name}")
     inp = synth.make_inputs(wl)
-    run = GpuRun(inp, wl.scale)
+    run = DeviceRun(inp, wl.scale)
     check_preprocess_exact(inp.routes, wl.Skv, run.routes)
     _full_compare(inp, wl.scale, run)
 
@@ -143,7 +143,7 @@ def test_full_size_workload_parity(idx):
     wl = synth.WORKLOADS[idx]
     log(f"workload {wl.name}: generating")
     inp = synth.make_inputs(wl)
-    run = GpuRun(inp, wl.scale)
+    run = DeviceRun(inp, wl.scale)
     log("  preprocess check")
     check_preprocess_exact(inp.routes, wl.Skv, run.routes)
     P = oracle.Problem(inp.q, inp.k, inp.v, inp.routes, wl.scale, inp.grad_out)
@@ -175,7 +175,7 @@ def test_full_size_workload_parity(idx):
 
 def test_route_order_duplicates_invalid_ids_bitwise():
     inp = synth.random_case(51, 1, 260, 300, 12, 1, 48)
-    base = GpuRun(inp, 0.0625, deterministic=True)
+    base = DeviceRun(inp, 0.0625, deterministic=True)
     rng = np.random.default_rng(9)
     perm = np.take_along_axis(inp.routes,
                               rng.permuted(np.tile(np.arange(48), (1, 260, 1)), axis=2), 2)
@@ -189,7 +189,7 @@ def test_route_order_duplicates_invalid_ids_bitwise():
     bad[bad == -1] = 300
     bad[0, ::2][bad[0, ::2] == 300] = -77
     for name, r in (("permuted", perm), ("duplicated", dup), ("invalid", bad)):
-        other = GpuRun(inp, 0.0625, routes=r, deterministic=True)
+        other = DeviceRun(inp, 0.0625, routes=r, deterministic=True)
         for a, b in ((base.out, other.out), (base.out32, other.out32), (base.lse, other.lse),
                      (base.dq, other.dq), (base.dk, other.dk), (base.dv, other.dv)):
             assert torch.equal(a, b), name
@@ -200,8 +200,8 @@ def test_run_to_run_bitwise_determinism():
     # QSA_FLAG_DETERMINISTIC: every walk starts at the head of its key list.
     wl = synth.WORKLOADS[2]
     inp = synth.make_inputs(wl)
-    a = GpuRun(inp, wl.scale, deterministic=True)
-    b = GpuRun(inp, wl.scale, deterministic=True)
+    a = DeviceRun(inp, wl.scale, deterministic=True)
+    b = DeviceRun(inp, wl.scale, deterministic=True)
     for x, y in ((a.out32, b.out32), (a.lse, b.lse), (a.dq, b.dq), (a.dk, b.dk), (a.dv, b.dv)):
         assert torch.equal(x, y)
 
@@ -214,8 +214,8 @@ def test_default_walks_match_deterministic_walks():
     # chunk walked twice or skipped would miss it by orders of magnitude.
     wl = synth.WORKLOADS[3]
     inp = synth.make_inputs(wl)
-    a = GpuRun(inp, wl.scale, deterministic=True)
-    b = GpuRun(inp, wl.scale)
+    a = DeviceRun(inp, wl.scale, deterministic=True)
+    b = DeviceRun(inp, wl.scale)
     assert not torch.equal(a.out32, b.out32)  # the walks were rotated
     for name, x, y in (("out_fp32", a.out32, b.out32), ("lse", a.lse, b.lse)):
         x = x.double()
@@ -239,7 +239,7 @@ def test_nan_in_unselected_kv_does_not_leak():
     inp = synth.random_case(61, 1, 100, 120, 12, 1, 20)
     r = inp.routes.copy()
     r[(r >= 100) & (r < 120)] = -1                   # keys 100.. selected by nobody
-    base = GpuRun(inp, 0.0625, routes=r)
+    base = DeviceRun(inp, 0.0625, routes=r)
     k = inp.k.copy()
     v = inp.v.copy()
     k[0, 100:] = 0x7FC0                              # NaN
@@ -248,7 +248,7 @@ def test_nan_in_unselected_kv_does_not_leak():
     empty = np.nonzero(~((r >= 0) & (r < 120)).any(-1)[0])[0]
     q[0, empty] = 0x7FC0                             # Q of padding rows is irrelevant
     nan_inp = synth.Inputs(inp.wl, r, q, k, v, inp.grad_out, {})
-    other = GpuRun(nan_inp, 0.0625)
+    other = DeviceRun(nan_inp, 0.0625)
     for a, b in ((base.out32, other.out32), (base.lse, other.lse), (base.dq, other.dq),
                  (base.dv, other.dv)):
         assert torch.equal(a, b)
@@ -283,7 +283,7 @@ def test_membership_offsets_beyond_int32():
     q = synth.bf16_bits(rng.standard_normal((1, Sq, 12, 256), dtype=np.float32))
     kv = synth.bf16_bits(rng.standard_normal((1, Skv, 1, 256), dtype=np.float32))
     inp = synth.Inputs(None, routes, q, kv, kv, None, {})
-    run = GpuRun(inp, 0.0625, backward=False)
+    run = DeviceRun(inp, 0.0625, backward=False)
     Pr = oracle.Problem(q, kv, kv, routes, 0.0625)
     rows = tail[-40:]
     o_ref, l_ref = Pr.forward(rows)
