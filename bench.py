@@ -6,15 +6,24 @@ call, as the cuDNN Frontend QSA page's "Support and execution" section asks for
 benchmarks). Outputs and workspaces are allocated before the timed region.
 
 Prints one JSON line:
-  value      sparse TFLOP/s = (4 + 10) * Hq * 256 * nnz / step time, with nnz the
-             number of distinct valid (query, key) pairs of the routes
-  roofline   the longest-running kernel: algorithmic FLOP per launch / its
-             average duration measured with HIP events on its own stream,
-             against the MI355X dense bf16 MFMA peak; `traffic` is its HBM
-             bytes per launch from the committed rocprofv3 counter summary
-             (profiles/traffic_<workload>.txt), null once the kernels changed
-  cpu_baseline  the FP64 oracle on a bounded sample of the same workload,
-             on this host's cores, scaled to TFLOP/s
+  value      sparse TFLOP/s = (4 + 10) * Hq * 256 * nnz / step time (wall clock
+             over the timed steps), with nnz the number of distinct valid
+             (query, key) pairs of the routes
+  roofline   the longest-running kernel, on its counted work: forward 4d, dQ 6d
+             (S, dP, dQ), dK/dV 4d (dV, dK; its S and dP are recomputed and
+             counted once, in dQ) FLOP per (pair, head), against the dense bf16
+             MFMA peak; and its HBM bytes (calibrated rocprofv3 FETCH_SIZE +
+             WRITE_SIZE from the committed summary, null once the kernels
+             changed) per average launch time against 8 TB/s. `bound` is the
+             larger of the two fractions. Gathered kernels also report
+             `gather`: their staged bytes per unit of work (1 KB of K/V per
+             pair in the forward and dQ, 12 KB of Q/dO per (query, key tile)
+             in dK/dV) per launch time, against the staging rate a
+             direct-to-LDS probe of the same access shape reaches from L2
+             (measured in the same run)
+  cpu_baseline  the FP64 oracle (forward + full backward) on a bounded sample
+             of the same workload, on all of this host's cores, scaled to
+             TFLOP/s
 """
 from __future__ import annotations
 
@@ -34,17 +43,26 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "QSA fwd+bwd sparse TFLOP/s (12Q/1KV, d=256) and % of MFMA peak, 1 GPU"
 
-# Algorithmic FLOP per (distinct valid pair, query head), by kernel, and which
-# pairs each kernel computes: "partial" = pairs outside full 128 x 128 tiles
-# (gathered kernels), "full" = pairs inside them (dense kernels).
+# Counted FLOP per (distinct valid pair, query head), by kernel: the method's
+# forward (S = QK^T, O = PV) and its five backward products (S, dP, dV, dK, dQ)
+# each counted once. The dK/dV kernels recompute S and dP (executed 8d), which
+# the dQ kernels have already been credited with. Which pairs each kernel
+# computes: "partial" = pairs outside full 128 x 128 tiles (gathered kernels),
+# "full" = pairs inside them (dense kernels).
 FLOP_PER_PAIR_HEAD = {
     "forward": 4 * 256,        # S = QK^T and O = PV
     "forward_dense": 4 * 256,
     "dq": 6 * 256,             # S, dP = dO V^T, dQ = dS K
     "dq_dense": 6 * 256,
-    "dkdv": 8 * 256,           # S, dP, dV = P^T dO, dK = dS^T Q
-    "dkdv_dense": 8 * 256,
+    "dkdv": 4 * 256,           # dV = P^T dO, dK = dS^T Q
+    "dkdv_dense": 4 * 256,
 }
+EXECUTED_PER_PAIR_HEAD = dict(FLOP_PER_PAIR_HEAD, dkdv=8 * 256, dkdv_dense=8 * 256)
+# Staged bytes per unit of work of the gathered kernels: K and V rows (512 B
+# each) per (query, key) pair; Q and dO rows (12 heads x 512 B each) per
+# (query, partial 128-key tile).
+GATHER_UNIT = {"forward": ("pair", 1024, 512), "dq": ("pair", 1024, 512),
+               "dkdv": ("query_keytile", 12 * 1024, 6144)}
 KERNEL_PAIRS = {"forward": "partial", "forward_dense": "full", "dq": "partial",
                 "dq_dense": "full", "dkdv": "partial", "dkdv_dense": "full"}
 COUNTED_FWD = 4 * 256
@@ -81,6 +99,30 @@ def full_tile_pairs(routes: np.ndarray, Sq: int, Skv: int) -> int:
             rows = np.broadcast_to(np.arange(a, a + c.shape[0])[:, None] // 128, s.shape)
             np.add.at(cnt, (rows[keep], s[keep] // 128), 1)
         total += int((cnt == 128 * 128).sum()) * 128 * 128
+    return total
+
+
+def partial_tile_hits(routes: np.ndarray, Sq: int, Skv: int) -> int:
+    """(query row, key tile) pairs where the row selects a key of the tile and the
+    tile is not full: the units of the gathered dK/dV."""
+    B = routes.shape[0]
+    nQT, nKT = (Sq + 127) // 128, (Skv + 127) // 128
+    total = 0
+    for b in range(B):
+        r = routes[b]
+        hit = np.zeros((Sq, nKT), bool)
+        cnt = np.zeros((nQT, nKT), np.int64)
+        for a in range(0, Sq, 1024):
+            c = r[a:a + 1024].astype(np.int64)
+            s = np.sort(np.where((c >= 0) & (c < Skv), c, -1), axis=-1)
+            keep = s >= 0
+            keep[:, 1:] &= s[:, 1:] != s[:, :-1]
+            rows = np.broadcast_to(np.arange(a, a + c.shape[0])[:, None], s.shape)
+            hit[rows[keep], s[keep] // 128] = True
+            np.add.at(cnt, (rows[keep] // 128, s[keep] // 128), 1)
+        full = cnt == 128 * 128
+        hit &= ~full[np.arange(Sq) // 128]
+        total += int(hit.sum())
     return total
 
 
@@ -143,28 +185,74 @@ class Events:
         return ms.value
 
 
+def host_cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, wl, nnz_row: np.ndarray, seconds: float) -> dict:
-    """The oracle (fwd + full bwd of a sample of query rows), timed on host cores."""
+    """The oracle (forward + full backward of a sample of query rows), timed on all
+    host cores (its row loop is split over OpenMP threads)."""
     import oracle
     P = oracle.Problem(inp.q, inp.k, inp.v, inp.routes, wl.scale, inp.grad_out)
+    threads = oracle.num_threads()
     rng = np.random.default_rng(0)
     rows_all = np.nonzero(nnz_row > 0)[0]
-    # calibrate on a few rows, then size the sample to the time budget
-    probe = rng.choice(rows_all, min(4, len(rows_all)), replace=False)
+    # calibrate on one row per thread, then size the sample to the time budget
+    probe = np.sort(rng.choice(rows_all, min(threads, len(rows_all)), replace=False))
     t = time.perf_counter()
     P.backward_rows(probe)
-    per_row = (time.perf_counter() - t) / len(probe)
-    n = int(max(4, min(len(rows_all), seconds / max(per_row, 1e-9))))
+    per_round = time.perf_counter() - t
+    n = int(max(threads, min(len(rows_all), threads * seconds / max(per_round, 1e-9))))
     rows = np.sort(rng.choice(rows_all, n, replace=False))
     t = time.perf_counter()
     P.backward_rows(rows)
     dt = time.perf_counter() - t
     flop = (COUNTED_FWD + COUNTED_BWD) * wl.Hq * float(nnz_row[rows].sum())
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"forward + full backward (dq and the rows' dk/dv contributions) of {n} "
                       f"random query rows of {wl.name} ({int(nnz_row[rows].sum())} pairs), "
-                      f"FP64 C oracle, one thread, {dt:.1f} s",
-            "host_threads_available": os.cpu_count()}
+                      f"FP64 C oracle, {threads} OpenMP threads, {dt:.1f} s",
+            "nproc": os.cpu_count(), "cpu_model": host_cpu_model()}
+
+
+def gather_ceiling(torch, lib, hip, stream, row_bytes: int, footprint_bytes: int,
+                   n_items: int = 1 << 21) -> float:
+    """Staging rate (GB/s) of the direct-to-LDS probe: rows of `row_bytes` drawn
+    uniformly from a footprint of `footprint_bytes`, 8192 work groups of 4 waves."""
+    dev = torch.device("cuda:0")
+    nrows = max(2, footprint_bytes // row_bytes)
+    src = torch.zeros(nrows * row_bytes, dtype=torch.uint8, device=dev)
+    per_item = 2 if row_bytes == 512 else 1
+    g = torch.Generator(device="cpu").manual_seed(7)
+    idx = torch.randint(0, nrows, (n_items * per_item,), generator=g, dtype=torch.int32).to(dev)
+    ev = Events(hip, 2)
+    lib.qsa_bench_gather.restype = ctypes.c_int
+    lib.qsa_bench_gather.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                     ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_void_p]
+
+    def run():
+        st = lib.qsa_bench_gather(src.data_ptr(), src.numel(), idx.data_ptr(), idx.numel(),
+                                  row_bytes, 8192, stream)
+        assert st == 0, st
+
+    run()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(3):
+        hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), ctypes.c_void_p(stream))
+        run()
+        hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), ctypes.c_void_p(stream))
+        torch.cuda.synchronize()
+        ms = ev.elapsed(0, 1)
+        best = ms if best is None else min(best, ms)
+    return n_items * 1024 / (best * 1e-3) / 1e9
 
 
 def main() -> int:
@@ -180,6 +268,8 @@ def main() -> int:
                     help="set QSA_FLAG_DETERMINISTIC (head-first key walks, bitwise reproducible)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--calibrate-gather", action="store_true",
+                    help="print the direct-to-LDS staging rates of the gather probe and exit")
     args = ap.parse_args()
     if args.calibrate_copy:
         import torch
@@ -198,6 +288,20 @@ def main() -> int:
     import torch
     from token_indexed_sparse_amd import qsa, synth
 
+    lib = qsa.library()
+    hip = hip_runtime()
+    hip.hipEventRecord.restype = ctypes.c_int
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    if args.calibrate_gather:
+        rows = []
+        for rb, fp in ((512, 2 << 20), (512, 32 << 20), (6144, 2 << 20), (6144, 24 << 20),
+                       (6144, 384 << 20)):
+            gbs = gather_ceiling(torch, lib, hip, stream, rb, fp)
+            rows.append({"row_bytes": rb, "footprint_bytes": fp, "GB/s": gbs})
+            print(json.dumps(rows[-1]), flush=True)
+        return 0
+
     wl = None
     for idx, w in synth.WORKLOADS.items():
         if args.workload in (w.name, str(idx)):
@@ -210,6 +314,8 @@ def main() -> int:
     nnz = int(nnz_row.sum())
     nnz_full = full_tile_pairs(inp.routes, wl.Sq, wl.Skv)
     pairs = {"all": nnz, "full": nnz_full, "partial": nnz - nnz_full}
+    units = {"pair": pairs["partial"],
+             "query_keytile": partial_tile_hits(inp.routes, wl.Sq, wl.Skv)}
 
     dev = torch.device("cuda:0")
 
@@ -226,7 +332,6 @@ def main() -> int:
                          deterministic=args.deterministic)
     ws_f = torch.empty(qsa.forward_workspace_bytes(dims), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(qsa.backward_workspace_bytes(dims), dtype=torch.uint8, device=dev)
-    lib = qsa.library()
     lib.qsa_forward_timed.restype = ctypes.c_int
     lib.qsa_forward_timed.argtypes = [ctypes.POINTER(qsa.Dims)] + [ctypes.c_void_p] * 4 + [
         ctypes.c_float] + [ctypes.c_void_p] * 3 + [ctypes.c_void_p, ctypes.c_size_t,
@@ -237,8 +342,6 @@ def main() -> int:
         ctypes.c_float] + [ctypes.c_void_p] * 3 + [ctypes.c_void_p, ctypes.c_size_t,
                                                    ctypes.c_void_p, ctypes.c_void_p,
                                                    ctypes.c_int32]
-    hip = hip_runtime()
-    stream = torch.cuda.current_stream().cuda_stream
     K, W = args.steps, args.warmup
     NF, NB = len(FWD_STAGES), len(BWD_STAGES)
     fev = [Events(hip, NF + 1) for _ in range(K)]
@@ -275,28 +378,71 @@ def main() -> int:
         stage_ms[name] = float(np.mean([e.elapsed(a, a + 1) for e in fev]))
     for a, name in enumerate(BWD_STAGES):
         stage_ms[name] = float(np.mean([e.elapsed(a, a + 1) for e in bev]))
-    fwd_ms = float(np.mean([e.elapsed(0, NF) for e in fev]))
-    bwd_ms = float(np.mean([e.elapsed(0, NB) for e in bev]))
+    fwd_each = np.array([e.elapsed(0, NF) for e in fev])
+    bwd_each = np.array([e.elapsed(0, NB) for e in bev])
+    step_each = fwd_each + bwd_each   # event-timed forward + backward of each step
+    fwd_ms = float(np.mean(fwd_each))
+    bwd_ms = float(np.mean(bwd_each))
     flop_fwd = COUNTED_FWD * wl.Hq * nnz
     flop_bwd = COUNTED_BWD * wl.Hq * nnz
     value = (flop_fwd + flop_bwd) / (ms_step * 1e-3) / 1e12
 
-    dom = max(KERNEL_PAIRS, key=lambda s: stage_ms[s])
-    dom_flop = FLOP_PER_PAIR_HEAD[dom] * wl.Hq * pairs[KERNEL_PAIRS[dom]]
-    achieved = dom_flop / (stage_ms[dom] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": measured_traffic(wl.name, dom),
-                "flop_per_launch": dom_flop, "avg_launch_ms": stage_ms[dom]}
+    # gather ceilings: the probe's staging rate for each access shape from an
+    # L2-resident footprint (2 MB per shape)
+    print("[bench] gather probe", file=sys.stderr, flush=True)
+    ceiling = {rb: gather_ceiling(torch, lib, hip, stream, rb, 2 << 20) for rb in (512, 6144)}
 
-    # algorithmic HBM bytes of one step (each tensor once per call, membership once per call)
+    def kernel_roofline(name):
+        ms = stage_ms[name]
+        flop = FLOP_PER_PAIR_HEAD[name] * wl.Hq * pairs[KERNEL_PAIRS[name]]
+        tflops = flop / (ms * 1e-3) / 1e12
+        traffic = measured_traffic(wl.name, name)
+        r = {"kernel": name, "avg_launch_ms": ms,
+             "mfma": {"achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                      "frac": tflops / PEAK_BF16_TFLOPS, "counted_flop_per_launch": flop,
+                      "executed_flop_per_launch":
+                          EXECUTED_PER_PAIR_HEAD[name] * wl.Hq * pairs[KERNEL_PAIRS[name]]},
+             "traffic": traffic}
+        if traffic is not None:
+            gbs = traffic / (ms * 1e-3) / 1e9
+            r["hbm"] = {"achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": gbs / PEAK_HBM_GBS,
+                        "note": "FETCH_SIZE counts fetches beyond L2; the last-level cache "
+                                "(MALL) may serve part of them"}
+        if name in GATHER_UNIT:
+            unit, nbytes, rb = GATHER_UNIT[name]
+            staged = nbytes * units[unit]
+            gbs = staged / (ms * 1e-3) / 1e9
+            r["gather"] = {"achieved": gbs, "peak": ceiling[rb], "unit": "GB/s",
+                           "frac": gbs / ceiling[rb], "unit_of_work": unit,
+                           "bytes_per_unit": nbytes, "units_per_launch": units[unit],
+                           "staged_bytes_per_launch": staged,
+                           "peak_source": f"direct-to-LDS probe, {rb}-byte rows, 2 MB footprint"}
+        return r
+
+    per_kernel = {n: kernel_roofline(n) for n in KERNEL_PAIRS}
+    dom = max(KERNEL_PAIRS, key=lambda s: stage_ms[s])
+    d = per_kernel[dom]
+    use_hbm = "hbm" in d and d["hbm"]["frac"] > d["mfma"]["frac"]
+    main_part = d["hbm"] if use_hbm else d["mfma"]
+    roofline = {"bound": "hbm" if use_hbm else "mfma", "kernel": dom,
+                "achieved": main_part["achieved"], "peak": main_part["peak"],
+                "unit": main_part["unit"], "frac": main_part["frac"], "traffic": d["traffic"],
+                "avg_launch_ms": d["avg_launch_ms"], "mfma": d["mfma"]}
+    for key in ("hbm", "gather"):
+        if key in d:
+            roofline[key] = d[key]
+
+    # algorithmic HBM bytes of one step (each tensor once per call; the backward
+    # also writes and reads its bit-packed membership once)
     Bq = wl.B * wl.Sq * wl.Hq * wl.D
     Bk = wl.B * wl.Skv * wl.Hkv * wl.D
-    memb = wl.B * wl.Sq * (-(-wl.Skv // 128) * 128)
+    mbits = wl.B * wl.Sq * (-(-wl.Skv // 128) * 128) // 8
     rt = inp.routes.nbytes
-    fwd_bytes = rt + memb + 2 * Bq + 2 * 2 * Bk + 2 * Bq + 4 * Bq + 4 * wl.B * wl.Hq * wl.Sq
-    bwd_bytes = (rt + memb + 2 * Bq + 2 * 2 * Bk + 2 * Bq + 4 * Bq + 4 * wl.B * wl.Hq * wl.Sq
-                 + 2 * 4 * wl.B * wl.Hq * wl.Sq + 2 * Bq + 2 * 2 * Bk)
+    lse_b = 4 * wl.B * wl.Hq * wl.Sq
+    fwd_bytes = rt + 2 * Bq + 2 * 2 * Bk + 2 * Bq + 4 * Bq + lse_b
+    bwd_bytes = (rt + 2 * mbits + 2 * Bq + 2 * 2 * Bk + 2 * Bq + 4 * Bq + lse_b + 2 * lse_b
+                 + 2 * Bq + 2 * 2 * Bk)
 
     res = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
@@ -304,14 +450,20 @@ def main() -> int:
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "Sq": wl.Sq, "Skv": wl.Skv, "Hq": wl.Hq,
                    "Hkv": wl.Hkv, "D": wl.D, "W": wl.W, "nnz_pairs": nnz, "full_tile_pairs": nnz_full,
+                   "partial_query_keytile_pairs": units["query_keytile"],
                    "flop_per_step": flop_fwd + flop_bwd, "parallelism": "single GPU",
                    "deterministic": bool(args.deterministic)},
         "mfma_peak_frac": value / PEAK_BF16_TFLOPS,
+        "step_ms_events": {"median": float(np.median(step_each)), "min": float(np.min(step_each)),
+                           "mean": float(np.mean(step_each))},
         "forward_tflops": flop_fwd / (fwd_ms * 1e-3) / 1e12,
         "backward_tflops": flop_bwd / (bwd_ms * 1e-3) / 1e12,
         "stage_ms": stage_ms,
         "algorithmic_hbm_gbs": (fwd_bytes + bwd_bytes) / (ms_step * 1e-3) / 1e9,
+        "gather_ceiling_gbs": {str(k): v for k, v in ceiling.items()},
         "roofline": roofline,
+        "kernels": {n: {k2: v2 for k2, v2 in r.items() if k2 != "kernel"}
+                    for n, r in per_kernel.items()},
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -42,7 +42,8 @@ class _Problem(ctypes.Structure):
                 ("W", ctypes.c_int64), ("route_is_i64", ctypes.c_int32), ("pad_", ctypes.c_int32),
                 ("scale", ctypes.c_double), ("routes", ctypes.c_void_p),
                 ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
-                ("dout", ctypes.c_void_p)]
+                ("dout", ctypes.c_void_p), ("o_saved", ctypes.c_void_p),
+                ("lse_saved", ctypes.c_void_p)]
 
 
 def _load():
@@ -65,7 +66,7 @@ def _load():
         lib.orc_backward_dkdv.restype = None
         lib.orc_backward_dkdv.argtypes = [ctypes.POINTER(_Problem), I, P, P, P]
         lib.orc_backward_rows.restype = None
-        lib.orc_backward_rows.argtypes = [ctypes.POINTER(_Problem), I, P, P, P, P]
+        lib.orc_backward_rows.argtypes = [ctypes.POINTER(_Problem), I, P, P, P, P, P, P]
         lib.orc_num_threads.restype = ctypes.c_int32
         _lib = lib
     return _lib
@@ -154,9 +155,27 @@ class Problem:
         self.B, self.Sq, self.Skv, self.Hq, self.Hkv, self.D = B, Sq, Skv, Hq, Hkv, D
         self.W = self.routes.shape[2]
         self.scale = float(scale)
+        self.o_saved = self.lse_saved = None
         self._c = _Problem(B, Sq, Skv, Hq, Hkv, D, self.W, self.i64, 0, self.scale,
                            _ptr(self.routes), _ptr(self.q), _ptr(self.k), _ptr(self.v),
-                           _ptr(self.dout) if self.dout is not None else 0)
+                           _ptr(self.dout) if self.dout is not None else 0, 0, 0)
+
+    def use_saved(self, out, lse) -> "Problem":
+        """Make the backward take this O ``[B, Sq, Hq, D]`` and LSE ``[B, Hq, Sq]`` (for
+        instance a GPU forward's out_fp32 and lse) instead of the oracle's own forward;
+        ``None`` restores the oracle's own."""
+        if out is None:
+            self.o_saved = self.lse_saved = None
+            self._c.o_saved = self._c.lse_saved = 0
+            return self
+        out = np.ascontiguousarray(out, dtype=np.float64)
+        lse = np.ascontiguousarray(lse, dtype=np.float64)
+        if out.shape != (self.B, self.Sq, self.Hq, self.D) or lse.shape != (self.B, self.Hq,
+                                                                              self.Sq):
+            raise ValueError("saved out must be [B, Sq, Hq, D] and lse [B, Hq, Sq]")
+        self.o_saved, self.lse_saved = out, lse
+        self._c.o_saved, self._c.lse_saved = _ptr(out), _ptr(lse)
+        return self
 
     def _rows(self, rows: Optional[np.ndarray]) -> np.ndarray:
         if rows is None:
@@ -205,8 +224,26 @@ class Problem:
         dk = np.empty((self.B, self.Skv, self.Hkv, self.D), np.float64)
         dv = np.empty_like(dk)
         _load().orc_backward_rows(ctypes.byref(self._c), rows.shape[0], _ptr(rows), _ptr(dq),
-                                  _ptr(dk), _ptr(dv))
+                                  _ptr(dk), _ptr(dv), None, None)
         return dq, dk, dv
+
+    def all_outputs(self):
+        """Forward and full backward in one pass over every row:
+        out [B, Sq, Hq, D], lse [B, Hq, Sq], dq [B, Sq, Hq, D], dk, dv [B, Skv, Hkv, D]."""
+        if self.dout is None:
+            raise ValueError("grad_out missing")
+        rows = self._rows(None)
+        n = rows.shape[0]
+        out = np.empty((n, self.Hq, self.D), np.float64)
+        lse = np.empty((n, self.Hq), np.float64)
+        dq = np.empty((n, self.Hq, self.D), np.float64)
+        dk = np.empty((self.B, self.Skv, self.Hkv, self.D), np.float64)
+        dv = np.empty_like(dk)
+        _load().orc_backward_rows(ctypes.byref(self._c), n, _ptr(rows), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), _ptr(out), _ptr(lse))
+        shp = (self.B, self.Sq, self.Hq, self.D)
+        return (out.reshape(shp), lse.reshape(self.B, self.Sq, self.Hq).transpose(0, 2, 1).copy(),
+                dq.reshape(shp), dk, dv)
 
     def backward_full(self):
         """dq [B, Sq, Hq, D], dk, dv [B, Skv, Hkv, D]."""

@@ -50,6 +50,11 @@ typedef struct {
     double scale;
     const void *routes;
     const double *q, *k, *v, *dout;
+    /* Saved forward state for the backward, or NULL: out [B, Sq, Hq, D] and
+     * lse [B, Hq, Sq]. The backward equations take O and LSE as inputs (the
+     * forward's FP32 output and LSE); when these are NULL the oracle uses the
+     * O and LSE of its own FP64 forward. */
+    const double *o_saved, *lse_saved;
 } orc_problem;
 
 static int cmp_i64(const void *a, const void *b)
@@ -210,8 +215,18 @@ void orc_forward(const orc_problem *P, int64_t nrows, const int64_t *rows, doubl
     }
 }
 
+/* Replace the row's O [Hq, D] and lse [Hq] by the saved ones, when given. */
+static void use_saved(const orc_problem *P, int64_t b, int64_t i, double *o, double *lse)
+{
+    if (!P->o_saved) return;
+    const int64_t Hq = P->Hq, D = P->D;
+    for (int64_t x = 0; x < Hq * D; ++x) o[x] = P->o_saved[(b * P->Sq + i) * Hq * D + x];
+    for (int64_t h = 0; h < Hq; ++h) lse[h] = P->lse_saved[(b * Hq + h) * P->Sq + i];
+}
+
 /*
- * Backward terms of one row: with the row's own O and lse, for each key of R
+ * Backward terms of one row: with the row's O and lse (its own forward's, or
+ * the saved ones), for each key of R
  * and each head, p = exp(s - lse), dp = <dO, v>, ds = p (dp - delta).
  * Accumulates dq [Hq, D] (zeroed here) unless dq is NULL. When dk/dv are given ([nsel, Hkv, D]),
  * also adds the row's contributions to the selected keys sel[0..nsel) of batch b.
@@ -222,6 +237,7 @@ static void backward_row(const orc_problem *P, int64_t b, int64_t i, const int64
 {
     const int64_t D = P->D, Hq = P->Hq, Hkv = P->Hkv, G = Hq / Hkv;
     forward_row(P, b, i, keys, n, s, o, lse);
+    use_saved(P, b, i, o, lse);
     if (dq)
         for (int64_t x = 0; x < Hq * D; ++x) dq[x] = 0.0;
     if (n == 0) return;
@@ -336,50 +352,86 @@ void orc_backward_dkdv(const orc_problem *P, int64_t nkeys, const int64_t *keys_
 /*
  * Whole backward restricted to a set of query rows: dq of those rows and their
  * contributions to every dk, dv ([B, Skv, Hkv, D], zeroed here). With all rows
- * listed this is the full backward. Rows are visited in list order, one thread.
+ * listed this is the full backward. out [nrows, Hq, D] and lse [nrows, Hq],
+ * when not NULL, receive the rows' forward results (the oracle's own forward,
+ * also when the backward runs on saved state). The rows are split over the threads in
+ * contiguous blocks; each thread adds its rows' dk, dv terms in list order
+ * into a sum of its own, and the threads' sums are added in thread order.
  */
 void orc_backward_rows(const orc_problem *P, int64_t nrows, const int64_t *rows, double *dq,
-                       double *dk, double *dv)
+                       double *dk, double *dv, double *out, double *lse_out)
 {
     const int64_t D = P->D, Hq = P->Hq, Hkv = P->Hkv, G = Hq / Hkv;
     const int64_t W1 = P->W > 0 ? P->W : 1;
-    memset(dk, 0, sizeof(double) * (size_t)(P->B * P->Skv * Hkv * D));
-    memset(dv, 0, sizeof(double) * (size_t)(P->B * P->Skv * Hkv * D));
-    int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)W1);
-    double *s = (double *)malloc(sizeof(double) * (size_t)W1);
-    double *o = (double *)malloc(sizeof(double) * (size_t)(Hq * D));
-    double *lse = (double *)malloc(sizeof(double) * (size_t)Hq);
-    for (int64_t t = 0; t < nrows; ++t) {
-        const int64_t row = rows[t], b = row / P->Sq, i = row % P->Sq;
-        const int64_t n = route_set_raw(P->routes, P->route_is_i64, P->W, P->Skv, row, keys);
-        double *dqr = dq + t * Hq * D;
-        forward_row(P, b, i, keys, n, s, o, lse);
-        for (int64_t x = 0; x < Hq * D; ++x) dqr[x] = 0.0;
-        for (int64_t h = 0; h < Hq && n > 0; ++h) {
-            const int64_t g = h / G;
-            const double *qh = P->q + ((b * P->Sq + i) * Hq + h) * D;
-            const double *doh = P->dout + ((b * P->Sq + i) * Hq + h) * D;
-            const double delta = dot(doh, o + h * D, D);
-            for (int64_t u = 0; u < n; ++u) {
-                const int64_t j = keys[u];
-                const double *kj = P->k + ((b * P->Skv + j) * Hkv + g) * D;
-                const double *vj = P->v + ((b * P->Skv + j) * Hkv + g) * D;
-                const double p = exp(P->scale * dot(qh, kj, D) - lse[h]);
-                const double ds = p * (dot(doh, vj, D) - delta);
-                double *dkj = dk + ((b * P->Skv + j) * Hkv + g) * D;
-                double *dvj = dv + ((b * P->Skv + j) * Hkv + g) * D;
-                for (int64_t d = 0; d < D; ++d) {
-                    dqr[h * D + d] += P->scale * ds * kj[d];
-                    dkj[d] += P->scale * ds * qh[d];
-                    dvj[d] += p * doh[d];
+    const int64_t per = P->B * P->Skv * Hkv * D;
+    memset(dk, 0, sizeof(double) * (size_t)per);
+    memset(dv, 0, sizeof(double) * (size_t)per);
+    int nthreads = 1;
+#ifdef _OPENMP
+    nthreads = omp_get_max_threads();
+    if (nthreads > nrows) nthreads = nrows > 0 ? (int)nrows : 1;
+#endif
+    double *acc_k = nthreads > 1 ? (double *)calloc((size_t)(per * nthreads), sizeof(double)) : dk;
+    double *acc_v = nthreads > 1 ? (double *)calloc((size_t)(per * nthreads), sizeof(double)) : dv;
+#pragma omp parallel num_threads(nthreads)
+    {
+        int tid = 0;
+#ifdef _OPENMP
+        tid = omp_get_thread_num();
+#endif
+        double *tk = acc_k + (nthreads > 1 ? tid * per : 0);
+        double *tv = acc_v + (nthreads > 1 ? tid * per : 0);
+        int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)W1);
+        double *s = (double *)malloc(sizeof(double) * (size_t)W1);
+        double *o = (double *)malloc(sizeof(double) * (size_t)(Hq * D));
+        double *lse = (double *)malloc(sizeof(double) * (size_t)Hq);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < nrows; ++t) {
+            const int64_t row = rows[t], b = row / P->Sq, i = row % P->Sq;
+            const int64_t n = route_set_raw(P->routes, P->route_is_i64, P->W, P->Skv, row, keys);
+            double *dqr = dq + t * Hq * D;
+            forward_row(P, b, i, keys, n, s, o, lse);
+            if (out)
+                for (int64_t x = 0; x < Hq * D; ++x) out[t * Hq * D + x] = o[x];
+            if (lse_out)
+                for (int64_t h = 0; h < Hq; ++h) lse_out[t * Hq + h] = lse[h];
+            use_saved(P, b, i, o, lse);
+            for (int64_t x = 0; x < Hq * D; ++x) dqr[x] = 0.0;
+            for (int64_t h = 0; h < Hq && n > 0; ++h) {
+                const int64_t g = h / G;
+                const double *qh = P->q + ((b * P->Sq + i) * Hq + h) * D;
+                const double *doh = P->dout + ((b * P->Sq + i) * Hq + h) * D;
+                const double delta = dot(doh, o + h * D, D);
+                for (int64_t u = 0; u < n; ++u) {
+                    const int64_t j = keys[u];
+                    const double *kj = P->k + ((b * P->Skv + j) * Hkv + g) * D;
+                    const double *vj = P->v + ((b * P->Skv + j) * Hkv + g) * D;
+                    const double p = exp(P->scale * dot(qh, kj, D) - lse[h]);
+                    const double ds = p * (dot(doh, vj, D) - delta);
+                    double *dkj = tk + ((b * P->Skv + j) * Hkv + g) * D;
+                    double *dvj = tv + ((b * P->Skv + j) * Hkv + g) * D;
+                    for (int64_t d = 0; d < D; ++d) {
+                        dqr[h * D + d] += P->scale * ds * kj[d];
+                        dkj[d] += P->scale * ds * qh[d];
+                        dvj[d] += p * doh[d];
+                    }
                 }
             }
         }
+        free(keys);
+        free(s);
+        free(o);
+        free(lse);
     }
-    free(keys);
-    free(s);
-    free(o);
-    free(lse);
+    if (nthreads > 1) {
+        for (int t = 0; t < nthreads; ++t)
+            for (int64_t x = 0; x < per; ++x) {
+                dk[x] += acc_k[t * per + x];
+                dv[x] += acc_v[t * per + x];
+            }
+        free(acc_k);
+        free(acc_v);
+    }
 }
 
 int32_t orc_num_threads(void)

@@ -42,13 +42,15 @@ def dense_forward(q, k, v, mask, scale):
     return out, lse
 
 
-def dense_backward(q, k, v, dout, mask, scale):
-    """Closed-form gradients of the dense masked softmax attention."""
+def dense_backward(q, k, v, dout, mask, scale, out=None, lse=None):
+    """Closed-form gradients of the dense masked softmax attention. ``out`` and
+    ``lse`` replace the forward's own O and LSE when given (saved state)."""
     B, Sq, Hq, D = q.shape
     Hkv = k.shape[2]
     G = Hq // Hkv
     kk, vv = _expand(k, Hq), _expand(v, Hq)
-    out, lse = dense_forward(q, k, v, mask, scale)
+    if out is None:
+        out, lse = dense_forward(q, k, v, mask, scale)
     s = scale * np.einsum("bihd,bjhd->bhij", q, kk)
     m4 = np.broadcast_to(mask[:, None], s.shape)
     p = np.where(m4, np.exp(s - np.where(np.isfinite(lse), lse, 0.0)[..., None]), 0.0)

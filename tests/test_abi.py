@@ -19,7 +19,9 @@ def lib():
 
 
 def _declared_functions():
-    text = open(os.path.join(ROOT, "include", "qsa.h")).read()
+    inc = os.path.join(ROOT, "include")
+    text = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc))
+                   if f.endswith(".h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(qsa_[a-z_]+)\s*\(", text)))
 
@@ -28,7 +30,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("qsa_forward", "qsa_backward", "qsa_preprocess", "qsa_forward_workspace_bytes",
               "qsa_backward_workspace_bytes", "qsa_preprocess_workspace_bytes",
-              "qsa_status_string", "qsa_version"):
+              "qsa_status_string", "qsa_version", "qsa_forward_timed",
+              "qsa_backward_timed", "qsa_bench_gather"):
         assert n in names
 
 
@@ -104,3 +107,4 @@ def test_no_gpu_here_reports_device_error(lib):
     a = ctypes.c_void_p(4096)
     ws = lib.qsa_forward_workspace_bytes(ctypes.byref(d))
     assert lib.qsa_forward(ctypes.byref(d), a, a, a, a, 0.0625, a, a, a, a, ws, None) == 9
+

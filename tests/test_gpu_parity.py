@@ -115,9 +115,16 @@ def test_tiny_workload_full_parity():
     _full_compare(inp, wl.scale, run)
 
 
-def _sample_rows(wl, inp, rng, n=48):
+def _sample_rows(wl, inp, rng, n=160):
+    """At least 256 flat rows: the first and last rows, every 128-row tile boundary
+    (rows 128t - 1, 128t), document starts and valid-length edges, and random rows."""
     rows = set(range(3)) | set(range(wl.Sq - 3, wl.Sq))
+    for t in range(1, -(-wl.Sq // 128)):
+        rows |= {128 * t - 1, 128 * t}
+    rows = set(sorted(rows)[:96]) | set(range(wl.Sq - 3, wl.Sq))
     rows |= set(int(x) for x in rng.choice(wl.Sq, n, replace=False))
+    while len(rows) < 256:
+        rows.add(int(rng.integers(0, wl.Sq)))
     for s in inp.info.get("doc_starts", []):
         rows |= {int(s), min(int(s) + 5, wl.Sq - 1)}
     flat = []
@@ -130,16 +137,39 @@ def _sample_rows(wl, inp, rng, n=48):
     return np.array(sorted(set(flat)), np.int64)
 
 
-SAMPLED_KEYS = {
-    2: [0, 1, 2000, 4095, 6000, 8191],
-    3: [0, 77, 1030, 4095, 4096 + 5, 4096 * 2 + 3000, 4096 * 3 + 4095],
-    4: [16000, 16002, 31000, 32767],
-    5: [0, 5000, 20001, 28700, 32767],
-}
+def _sample_keys(wl, rng, n=24):
+    """At least 64 flat keys: keys 0..15, both sides of every key-tile boundary
+    that is a power-of-two multiple of 128, the last keys, and random keys."""
+    keys = set(range(16)) | set(range(wl.Skv - 4, wl.Skv))
+    t = 128
+    while t < wl.Skv:
+        keys |= {t - 1, t}
+        t *= 2
+    keys |= set(int(x) for x in rng.choice(wl.Skv, n, replace=False))
+    while len(keys) < 64:
+        keys.add(int(rng.integers(0, wl.Skv)))
+    flat = []
+    for b in range(wl.B):
+        flat += [b * wl.Skv + k for k in sorted(keys)]
+    return np.array(flat, np.int64)
 
 
+def _check_all(run, refs, wl, label=""):
+    o_ref, l_ref, dq_ref, dk_ref, dv_ref = refs
+    check_close(f"{label}out_fp32 (all rows)", to_np(run.out32), o_ref, TOL_FP32)
+    check_close(f"{label}lse (all rows)", to_np(run.lse), l_ref, TOL_FP32)
+    check_close(f"{label}out (all rows)", to_np(run.out), o_ref, TOL_BF16)
+    check_close(f"{label}dq (all rows)", to_np(run.dq), dq_ref, TOL_BF16)
+    check_close(f"{label}dk (all keys)", to_np(run.dk), dk_ref, TOL_BF16)
+    check_close(f"{label}dv (all keys)", to_np(run.dv), dv_ref, TOL_BF16)
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("idx", [2, 3, 4, 5])
 def test_full_size_workload_parity(idx):
+    """Every output element of the full-size workload against the oracle (one
+    pass over all rows), then the oracle's backward fed the GPU's own out_fp32
+    and lse on sampled rows and keys, which isolates the backward's error."""
     wl = synth.WORKLOADS[idx]
     log(f"workload {wl.name}: generating")
     inp = synth.make_inputs(wl)
@@ -147,21 +177,24 @@ def test_full_size_workload_parity(idx):
     log("  preprocess check")
     check_preprocess_exact(inp.routes, wl.Skv, run.routes)
     P = oracle.Problem(inp.q, inp.k, inp.v, inp.routes, wl.scale, inp.grad_out)
+    log(f"  oracle: all outputs ({oracle.num_threads()} threads)")
+    _check_all(run, P.all_outputs(), wl)
+    # backward on the GPU's saved state
     rng = np.random.default_rng(100 + idx)
     rows = _sample_rows(wl, inp, rng)
-    o_ref, l_ref = P.forward(rows)
-    out32 = to_np(run.out32).reshape(-1, wl.Hq, wl.D)[rows]
-    lse = to_np(run.lse).transpose(0, 2, 1).reshape(-1, wl.Hq)[rows]
-    check_close(f"out_fp32[{len(rows)} rows]", out32, o_ref, TOL_FP32)
-    check_close("lse[rows]", lse, l_ref, TOL_FP32)
-    check_close("out[rows]", to_np(run.out).reshape(-1, wl.Hq, wl.D)[rows], o_ref, TOL_BF16)
-    dq_ref = P.backward_dq(rows)
-    check_close("dq[rows]", to_np(run.dq).reshape(-1, wl.Hq, wl.D)[rows], dq_ref, TOL_BF16)
-    keys = np.array(SAMPLED_KEYS[idx], np.int64)
-    log(f"  oracle dk/dv for keys {keys.tolist()}")
-    dk_ref, dv_ref = P.backward_dkdv(keys)
-    check_close("dk[keys]", to_np(run.dk).reshape(-1, wl.Hkv, wl.D)[keys], dk_ref, TOL_BF16)
-    check_close("dv[keys]", to_np(run.dv).reshape(-1, wl.Hkv, wl.D)[keys], dv_ref, TOL_BF16)
+    keys = _sample_keys(wl, rng)
+    assert len(rows) >= 256 and len(keys) >= 64
+    P.use_saved(to_np(run.out32), to_np(run.lse))
+    log(f"  oracle on the GPU's out_fp32 and lse: dq of {len(rows)} rows, dk/dv of "
+        f"{len(keys)} keys")
+    dq_s = P.backward_dq(rows)
+    check_close("dq[rows] (saved state)", to_np(run.dq).reshape(-1, wl.Hq, wl.D)[rows], dq_s,
+                TOL_BF16)
+    dk_s, dv_s = P.backward_dkdv(keys)
+    check_close("dk[keys] (saved state)", to_np(run.dk).reshape(-1, wl.Hkv, wl.D)[keys], dk_s,
+                TOL_BF16)
+    check_close("dv[keys] (saved state)", to_np(run.dv).reshape(-1, wl.Hkv, wl.D)[keys], dv_s,
+                TOL_BF16)
     # properties at full size: empty rows are exactly zero with -inf lse
     has = (inp.routes >= 0).any(-1)
     empty = ~has
@@ -170,7 +203,34 @@ def test_full_size_workload_parity(idx):
         assert (o == 0).all() and not np.signbit(o).any()
         assert (to_np(run.dq)[empty] == 0).all()
         assert np.isneginf(to_np(run.lse).transpose(0, 2, 1)[empty]).all()
-    assert np.isfinite(to_np(run.out32)).all() and np.isfinite(to_np(run.dk)).all()
+
+
+@pytest.mark.timeout(600)
+def test_rotated_walks_with_restarts_and_redo():
+    # 16384 query rows (eight per resident wave slot of a 256-CU device), so the
+    # default mode rotates the gathered walks, with very large scores in the last
+    # chosen key tile: rows whose walk starts mid-list meet the large scores
+    # after smaller ones and restart, and the dense forward redoes its tiles.
+    # Both modes against the oracle, and against each other.
+    case = dict(seed=57, B=1, Sq=16384, Skv=512, Hq=12, Hkv=1, p_full=0.6, extra=20,
+                loud_keys=48.0, loud_last=True)
+    log(f"case {case}")
+    inp = synth.tiled_case(**case)
+    a = DeviceRun(inp, 0.0625, deterministic=True)
+    b = DeviceRun(inp, 0.0625)
+    P = oracle.Problem(inp.q, inp.k, inp.v, inp.routes, 0.0625, inp.grad_out)
+    refs = P.all_outputs()
+    wl = inp.wl
+    _check_all(a, refs, wl, "deterministic ")
+    _check_all(b, refs, wl, "default ")
+    for name, x, y in (("out_fp32", a.out32, b.out32), ("lse", a.lse, b.lse)):
+        x = x.double()
+        y = y.double()
+        fin = torch.isfinite(x)
+        assert torch.equal(fin, torch.isfinite(y)) and torch.equal(x[~fin], y[~fin]), name
+        err = ((x - y)[fin].abs() / (1e-4 + 1e-4 * x[fin].abs())).max().item()
+        log(f"  {name}: max |default - deterministic| / (1e-4 + 1e-4 |x|) = {err:.3f}")
+        assert err <= 1.0, name
 
 
 def test_route_order_duplicates_invalid_ids_bitwise():

@@ -353,3 +353,48 @@ def test_padding_rows_and_unselected_nan():
     assert np.isneginf(lse[0, :, 4]).all()
     assert (dq[0, 4] == 0).all()
     assert (dk[0, 25:] == 0).all() and (dv[0, 25:] == 0).all()
+
+
+def test_backward_on_saved_state_matches_dense_closed_form():
+    # The backward equations take the saved O and LSE as inputs (a GPU run feeds
+    # its out_fp32 and lse). With perturbed saved values the oracle must follow
+    # the same closed form as the dense NumPy backward fed the same values, and
+    # differ from its own-forward result (the saved values are really used).
+    c = _case(16, B=2, Sq=33, Skv=27, Hq=24, Hkv=2, W=11, D=16)
+    P = _problem(c)
+    own = P.backward_full()
+    o, lse = P.forward_full()
+    rng = np.random.default_rng(5)
+    o2 = o + 1e-2 * rng.standard_normal(o.shape)
+    lse2 = np.where(np.isfinite(lse), lse + 1e-2 * rng.standard_normal(lse.shape), lse)
+    P.use_saved(o2, lse2)
+    got = P.backward_full()
+    m = dense_mask(c.routes, 27)
+    want = dense_backward(P.q, P.k, P.v, P.dout, m, P.scale, out=o2, lse=lse2)
+    for a, b in zip(got, want):
+        np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-11)
+    rows = np.array([0, 5, 40, 65], np.int64)
+    np.testing.assert_allclose(P.backward_dq(rows), got[0].reshape(-1, 24, 16)[rows],
+                               rtol=1e-12, atol=1e-12)
+    keys = np.array([0, 3, 30, 53], np.int64)
+    dk, dv = P.backward_dkdv(keys)
+    np.testing.assert_allclose(dk, got[1].reshape(-1, 2, 16)[keys], rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(dv, got[2].reshape(-1, 2, 16)[keys], rtol=1e-11, atol=1e-11)
+    assert np.abs(got[0] - own[0]).max() > 1e-4
+    P.use_saved(None, None)
+    again = P.backward_full()
+    for a, b in zip(again, own):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_all_outputs_pass_matches_separate_calls():
+    c = _case(17, B=2, Sq=31, Skv=40, Hq=24, Hkv=2, W=9, D=16)
+    P = _problem(c)
+    o, lse, dq, dk, dv = P.all_outputs()
+    o2, lse2 = P.forward_full()
+    dq2, dk2, dv2 = P.backward_full()
+    for a, b in ((o, o2), (lse, lse2), (dq, dq2), (dk, dk2), (dv, dv2)):
+        np.testing.assert_array_equal(a, b)
+    m = dense_mask(c.routes, 40)
+    o3, lse3 = dense_forward(P.q, P.k, P.v, m, P.scale)
+    np.testing.assert_allclose(o, o3, rtol=1e-12, atol=1e-12)

@@ -1,10 +1,11 @@
 // Host side of the QSA C ABI: validation before any launch, workspace sizing
 // and carving, and the launch sequence of each call. See include/qsa.h for the
 // contract of every entry point.
-#include "../../include/qsa.h"
+#include "../../include/qsa_bench.h"
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "common.h"
 
@@ -120,40 +121,52 @@ Layout layout(const qsa_dims *d, int which)
     return L;
 }
 
+// Properties of each device the library has run on, read once per device
+// (std::call_once, so concurrent first calls on one device do not race) and
+// never changed afterwards.
+constexpr int kMaxDevices = 64;
 struct DeviceInfo {
-    bool checked = false, ok = false;
+    bool ok = false;
     size_t max_lds = 0;
     uint32_t cus = 0;
 };
-DeviceInfo g_dev[64];
+DeviceInfo g_dev[kMaxDevices];
+std::once_flag g_dev_once[kMaxDevices];
+
+const DeviceInfo *device_info(int &dev)
+{
+    dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::call_once(g_dev_once[dev], [dev]() {
+        hipDeviceProp_t prop;
+        DeviceInfo &info = g_dev[dev];
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
+        info.max_lds = prop.sharedMemPerBlock;
+        info.cus = (uint32_t)prop.multiProcessorCount;
+        info.ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 && info.cus > 0;
+    });
+    return &g_dev[dev];
+}
 
 qsa_status check_device(const qsa_dims *d)
 {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return QSA_ERR_DEVICE;
-    DeviceInfo &info = g_dev[dev];
-    if (!info.checked) {
-        hipDeviceProp_t prop;
-        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return QSA_ERR_DEVICE;
-        info.ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-        info.max_lds = prop.sharedMemPerBlock;
-        info.cus = (uint32_t)prop.multiProcessorCount;
-        info.checked = true;
-    }
-    if (!info.ok || info.cus == 0) return QSA_ERR_DEVICE;
+    const DeviceInfo *info = device_info(dev);
+    if (!info || !info->ok) return QSA_ERR_DEVICE;
     const int64_t stride = (d->Skv + kTile - 1) / kTile * kTile;
     const size_t lds = (size_t)(stride / 32) * 4 + 257 * 4;
-    if (lds > info.max_lds) return QSA_ERR_SHAPE;
+    if (lds > info->max_lds) return QSA_ERR_SHAPE;
     return QSA_OK;
 }
 
 // Resident waves of the gathered forward and dQ passes: two per SIMD, four
-// SIMDs per CU (their register use keeps two waves per SIMD).
+// SIMDs per CU (their register use keeps two waves per SIMD). Called after
+// check_device has succeeded on the current device.
 uint32_t walk_slots()
 {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
-    return g_dev[dev].cus * 8u;
+    const DeviceInfo *info = device_info(dev);
+    return info && info->ok ? info->cus * 8u : 1u;
 }
 
 void fill_common(Problem &p, const qsa_dims *d, const void *routes, float scale)
