@@ -87,7 +87,9 @@ typedef enum qsa_status {
     QSA_ERR_ROUTE_DTYPE = 7, /* route_is_i64 not 0 or 1, or an unknown flags bit */
     QSA_ERR_WORKSPACE = 8,   /* workspace NULL or smaller than required */
     QSA_ERR_DEVICE = 9,      /* no gfx950 device current, or a HIP runtime error */
-    QSA_ERR_LAUNCH = 10      /* a kernel launch failed */
+    QSA_ERR_LAUNCH = 10,     /* a kernel launch failed */
+    QSA_ERR_SCRATCH = 11     /* qsa_forward_noalloc: the call needs more workspace than
+                                the library's fixed device scratch holds */
 } qsa_status;
 
 /* Bits of qsa_dims.flags.
@@ -165,6 +167,26 @@ qsa_status qsa_preprocess(const qsa_dims *dims, const void *routes, uint8_t *mem
                           int32_t *rev_p_cnt, int32_t *rev_p_idx, int32_t *rev_f_cnt,
                           int32_t *rev_f_idx, int32_t *row_keys, int32_t *row_cnt,
                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Forward that allocates nothing, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). Same operation, arguments, validation and results as
+ * qsa_forward, without the workspace arguments: the workspace is a fixed
+ * device array of this library, QSA_NOALLOC_SCRATCH_BYTES (64 MiB) per
+ * device, which each device holds from the first call until the process
+ * ends. A call whose qsa_forward_workspace_bytes exceeds it returns
+ * QSA_ERR_SCRATCH before touching the device. The call makes no device
+ * allocation and no allocating library call. Every call on one device uses
+ * that device's one array, so calls that overlap on one device (different
+ * streams, or different host threads without ordering) race and give wrong
+ * results: order them on one stream. The first call on each device looks up
+ * the array's device address once (thread-safe).
+ */
+#define QSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+qsa_status qsa_forward_noalloc(const qsa_dims *dims, const void *q, const void *k, const void *v,
+                               const void *routes, float scale, void *out, float *out_fp32,
+                               float *lse, void *stream);
 
 /* Static description of a status code. */
 const char *qsa_status_string(qsa_status status);

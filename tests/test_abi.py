@@ -30,8 +30,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("qsa_forward", "qsa_backward", "qsa_preprocess", "qsa_forward_workspace_bytes",
               "qsa_backward_workspace_bytes", "qsa_preprocess_workspace_bytes",
-              "qsa_status_string", "qsa_version", "qsa_forward_timed",
-              "qsa_backward_timed", "qsa_bench_gather"):
+              "qsa_status_string", "qsa_version", "qsa_forward_noalloc",
+              "qsa_forward_timed", "qsa_backward_timed", "qsa_bench_gather"):
         assert n in names
 
 
@@ -95,7 +95,7 @@ def test_pointer_scale_alignment_and_workspace_errors(lib):
     assert call(a, a, a, ctypes.c_void_p(4098), 0.0625, a, a, a, a, ws, None) == 6
     assert call(a, a, a, a, 0.0625, a, a, a, a, ws - 1, None) == 8
     assert call(a, a, a, a, 0.0625, a, a, a, None, ws, None) == 8
-    for s in range(11):
+    for s in range(12):
         assert lib.qsa_status_string(s)
 
 
@@ -108,3 +108,22 @@ def test_no_gpu_here_reports_device_error(lib):
     ws = lib.qsa_forward_workspace_bytes(ctypes.byref(d))
     assert lib.qsa_forward(ctypes.byref(d), a, a, a, a, 0.0625, a, a, a, a, ws, None) == 9
 
+def test_noalloc_validates_before_touching_the_device(lib):
+    fake = ctypes.c_void_p(4096)
+    args = (fake, fake, fake, fake, 0.0625, fake, fake, fake, None)
+    # invalid calls: the same status as qsa_forward
+    for kw, status in ((dict(D=128), 4), (dict(Hq=16), 3), (dict(B=0), 2), (dict(flags=2), 7)):
+        d = _dims(**kw)
+        assert lib.qsa_forward_noalloc(ctypes.byref(d), *args) == status
+    d = _dims()
+    assert lib.qsa_forward_noalloc(ctypes.byref(d), None, *args[1:]) == 1
+    assert lib.qsa_forward_noalloc(ctypes.byref(d), *args[:4], float("nan"), *args[5:]) == 5
+    # a call whose workspace exceeds the fixed scratch: the scratch error, on the host
+    big = _dims(Sq=32768, Skv=32768, W=2052)
+    assert lib.qsa_forward_workspace_bytes(ctypes.byref(big)) > (64 << 20)
+    assert lib.qsa_forward_noalloc(ctypes.byref(big), *args) == 11
+    assert b"scratch" in lib.qsa_status_string(11)
+    # the workloads up to 8192 tokens (and the 4096-query shard) fit the scratch
+    for kw in (dict(Sq=8192, Skv=8192, W=260), dict(B=4, Sq=4096, Skv=4096, Hq=24, Hkv=2, W=260),
+               dict(Sq=4096, Skv=32768, W=1028)):
+        assert lib.qsa_forward_workspace_bytes(ctypes.byref(_dims(**kw))) <= (64 << 20)

@@ -434,6 +434,9 @@ const char *qsa_status_string(qsa_status status)
     case QSA_ERR_WORKSPACE: return "workspace is NULL or smaller than the size query returned";
     case QSA_ERR_DEVICE: return "no gfx950 device is current, or the HIP runtime failed";
     case QSA_ERR_LAUNCH: return "a kernel launch failed";
+    case QSA_ERR_SCRATCH:
+        return "the call needs more workspace than the fixed device scratch of "
+               "qsa_forward_noalloc holds (QSA_NOALLOC_SCRATCH_BYTES)";
     }
     return "unknown status";
 }

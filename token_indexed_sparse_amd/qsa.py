@@ -22,7 +22,8 @@ GROUP = 12
 HEAD_DIM = 256
 
 OK, ERR_NULL, ERR_SHAPE, ERR_HEADS, ERR_HEADDIM, ERR_SCALE, ERR_ALIGN, ERR_ROUTE_DTYPE, \
-    ERR_WORKSPACE, ERR_DEVICE, ERR_LAUNCH = range(11)
+    ERR_WORKSPACE, ERR_DEVICE, ERR_LAUNCH, ERR_SCRATCH = range(12)
+NOALLOC_SCRATCH_BYTES = 64 << 20  # QSA_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -55,6 +56,8 @@ def library() -> ctypes.CDLL:
             getattr(lib, name).argtypes = [D]
         lib.qsa_forward.restype = ctypes.c_int
         lib.qsa_forward.argtypes = [D, P, P, P, P, ctypes.c_float, P, P, P, P, S, P]
+        lib.qsa_forward_noalloc.restype = ctypes.c_int
+        lib.qsa_forward_noalloc.argtypes = [D, P, P, P, P, ctypes.c_float, P, P, P, P]
         lib.qsa_backward.restype = ctypes.c_int
         lib.qsa_backward.argtypes = [D, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, S, P]
         lib.qsa_preprocess.restype = ctypes.c_int
@@ -71,7 +74,8 @@ def _raise(status: int) -> None:
     if status == OK:
         return
     msg = library().qsa_status_string(status).decode()
-    if status in (ERR_SHAPE, ERR_HEADS, ERR_HEADDIM, ERR_SCALE, ERR_NULL, ERR_ALIGN):
+    if status in (ERR_SHAPE, ERR_HEADS, ERR_HEADDIM, ERR_SCALE, ERR_NULL, ERR_ALIGN,
+                  ERR_SCRATCH):
         raise ValueError(f"QSA status {status}: {msg}")
     if status == ERR_ROUTE_DTYPE:
         raise TypeError(f"QSA status {status}: {msg}")
@@ -166,6 +170,29 @@ def forward(q, k, v, routes, scale: Optional[float] = None, *, out=None, out_fp3
                          routes.data_ptr(), float(scale), out.data_ptr(), out_fp32.data_ptr(),
                          lse.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
                          _stream())
+    _raise(st)
+    return out, out_fp32, lse
+
+
+def forward_noalloc(q, k, v, routes, scale: Optional[float] = None, *, out, out_fp32, lse,
+                    deterministic: bool = False):
+    """QSA forward through ``qsa_forward_noalloc``: the caller passes every output,
+    and the library uses its fixed device scratch as workspace (no allocation)."""
+    q = _check(q, torch.bfloat16, "q")
+    k = _check(k, torch.bfloat16, "k")
+    v = _check(v, torch.bfloat16, "v")
+    if not routes.is_cuda:
+        raise ValueError("routes must be a GPU tensor")
+    for t, name in ((routes, "routes"), (out, "out"), (out_fp32, "out_fp32"), (lse, "lse")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    dims = _dims(q, k, routes, deterministic)
+    if scale is None:
+        scale = 1.0 / (q.shape[-1] ** 0.5)
+    st = library().qsa_forward_noalloc(ctypes.byref(dims), q.data_ptr(), k.data_ptr(),
+                                       v.data_ptr(), routes.data_ptr(), float(scale),
+                                       out.data_ptr(), out_fp32.data_ptr(), lse.data_ptr(),
+                                       _stream())
     _raise(st)
     return out, out_fp32, lse
 
