@@ -252,7 +252,8 @@ def gather_ceiling(torch, lib, hip, stream, row_bytes: int, footprint_bytes: int
         torch.cuda.synchronize()
         ms = ev.elapsed(0, 1)
         best = ms if best is None else min(best, ms)
-    return n_items * 1024 / (best * 1e-3) / 1e9
+    item_bytes = 1024 if row_bytes == 512 else row_bytes  # two 512 B rows, or one 6 KB row
+    return n_items * item_bytes / (best * 1e-3) / 1e9
 
 
 def main() -> int:
