@@ -88,8 +88,10 @@ typedef enum qsa_status {
     QSA_ERR_WORKSPACE = 8,   /* workspace NULL or smaller than required */
     QSA_ERR_DEVICE = 9,      /* no gfx950 device current, or a HIP runtime error */
     QSA_ERR_LAUNCH = 10,     /* a kernel launch failed */
-    QSA_ERR_SCRATCH = 11     /* qsa_forward_noalloc: the call needs more workspace than
+    QSA_ERR_SCRATCH = 11,    /* qsa_forward_noalloc: the call needs more workspace than
                                 the library's fixed device scratch holds */
+    QSA_ERR_PLAN = 12        /* a plan not built by qsa_plan_build, edited so that its
+                                buffer no longer fits its dims, or used on another device */
 } qsa_status;
 
 /* Bits of qsa_dims.flags.
@@ -168,6 +170,70 @@ qsa_status qsa_preprocess(const qsa_dims *dims, const void *routes, uint8_t *mem
                           int32_t *rev_f_idx, int32_t *row_keys, int32_t *row_cnt,
                           void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Route plan, built once and used by any number of forward, recomputed
+ * forward and backward calls on the same routes (the mask object that the
+ * "flex_qsa" page builds once per step and hands to both the checkpointed
+ * forward and its recompute: `FlexQSAMask`, `build_flex_qsa_mask`, and the
+ * `mask` argument of `flex_sparse_gqa_attention`).
+ *
+ * qsa_plan_build runs the route preprocessing of qsa_forward and
+ * qsa_backward once (per-row sorted key lists, the membership bits the dK/dV
+ * pass reads, tile kinds and forward and reverse tile lists) into plan_mem, a
+ * caller-owned device buffer of at least qsa_plan_bytes(dims) bytes (16-byte
+ * aligned), and fills the host struct *plan. The routes are not read again
+ * after the build's kernels have run. The planned calls below read plan_mem
+ * and never write it, so one plan serves calls on several streams once its
+ * build is complete on each of them (order them after the build, e.g. with
+ * an event).
+ *
+ * Ownership: plan_mem stays the caller's; the plan struct only records it.
+ * The plan is valid while plan_mem holds what the build wrote and only on
+ * the device that was current during the build. Freeing or overwriting
+ * plan_mem, or changing the routes, needs a new build. qsa_plan_build clears
+ * *plan first, so a failed build leaves a plan that every planned call
+ * rejects with QSA_ERR_PLAN.
+ *
+ * The planned calls take the plan in place of dims and routes and compute
+ * exactly what qsa_forward and qsa_backward compute from the same routes
+ * (bitwise, with QSA_FLAG_DETERMINISTIC in the plan's dims); their own
+ * workspace holds only per-call scratch (the sizes below, much smaller than
+ * the plain calls'). The plan's dims, including flags, apply to every
+ * planned call.
+ */
+#define QSA_PLAN_TAG 0x51534150u
+typedef struct qsa_plan {
+    qsa_dims dims;    /* the dims the plan was built for */
+    void *mem;        /* the caller's device buffer holding the plan */
+    size_t bytes;     /* its size as passed to qsa_plan_build */
+    int32_t device;   /* HIP device current during the build */
+    uint32_t tag;     /* QSA_PLAN_TAG after a successful build */
+} qsa_plan;
+size_t qsa_plan_bytes(const qsa_dims *dims);
+size_t qsa_forward_planned_workspace_bytes(const qsa_dims *dims);
+size_t qsa_backward_planned_workspace_bytes(const qsa_dims *dims);
+qsa_status qsa_plan_build(const qsa_dims *dims, const void *routes, void *plan_mem,
+                          size_t plan_bytes, qsa_plan *plan, void *stream);
+qsa_status qsa_forward_planned(const qsa_plan *plan, const void *q, const void *k, const void *v,
+                               float scale, void *out, float *out_fp32, float *lse,
+                               void *workspace, size_t workspace_bytes, void *stream);
+qsa_status qsa_backward_planned(const qsa_plan *plan, const void *grad_out, const void *q,
+                                const void *k, const void *v, const float *out_fp32,
+                                const float *lse, float scale, void *dq, void *dk, void *dv,
+                                void *workspace, size_t workspace_bytes, void *stream);
+/*
+ * Copies of a built plan's tables, for inspection and bit-exact checks, in
+ * the layouts qsa_preprocess documents, except that the membership comes bit
+ * packed: mbits uint32 [B, Sq, stride / 32], bit (j % 32) of word j / 32 set
+ * where j is in R(b, i). Every pointer is a device pointer to a buffer of
+ * that size, 4-byte aligned, none may be NULL. Copies are enqueued on
+ * `stream` after whatever the stream already holds; the plan is not changed.
+ */
+qsa_status qsa_plan_tables(const qsa_plan *plan, uint32_t *mbits, int32_t *kinds,
+                           int32_t *fwd_p_cnt, int32_t *fwd_p_idx, int32_t *fwd_f_cnt,
+                           int32_t *fwd_f_idx, int32_t *rev_p_cnt, int32_t *rev_p_idx,
+                           int32_t *rev_f_cnt, int32_t *rev_f_idx, int32_t *row_keys,
+                           int32_t *row_cnt, void *stream);
 /*
  * Forward that allocates nothing, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that

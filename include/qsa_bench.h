@@ -41,6 +41,18 @@ qsa_status qsa_backward_timed(const qsa_dims *dims, const void *grad_out, const 
                               void *dk, void *dv, void *workspace, size_t workspace_bytes,
                               void *stream, void *const *events, int32_t n_events);
 
+/* The same for the planned calls; their stage 0 only resets the walk clocks
+ * (the plan replaces the preprocessing). */
+qsa_status qsa_forward_planned_timed(const qsa_plan *plan, const void *q, const void *k,
+                                     const void *v, float scale, void *out, float *out_fp32,
+                                     float *lse, void *workspace, size_t workspace_bytes,
+                                     void *stream, void *const *events, int32_t n_events);
+qsa_status qsa_backward_planned_timed(const qsa_plan *plan, const void *grad_out, const void *q,
+                                      const void *k, const void *v, const float *out_fp32,
+                                      const float *lse, float scale, void *dq, void *dk,
+                                      void *dv, void *workspace, size_t workspace_bytes,
+                                      void *stream, void *const *events, int32_t n_events);
+
 /*
  * Gather-rate probe: stages rows rows[0 .. n_rows) of `src` (device memory of
  * src_bytes < 2^31; row i occupies bytes [rows[i] * row_bytes, + row_bytes))

@@ -31,7 +31,10 @@ def test_header_declares_the_entry_points():
     for n in ("qsa_forward", "qsa_backward", "qsa_preprocess", "qsa_forward_workspace_bytes",
               "qsa_backward_workspace_bytes", "qsa_preprocess_workspace_bytes",
               "qsa_status_string", "qsa_version", "qsa_forward_noalloc",
-              "qsa_forward_timed", "qsa_backward_timed", "qsa_bench_gather"):
+              "qsa_forward_timed", "qsa_backward_timed", "qsa_bench_gather",
+              "qsa_plan_bytes", "qsa_plan_build", "qsa_forward_planned", "qsa_backward_planned",
+              "qsa_forward_planned_workspace_bytes", "qsa_backward_planned_workspace_bytes",
+              "qsa_plan_tables", "qsa_forward_planned_timed", "qsa_backward_planned_timed"):
         assert n in names
 
 
@@ -95,8 +98,9 @@ def test_pointer_scale_alignment_and_workspace_errors(lib):
     assert call(a, a, a, ctypes.c_void_p(4098), 0.0625, a, a, a, a, ws, None) == 6
     assert call(a, a, a, a, 0.0625, a, a, a, a, ws - 1, None) == 8
     assert call(a, a, a, a, 0.0625, a, a, a, None, ws, None) == 8
-    for s in range(12):
-        assert lib.qsa_status_string(s)
+    for s in range(13):
+        assert lib.qsa_status_string(s) != b"unknown status"
+    assert lib.qsa_status_string(13) == b"unknown status"
 
 
 def test_no_gpu_here_reports_device_error(lib):
@@ -127,3 +131,96 @@ def test_noalloc_validates_before_touching_the_device(lib):
     for kw in (dict(Sq=8192, Skv=8192, W=260), dict(B=4, Sq=4096, Skv=4096, Hq=24, Hkv=2, W=260),
                dict(Sq=4096, Skv=32768, W=1028)):
         assert lib.qsa_forward_workspace_bytes(ctypes.byref(_dims(**kw))) <= (64 << 20)
+
+
+def test_plan_sizes_split_the_plain_workspaces(lib):
+    """The plan holds the preprocessing of both calls; the planned calls' scratch is
+    the rest, so plan + planned scratch covers the plain backward exactly and the
+    plain forward plus the membership bits only the backward reads."""
+    from token_indexed_sparse_amd import qsa
+    for kw in (dict(), dict(Sq=32768, Skv=32768, W=2052), dict(B=4, Sq=4096, Skv=4096, Hq=24,
+                                                              Hkv=2, W=260)):
+        d = _dims(**kw)
+        plan = lib.qsa_plan_bytes(ctypes.byref(d))
+        pf = lib.qsa_forward_planned_workspace_bytes(ctypes.byref(d))
+        pb = lib.qsa_backward_planned_workspace_bytes(ctypes.byref(d))
+        f, b = qsa.forward_workspace_bytes(d), qsa.backward_workspace_bytes(d)
+        assert 0 < pf < f and 0 < pb < b
+        assert plan + pb == b
+        bits = -(-d.B * d.Sq * (-(-d.Skv // 128) * 4) * 4 // 256) * 256
+        assert plan + pf == f + bits
+    bad = _dims(D=128)
+    for n in ("qsa_plan_bytes", "qsa_forward_planned_workspace_bytes",
+              "qsa_backward_planned_workspace_bytes"):
+        assert getattr(lib, n)(ctypes.byref(bad)) == 0
+
+
+def _plan(**kw):
+    from token_indexed_sparse_amd import qsa
+    return qsa.PlanStruct(**kw)
+
+
+def test_plan_build_validates_before_touching_the_device(lib):
+    import torch
+    fake = ctypes.c_void_p(4096)
+    d = _dims()
+    need = lib.qsa_plan_bytes(ctypes.byref(d))
+    pl = _plan(tag=7, bytes=5)
+    assert lib.qsa_plan_build(ctypes.byref(d), fake, fake, need, None, None) == 1
+    for kw, status in ((dict(D=128), 4), (dict(Hq=16), 3), (dict(B=0), 2), (dict(flags=2), 7)):
+        pl = _plan(tag=7)
+        assert lib.qsa_plan_build(ctypes.byref(_dims(**kw)), fake, fake, need, ctypes.byref(pl),
+                                  None) == status
+        assert pl.tag == 0  # cleared first: a failed build leaves no usable plan
+    pl = _plan()
+    assert lib.qsa_plan_build(ctypes.byref(d), None, fake, need, ctypes.byref(pl), None) == 1
+    assert lib.qsa_plan_build(ctypes.byref(d), ctypes.c_void_p(4098), fake, need,
+                              ctypes.byref(pl), None) == 6
+    assert lib.qsa_plan_build(ctypes.byref(d), fake, fake, need - 1, ctypes.byref(pl), None) == 8
+    assert lib.qsa_plan_build(ctypes.byref(d), fake, None, need, ctypes.byref(pl), None) == 8
+    assert lib.qsa_plan_build(ctypes.byref(d), fake, ctypes.c_void_p(4100), need,
+                              ctypes.byref(pl), None) == 6
+    if not torch.cuda.is_available():
+        assert lib.qsa_plan_build(ctypes.byref(d), fake, fake, need, ctypes.byref(pl), None) == 9
+        assert pl.tag == 0
+
+
+def test_planned_calls_reject_unbuilt_or_edited_plans(lib):
+    import torch
+    from token_indexed_sparse_amd import qsa
+    a = ctypes.c_void_p(4096)
+    d = _dims()
+    need = lib.qsa_plan_bytes(ctypes.byref(d))
+    fws = lib.qsa_forward_planned_workspace_bytes(ctypes.byref(d))
+    bws = lib.qsa_backward_planned_workspace_bytes(ctypes.byref(d))
+
+    def fwd(pl, scale=0.0625, ws=fws):
+        return lib.qsa_forward_planned(pl, a, a, a, scale, a, a, a, a, ws, None)
+
+    def bwd(pl, scale=0.0625, ws=bws):
+        return lib.qsa_backward_planned(pl, a, a, a, a, a, a, scale, a, a, a, a, ws, None)
+
+    def tables(pl):
+        return lib.qsa_plan_tables(pl, *([a] * 12), None)
+
+    for call in (fwd, bwd, tables):
+        assert call(None) == 1
+        assert call(ctypes.byref(_plan())) == qsa.ERR_PLAN  # never built
+        built = _plan(dims=d, mem=4096, bytes=need, device=0, tag=qsa.PLAN_TAG)
+        built.bytes = need - 1  # edited: the buffer no longer fits the dims
+        assert call(ctypes.byref(built)) == qsa.ERR_PLAN
+        bad_dims = _plan(dims=_dims(D=128), mem=4096, bytes=need, device=0, tag=qsa.PLAN_TAG)
+        assert call(ctypes.byref(bad_dims)) == 4
+    ok = _plan(dims=d, mem=4096, bytes=need, device=0, tag=qsa.PLAN_TAG)
+    assert fwd(ctypes.byref(ok), scale=float("nan")) == 5
+    assert bwd(ctypes.byref(ok), scale=-1.0) == 5
+    assert fwd(ctypes.byref(ok), ws=fws - 1) == 8
+    assert bwd(ctypes.byref(ok), ws=bws - 1) == 8
+    assert lib.qsa_forward_planned(ctypes.byref(ok), a, ctypes.c_void_p(4097), a, 0.0625, a, a,
+                                   a, a, fws, None) == 6
+    assert lib.qsa_plan_tables(ctypes.byref(ok), *([a] * 11), None, None) == 1
+    assert lib.qsa_plan_tables(ctypes.byref(ok), ctypes.c_void_p(4098), *([a] * 11), None) == 6
+    if not torch.cuda.is_available():
+        assert fwd(ctypes.byref(ok)) == 9
+        assert bwd(ctypes.byref(ok)) == 9
+        assert tables(ctypes.byref(ok)) == 9

@@ -66,57 +66,70 @@ struct Layout {
         rpc, rpi, rfc, rfi, fstate, delta, kv_part, kv_flag, walk, total;
 };
 
-// which: 0 forward, 1 backward, 2 preprocess (only tile counts and, if the
-// caller does not want them, the row key lists).
-Layout layout(const qsa_dims *d, int which)
+// Parts of a workspace. The route plan: key lists and tile counts (core),
+// the membership bits that dK/dV reads (bits), the partial-tile key lists
+// (pkeys) and the tile kinds and tile lists (lists). The per-call scratch:
+// the forward's hand-over state (fwd), the backward's delta, partial sums and
+// flags (bwd), and the walk clocks of the gathered passes (walk).
+enum Part : unsigned {
+    kCore = 1u,
+    kBits = 2u,
+    kPkeys = 4u,
+    kLists = 8u,
+    kFwd = 16u,
+    kBwd = 32u,
+    kWalk = 64u,
+    kPlanParts = kCore | kBits | kPkeys | kLists,
+    kForwardParts = kCore | kPkeys | kLists | kFwd | kWalk,
+    kBackwardParts = kCore | kBits | kPkeys | kLists | kBwd | kWalk,
+};
+
+Layout layout(const qsa_dims *d, unsigned parts)
 {
     const int64_t nQT = (d->Sq + kTile - 1) / kTile, nKT = (d->Skv + kTile - 1) / kTile;
     const int64_t stride = nKT * kTile;
     const int64_t rows = d->B * d->Sq;
+    const size_t none = (size_t)-1;
     Layout L;
-    std::memset(&L, 0, sizeof(L));
+    std::memset(&L, 0xff, sizeof(L));
     size_t off = 0;
-    auto take = [&](size_t bytes) {
+    auto take = [&](bool want, size_t bytes) {
+        if (!want) return none;
         const size_t at = off;
         off += round_up(bytes);
         return at;
     };
-    const size_t none = (size_t)-1;
     // The byte membership table and has_routes are outputs of qsa_preprocess
     // only (caller buffers): no forward or backward kernel reads them, so those
     // calls do not materialise them.
-    L.memb = none;
-    L.has = none;
-    L.mbits = which == 1 ? take((size_t)(rows * (stride / 32)) * 4) : none;
-    L.row_keys = take((size_t)(rows * d->W) * 4);
-    L.row_cnt = take((size_t)rows * 4);
-    L.pkeys = which == 2 ? none : take((size_t)(rows * d->W) * 4);
-    L.pcnt = which == 2 ? none : take((size_t)rows * 4);
-    L.tile_cnt = take((size_t)(d->B * nQT * nKT) * 4);
-    if (which == 2) {
-        L.kinds = L.fpc = L.fpi = L.ffc = L.ffi = L.rpc = L.rpi = L.rfc = L.rfi = none;
-    } else {
-        L.kinds = take((size_t)(d->B * nQT * nKT) * 4);
-        L.fpc = take((size_t)(d->B * nQT) * 4);
-        L.fpi = take((size_t)(d->B * nQT * nKT) * 4);
-        L.ffc = take((size_t)(d->B * nQT) * 4);
-        L.ffi = take((size_t)(d->B * nQT * nKT) * 4);
-        L.rpc = take((size_t)(d->B * nKT) * 4);
-        L.rpi = take((size_t)(d->B * nKT * nQT) * 4);
-        L.rfc = take((size_t)(d->B * nKT) * 4);
-        L.rfi = take((size_t)(d->B * nKT * nQT) * 4);
-    }
-    L.fstate = which == 0 ? take((size_t)(d->B * d->Hq * d->Sq) * 8) : none;
-    L.delta = which == 1 ? take((size_t)(d->B * d->Hq * d->Sq) * 4) : none;
+    L.mbits = take(parts & kBits, (size_t)(rows * (stride / 32)) * 4);
+    L.row_keys = take(parts & kCore, (size_t)(rows * d->W) * 4);
+    L.row_cnt = take(parts & kCore, (size_t)rows * 4);
+    L.pkeys = take(parts & kPkeys, (size_t)(rows * d->W) * 4);
+    L.pcnt = take(parts & kPkeys, (size_t)rows * 4);
+    L.tile_cnt = take(parts & kCore, (size_t)(d->B * nQT * nKT) * 4);
+    const bool lists = parts & kLists;
+    L.kinds = take(lists, (size_t)(d->B * nQT * nKT) * 4);
+    L.fpc = take(lists, (size_t)(d->B * nQT) * 4);
+    L.fpi = take(lists, (size_t)(d->B * nQT * nKT) * 4);
+    L.ffc = take(lists, (size_t)(d->B * nQT) * 4);
+    L.ffi = take(lists, (size_t)(d->B * nQT * nKT) * 4);
+    L.rpc = take(lists, (size_t)(d->B * nKT) * 4);
+    L.rpi = take(lists, (size_t)(d->B * nKT * nQT) * 4);
+    L.rfc = take(lists, (size_t)(d->B * nKT) * 4);
+    L.rfi = take(lists, (size_t)(d->B * nKT * nQT) * 4);
+    L.fstate = take(parts & kFwd, (size_t)(d->B * d->Hq * d->Sq) * 8);
+    L.delta = take(parts & kBwd, (size_t)(d->B * d->Hq * d->Sq) * 4);
     const int64_t seg = seg_tiles_for(d);
     const int64_t nseg = (nQT + seg - 1) / seg;
     // The dK/dV partial sums and the dQ hand-over are never live together
     // (dQ finishes before dK/dV starts), so they share one region.
     const size_t kv_bytes = (size_t)(d->B * d->Hkv * (nseg + 1) * stride) * 2 * kD * 4;
     const size_t dq_bytes = (size_t)(rows * d->Hq) * kD * 4;
-    L.kv_part = which == 1 ? take(kv_bytes > dq_bytes ? kv_bytes : dq_bytes) : none;
-    L.kv_flag = which == 1 ? take((size_t)(d->B * d->Hkv * (nseg + 1) * (stride / 16))) : none;
-    L.walk = which == 2 ? none : take(16 * 4);
+    L.kv_part = take(parts & kBwd, kv_bytes > dq_bytes ? kv_bytes : dq_bytes);
+    L.kv_flag = take(parts & kBwd, (size_t)(d->B * d->Hkv * (nseg + 1) * (stride / 16)));
+    L.walk = take(parts & kWalk, 16 * 4);
+    L.memb = L.has = none;
     L.total = off;
     return L;
 }
@@ -197,13 +210,15 @@ void carve(Problem &p, const Layout &L, void *ws)
     if (L.memb != none) p.memb = reinterpret_cast<uint8_t *>(w + L.memb);
     if (L.has != none) p.has_routes = reinterpret_cast<uint8_t *>(w + L.has);
     if (L.mbits != none) p.mbits = reinterpret_cast<uint32_t *>(w + L.mbits);
-    p.row_keys = reinterpret_cast<int32_t *>(w + L.row_keys);
-    p.row_cnt = reinterpret_cast<int32_t *>(w + L.row_cnt);
+    if (L.row_keys != none) {
+        p.row_keys = reinterpret_cast<int32_t *>(w + L.row_keys);
+        p.row_cnt = reinterpret_cast<int32_t *>(w + L.row_cnt);
+        p.tile_cnt = reinterpret_cast<int32_t *>(w + L.tile_cnt);
+    }
     if (L.pkeys != none) {
         p.pkeys = reinterpret_cast<int32_t *>(w + L.pkeys);
         p.pcnt = reinterpret_cast<int32_t *>(w + L.pcnt);
     }
-    p.tile_cnt = reinterpret_cast<int32_t *>(w + L.tile_cnt);
     if (L.kinds != none) {
         p.kinds = reinterpret_cast<int32_t *>(w + L.kinds);
         p.fwd_p_cnt = reinterpret_cast<int32_t *>(w + L.fpc);
@@ -248,23 +263,143 @@ hipError_t mark(void *const *events, int at, hipStream_t s)
     return hipEventRecord(static_cast<hipEvent_t>(events[at]), s);
 }
 
+qsa_status check_forward_args(const void *q, const void *k, const void *v, float scale,
+                              const void *out, const float *out_fp32, const float *lse)
+{
+    if (!q || !k || !v || !out || !out_fp32 || !lse) return QSA_ERR_NULL;
+    const qsa_status st = check_scale(scale);
+    if (st != QSA_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(out_fp32, 16) || !aligned(lse, 4))
+        return QSA_ERR_ALIGN;
+    return QSA_OK;
+}
+
+qsa_status check_backward_args(const void *grad_out, const void *q, const void *k, const void *v,
+                               const float *out_fp32, const float *lse, float scale,
+                               const void *dq, const void *dk, const void *dv)
+{
+    if (!grad_out || !q || !k || !v || !out_fp32 || !lse || !dq || !dk || !dv)
+        return QSA_ERR_NULL;
+    const qsa_status st = check_scale(scale);
+    if (st != QSA_OK) return st;
+    if (!aligned(grad_out, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+        !aligned(out_fp32, 16) || !aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) ||
+        !aligned(dv, 16))
+        return QSA_ERR_ALIGN;
+    return QSA_OK;
+}
+
+// A workspace of `need` bytes: present (when needed), large enough, aligned.
+qsa_status check_workspace(const void *ws, size_t bytes, size_t need)
+{
+    if (need > 0 && (!ws || bytes < need)) return QSA_ERR_WORKSPACE;
+    if (ws && !aligned(ws, 16)) return QSA_ERR_ALIGN;
+    return QSA_OK;
+}
+
+// A plan that qsa_plan_build filled in and that still describes valid dims
+// and a large enough buffer (the caller may have edited the struct).
+qsa_status check_plan(const qsa_plan *plan)
+{
+    if (!plan) return QSA_ERR_NULL;
+    if (plan->tag != QSA_PLAN_TAG) return QSA_ERR_PLAN;
+    const qsa_status st = check_dims(&plan->dims);
+    if (st != QSA_OK) return st;
+    if (!plan->mem || plan->bytes < layout(&plan->dims, kPlanParts).total) return QSA_ERR_PLAN;
+    if (!aligned(plan->mem, 16)) return QSA_ERR_ALIGN;
+    return QSA_OK;
+}
+
+// The current device is the one the plan was built on.
+qsa_status check_plan_device(const qsa_plan *plan)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return QSA_ERR_DEVICE;
+    return dev == plan->device ? QSA_OK : QSA_ERR_PLAN;
+}
+
+// Forward launches after validation. With `prep` the route preprocessing
+// runs first into the workspace; otherwise a plan supplies its results and
+// only the walk clocks are reset.
+qsa_status run_forward(Problem &p, const void *q, const void *k, const void *v, void *out,
+                       float *out_fp32, float *lse, hipStream_t s, void *const *events, bool prep)
+{
+    p.q = static_cast<const uint16_t *>(q);
+    p.k = static_cast<const uint16_t *>(k);
+    p.v = static_cast<const uint16_t *>(v);
+    p.out = static_cast<uint16_t *>(out);
+    p.out_fp32 = out_fp32;
+    p.lse = lse;
+    if (mark(events, 0, s) != hipSuccess) return QSA_ERR_DEVICE;
+    if (prep) {
+        if (launch_preprocess(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+        if (launch_partial_keys(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    } else if (launch_walk_reset(p, s) != hipSuccess) {
+        return QSA_ERR_LAUNCH;
+    }
+    if (mark(events, 1, s) != hipSuccess) return QSA_ERR_DEVICE;
+    if (launch_forward(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 2, s) != hipSuccess) return QSA_ERR_DEVICE;
+    if (launch_forward_dense(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 3, s) != hipSuccess) return QSA_ERR_DEVICE;
+    return QSA_OK;
+}
+
+// Backward launches after validation; `prep` as for run_forward.
+qsa_status run_backward(Problem &p, const void *grad_out, const void *q, const void *k,
+                        const void *v, const float *out_fp32, const float *lse, void *dq, void *dk,
+                        void *dv, hipStream_t s, void *const *events, bool prep)
+{
+    p.q = static_cast<const uint16_t *>(q);
+    p.k = static_cast<const uint16_t *>(k);
+    p.v = static_cast<const uint16_t *>(v);
+    p.dout = static_cast<const uint16_t *>(grad_out);
+    p.out_fp32_in = out_fp32;
+    p.lse_in = lse;
+    p.dq = static_cast<uint16_t *>(dq);
+    p.dk = static_cast<uint16_t *>(dk);
+    p.dv = static_cast<uint16_t *>(dv);
+    if (mark(events, 0, s) != hipSuccess) return QSA_ERR_DEVICE;
+    if (prep) {
+        if (launch_preprocess(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+        if (launch_partial_keys(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    } else if (launch_walk_reset(p, s) != hipSuccess) {
+        return QSA_ERR_LAUNCH;
+    }
+    if (mark(events, 1, s) != hipSuccess) return QSA_ERR_DEVICE;
+    if (launch_delta(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 2, s) != hipSuccess) return QSA_ERR_DEVICE;
+    if (launch_dq(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 3, s) != hipSuccess) return QSA_ERR_DEVICE;
+    if (launch_dq_dense(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 4, s) != hipSuccess) return QSA_ERR_DEVICE;
+    if (launch_dkdv(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 5, s) != hipSuccess) return QSA_ERR_DEVICE;
+    if (launch_dkdv_dense(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 6, s) != hipSuccess) return QSA_ERR_DEVICE;
+    if (launch_dkdv_reduce(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 7, s) != hipSuccess) return QSA_ERR_DEVICE;
+    return QSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t qsa_forward_workspace_bytes(const qsa_dims *dims)
 {
-    return check_dims(dims) == QSA_OK ? layout(dims, 0).total : 0;
+    return check_dims(dims) == QSA_OK ? layout(dims, kForwardParts).total : 0;
 }
 
 size_t qsa_backward_workspace_bytes(const qsa_dims *dims)
 {
-    return check_dims(dims) == QSA_OK ? layout(dims, 1).total : 0;
+    return check_dims(dims) == QSA_OK ? layout(dims, kBackwardParts).total : 0;
 }
 
 size_t qsa_preprocess_workspace_bytes(const qsa_dims *dims)
 {
-    return check_dims(dims) == QSA_OK ? layout(dims, 2).total : 0;
+    return check_dims(dims) == QSA_OK ? layout(dims, kCore).total : 0;
 }
 
 qsa_status qsa_forward_timed(const qsa_dims *dims, const void *q, const void *k, const void *v,
@@ -274,36 +409,19 @@ qsa_status qsa_forward_timed(const qsa_dims *dims, const void *q, const void *k,
 {
     qsa_status st = check_dims(dims);
     if (st != QSA_OK) return st;
-    if (!q || !k || !v || !routes || !out || !out_fp32 || !lse) return QSA_ERR_NULL;
-    if ((st = check_scale(scale)) != QSA_OK) return st;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-        !aligned(out_fp32, 16) || !aligned(lse, 4) || !aligned(routes, route_align(dims)))
-        return QSA_ERR_ALIGN;
-    const Layout L = layout(dims, 0);
-    if (!workspace || workspace_bytes < L.total) return QSA_ERR_WORKSPACE;
-    if (!aligned(workspace, 16)) return QSA_ERR_ALIGN;
+    if (!routes) return QSA_ERR_NULL;
+    if ((st = check_forward_args(q, k, v, scale, out, out_fp32, lse)) != QSA_OK) return st;
+    if (!aligned(routes, route_align(dims))) return QSA_ERR_ALIGN;
+    const Layout L = layout(dims, kForwardParts);
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != QSA_OK) return st;
+    if (events && n_events < QSA_FORWARD_STAGES + 1) return QSA_ERR_NULL;
     if ((st = check_device(dims)) != QSA_OK) return st;
 
     Problem p;
     fill_common(p, dims, routes, scale);
     carve(p, L, workspace);
-    p.q = static_cast<const uint16_t *>(q);
-    p.k = static_cast<const uint16_t *>(k);
-    p.v = static_cast<const uint16_t *>(v);
-    p.out = static_cast<uint16_t *>(out);
-    p.out_fp32 = out_fp32;
-    p.lse = lse;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (events && n_events < QSA_FORWARD_STAGES + 1) return QSA_ERR_NULL;
-    if (mark(events, 0, s) != hipSuccess) return QSA_ERR_DEVICE;
-    if (launch_preprocess(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
-    if (launch_partial_keys(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
-    if (mark(events, 1, s) != hipSuccess) return QSA_ERR_DEVICE;
-    if (launch_forward(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
-    if (mark(events, 2, s) != hipSuccess) return QSA_ERR_DEVICE;
-    if (launch_forward_dense(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
-    if (mark(events, 3, s) != hipSuccess) return QSA_ERR_DEVICE;
-    return QSA_OK;
+    return run_forward(p, q, k, v, out, out_fp32, lse, static_cast<hipStream_t>(stream), events,
+                       true);
 }
 
 qsa_status qsa_forward(const qsa_dims *dims, const void *q, const void *k, const void *v,
@@ -322,49 +440,20 @@ qsa_status qsa_backward_timed(const qsa_dims *dims, const void *grad_out, const 
 {
     qsa_status st = check_dims(dims);
     if (st != QSA_OK) return st;
-    if (!grad_out || !q || !k || !v || !out_fp32 || !lse || !routes || !dq || !dk || !dv)
-        return QSA_ERR_NULL;
-    if ((st = check_scale(scale)) != QSA_OK) return st;
-    if (!aligned(grad_out, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
-        !aligned(out_fp32, 16) || !aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) ||
-        !aligned(dv, 16) || !aligned(routes, route_align(dims)))
-        return QSA_ERR_ALIGN;
-    const Layout L = layout(dims, 1);
-    if (!workspace || workspace_bytes < L.total) return QSA_ERR_WORKSPACE;
-    if (!aligned(workspace, 16)) return QSA_ERR_ALIGN;
+    if (!routes) return QSA_ERR_NULL;
+    if ((st = check_backward_args(grad_out, q, k, v, out_fp32, lse, scale, dq, dk, dv)) != QSA_OK)
+        return st;
+    if (!aligned(routes, route_align(dims))) return QSA_ERR_ALIGN;
+    const Layout L = layout(dims, kBackwardParts);
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != QSA_OK) return st;
+    if (events && n_events < QSA_BACKWARD_STAGES + 1) return QSA_ERR_NULL;
     if ((st = check_device(dims)) != QSA_OK) return st;
 
     Problem p;
     fill_common(p, dims, routes, scale);
     carve(p, L, workspace);
-    p.q = static_cast<const uint16_t *>(q);
-    p.k = static_cast<const uint16_t *>(k);
-    p.v = static_cast<const uint16_t *>(v);
-    p.dout = static_cast<const uint16_t *>(grad_out);
-    p.out_fp32_in = out_fp32;
-    p.lse_in = lse;
-    p.dq = static_cast<uint16_t *>(dq);
-    p.dk = static_cast<uint16_t *>(dk);
-    p.dv = static_cast<uint16_t *>(dv);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (events && n_events < QSA_BACKWARD_STAGES + 1) return QSA_ERR_NULL;
-    if (mark(events, 0, s) != hipSuccess) return QSA_ERR_DEVICE;
-    if (launch_preprocess(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
-    if (launch_partial_keys(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
-    if (mark(events, 1, s) != hipSuccess) return QSA_ERR_DEVICE;
-    if (launch_delta(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
-    if (mark(events, 2, s) != hipSuccess) return QSA_ERR_DEVICE;
-    if (launch_dq(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
-    if (mark(events, 3, s) != hipSuccess) return QSA_ERR_DEVICE;
-    if (launch_dq_dense(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
-    if (mark(events, 4, s) != hipSuccess) return QSA_ERR_DEVICE;
-    if (launch_dkdv(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
-    if (mark(events, 5, s) != hipSuccess) return QSA_ERR_DEVICE;
-    if (launch_dkdv_dense(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
-    if (mark(events, 6, s) != hipSuccess) return QSA_ERR_DEVICE;
-    if (launch_dkdv_reduce(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
-    if (mark(events, 7, s) != hipSuccess) return QSA_ERR_DEVICE;
-    return QSA_OK;
+    return run_backward(p, grad_out, q, k, v, out_fp32, lse, dq, dk, dv,
+                        static_cast<hipStream_t>(stream), events, true);
 }
 
 qsa_status qsa_backward(const qsa_dims *dims, const void *grad_out, const void *q, const void *k,
@@ -374,6 +463,115 @@ qsa_status qsa_backward(const qsa_dims *dims, const void *grad_out, const void *
 {
     return qsa_backward_timed(dims, grad_out, q, k, v, out_fp32, lse, routes, scale, dq, dk, dv,
                               workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+size_t qsa_plan_bytes(const qsa_dims *dims)
+{
+    return check_dims(dims) == QSA_OK ? layout(dims, kPlanParts).total : 0;
+}
+
+size_t qsa_forward_planned_workspace_bytes(const qsa_dims *dims)
+{
+    return check_dims(dims) == QSA_OK ? layout(dims, kFwd | kWalk).total : 0;
+}
+
+size_t qsa_backward_planned_workspace_bytes(const qsa_dims *dims)
+{
+    return check_dims(dims) == QSA_OK ? layout(dims, kBwd | kWalk).total : 0;
+}
+
+qsa_status qsa_plan_build(const qsa_dims *dims, const void *routes, void *plan_mem,
+                          size_t plan_bytes, qsa_plan *plan, void *stream)
+{
+    if (!plan) return QSA_ERR_NULL;
+    std::memset(plan, 0, sizeof(*plan));
+    qsa_status st = check_dims(dims);
+    if (st != QSA_OK) return st;
+    if (!routes) return QSA_ERR_NULL;
+    if (!aligned(routes, route_align(dims))) return QSA_ERR_ALIGN;
+    const Layout L = layout(dims, kPlanParts);
+    if ((st = check_workspace(plan_mem, plan_bytes, L.total)) != QSA_OK) return st;
+    if ((st = check_device(dims)) != QSA_OK) return st;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QSA_ERR_DEVICE;
+
+    Problem p;
+    fill_common(p, dims, routes, 1.f);
+    carve(p, L, plan_mem);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_preprocess(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (launch_partial_keys(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    plan->dims = *dims;
+    plan->mem = plan_mem;
+    plan->bytes = plan_bytes;
+    plan->device = dev;
+    plan->tag = QSA_PLAN_TAG;
+    return QSA_OK;
+}
+
+qsa_status qsa_forward_planned_timed(const qsa_plan *plan, const void *q, const void *k,
+                                     const void *v, float scale, void *out, float *out_fp32,
+                                     float *lse, void *workspace, size_t workspace_bytes,
+                                     void *stream, void *const *events, int32_t n_events)
+{
+    qsa_status st = check_plan(plan);
+    if (st != QSA_OK) return st;
+    const qsa_dims *dims = &plan->dims;
+    if ((st = check_forward_args(q, k, v, scale, out, out_fp32, lse)) != QSA_OK) return st;
+    const Layout L = layout(dims, kFwd | kWalk);
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != QSA_OK) return st;
+    if (events && n_events < QSA_FORWARD_STAGES + 1) return QSA_ERR_NULL;
+    if ((st = check_device(dims)) != QSA_OK) return st;
+    if ((st = check_plan_device(plan)) != QSA_OK) return st;
+
+    Problem p;
+    fill_common(p, dims, nullptr, scale);
+    carve(p, layout(dims, kPlanParts), plan->mem);
+    carve(p, L, workspace);
+    return run_forward(p, q, k, v, out, out_fp32, lse, static_cast<hipStream_t>(stream), events,
+                       false);
+}
+
+qsa_status qsa_forward_planned(const qsa_plan *plan, const void *q, const void *k, const void *v,
+                               float scale, void *out, float *out_fp32, float *lse,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    return qsa_forward_planned_timed(plan, q, k, v, scale, out, out_fp32, lse, workspace,
+                                     workspace_bytes, stream, nullptr, 0);
+}
+
+qsa_status qsa_backward_planned_timed(const qsa_plan *plan, const void *grad_out, const void *q,
+                                      const void *k, const void *v, const float *out_fp32,
+                                      const float *lse, float scale, void *dq, void *dk,
+                                      void *dv, void *workspace, size_t workspace_bytes,
+                                      void *stream, void *const *events, int32_t n_events)
+{
+    qsa_status st = check_plan(plan);
+    if (st != QSA_OK) return st;
+    const qsa_dims *dims = &plan->dims;
+    if ((st = check_backward_args(grad_out, q, k, v, out_fp32, lse, scale, dq, dk, dv)) != QSA_OK)
+        return st;
+    const Layout L = layout(dims, kBwd | kWalk);
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != QSA_OK) return st;
+    if (events && n_events < QSA_BACKWARD_STAGES + 1) return QSA_ERR_NULL;
+    if ((st = check_device(dims)) != QSA_OK) return st;
+    if ((st = check_plan_device(plan)) != QSA_OK) return st;
+
+    Problem p;
+    fill_common(p, dims, nullptr, scale);
+    carve(p, layout(dims, kPlanParts), plan->mem);
+    carve(p, L, workspace);
+    return run_backward(p, grad_out, q, k, v, out_fp32, lse, dq, dk, dv,
+                        static_cast<hipStream_t>(stream), events, false);
+}
+
+qsa_status qsa_backward_planned(const qsa_plan *plan, const void *grad_out, const void *q,
+                                const void *k, const void *v, const float *out_fp32,
+                                const float *lse, float scale, void *dq, void *dk, void *dv,
+                                void *workspace, size_t workspace_bytes, void *stream)
+{
+    return qsa_backward_planned_timed(plan, grad_out, q, k, v, out_fp32, lse, scale, dq, dk, dv,
+                                      workspace, workspace_bytes, stream, nullptr, 0);
 }
 
 qsa_status qsa_preprocess(const qsa_dims *dims, const void *routes, uint8_t *memb,
@@ -394,7 +592,7 @@ qsa_status qsa_preprocess(const qsa_dims *dims, const void *routes, uint8_t *mem
         !aligned(rev_f_idx, 4) || (row_keys && !aligned(row_keys, 4)) ||
         (row_cnt && !aligned(row_cnt, 4)) || !aligned(routes, route_align(dims)))
         return QSA_ERR_ALIGN;
-    const Layout L = layout(dims, 2);
+    const Layout L = layout(dims, kCore);
     if (!workspace || workspace_bytes < L.total) return QSA_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return QSA_ERR_ALIGN;
     if ((st = check_device(dims)) != QSA_OK) return st;
@@ -420,6 +618,54 @@ qsa_status qsa_preprocess(const qsa_dims *dims, const void *routes, uint8_t *mem
     return QSA_OK;
 }
 
+qsa_status qsa_plan_tables(const qsa_plan *plan, uint32_t *mbits, int32_t *kinds,
+                           int32_t *fwd_p_cnt, int32_t *fwd_p_idx, int32_t *fwd_f_cnt,
+                           int32_t *fwd_f_idx, int32_t *rev_p_cnt, int32_t *rev_p_idx,
+                           int32_t *rev_f_cnt, int32_t *rev_f_idx, int32_t *row_keys,
+                           int32_t *row_cnt, void *stream)
+{
+    qsa_status st = check_plan(plan);
+    if (st != QSA_OK) return st;
+    if (!mbits || !kinds || !fwd_p_cnt || !fwd_p_idx || !fwd_f_cnt || !fwd_f_idx || !rev_p_cnt ||
+        !rev_p_idx || !rev_f_cnt || !rev_f_idx || !row_keys || !row_cnt)
+        return QSA_ERR_NULL;
+    for (const void *x : {(const void *)mbits, (const void *)kinds, (const void *)fwd_p_cnt,
+                          (const void *)fwd_p_idx, (const void *)fwd_f_cnt,
+                          (const void *)fwd_f_idx, (const void *)rev_p_cnt,
+                          (const void *)rev_p_idx, (const void *)rev_f_cnt,
+                          (const void *)rev_f_idx, (const void *)row_keys, (const void *)row_cnt})
+        if (!aligned(x, 4)) return QSA_ERR_ALIGN;
+    if ((st = check_device(&plan->dims)) != QSA_OK) return st;
+    if ((st = check_plan_device(plan)) != QSA_OK) return st;
+    const qsa_dims *d = &plan->dims;
+    const Layout L = layout(d, kPlanParts);
+    const int64_t nQT = (d->Sq + kTile - 1) / kTile, nKT = (d->Skv + kTile - 1) / kTile;
+    const int64_t rows = d->B * d->Sq;
+    const char *m = static_cast<const char *>(plan->mem);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    struct Copy {
+        void *dst;
+        size_t at, bytes;
+    } copies[] = {
+        {mbits, L.mbits, (size_t)(rows * (nKT * kTile / 32)) * 4},
+        {kinds, L.kinds, (size_t)(d->B * nQT * nKT) * 4},
+        {fwd_p_cnt, L.fpc, (size_t)(d->B * nQT) * 4},
+        {fwd_p_idx, L.fpi, (size_t)(d->B * nQT * nKT) * 4},
+        {fwd_f_cnt, L.ffc, (size_t)(d->B * nQT) * 4},
+        {fwd_f_idx, L.ffi, (size_t)(d->B * nQT * nKT) * 4},
+        {rev_p_cnt, L.rpc, (size_t)(d->B * nKT) * 4},
+        {rev_p_idx, L.rpi, (size_t)(d->B * nKT * nQT) * 4},
+        {rev_f_cnt, L.rfc, (size_t)(d->B * nKT) * 4},
+        {rev_f_idx, L.rfi, (size_t)(d->B * nKT * nQT) * 4},
+        {row_keys, L.row_keys, (size_t)(rows * d->W) * 4},
+        {row_cnt, L.row_cnt, (size_t)rows * 4},
+    };
+    for (const Copy &c : copies)
+        if (hipMemcpyAsync(c.dst, m + c.at, c.bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+            return QSA_ERR_DEVICE;
+    return QSA_OK;
+}
+
 const char *qsa_status_string(qsa_status status)
 {
     switch (status) {
@@ -437,10 +683,13 @@ const char *qsa_status_string(qsa_status status)
     case QSA_ERR_SCRATCH:
         return "the call needs more workspace than the fixed device scratch of "
                "qsa_forward_noalloc holds (QSA_NOALLOC_SCRATCH_BYTES)";
+    case QSA_ERR_PLAN:
+        return "the plan was not built by qsa_plan_build, no longer matches its buffer, or was "
+               "built on another device";
     }
     return "unknown status";
 }
 
-int32_t qsa_version(void) { return (1 << 16) | 0; }
+int32_t qsa_version(void) { return (1 << 16) | 1; }
 
 }  // extern "C"

@@ -76,6 +76,7 @@ struct Problem {
 constexpr int kWalkRounds = 8;
 
 hipError_t launch_preprocess(const Problem &p, hipStream_t s);
+hipError_t launch_walk_reset(const Problem &p, hipStream_t s);
 hipError_t launch_partial_keys(const Problem &p, hipStream_t s);
 hipError_t launch_forward(const Problem &p, hipStream_t s);
 hipError_t launch_forward_dense(const Problem &p, hipStream_t s);

@@ -325,15 +325,24 @@ hipError_t launch_partial_keys(const Problem &p, hipStream_t s)
     return hipGetLastError();
 }
 
+hipError_t launch_walk_reset(const Problem &p, hipStream_t s)
+{
+    // A fill kernel, not a memset: callers may capture these launches in a
+    // graph.
+    if (p.walk)
+        hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, s, reinterpret_cast<int32_t *>(p.walk),
+                           (int64_t)16, 0);
+    return hipGetLastError();
+}
+
 hipError_t launch_preprocess(const Problem &p, hipStream_t s)
 {
     const int64_t ntiles = p.B * p.nQT * p.nKT;
     int blocks = (int)((ntiles + 255) / 256);
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL(k_fill_i32, dim3(blocks), dim3(256), 0, s, p.tile_cnt, ntiles, 0);
-    if (p.walk)
-        hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, s, reinterpret_cast<int32_t *>(p.walk),
-                           (int64_t)16, 0);
+    const hipError_t e = launch_walk_reset(p, s);
+    if (e != hipSuccess) return e;
     const size_t lds = prep_lds_base(p) + (prep_stage_keys(p) ? (size_t)p.W * 4 : 0);
     if (p.route_is_i64)
         hipLaunchKernelGGL(k_prep_rows<int64_t>, dim3((unsigned)(p.B * p.Sq)), dim3(kPrepThreads),

@@ -22,7 +22,8 @@ GROUP = 12
 HEAD_DIM = 256
 
 OK, ERR_NULL, ERR_SHAPE, ERR_HEADS, ERR_HEADDIM, ERR_SCALE, ERR_ALIGN, ERR_ROUTE_DTYPE, \
-    ERR_WORKSPACE, ERR_DEVICE, ERR_LAUNCH, ERR_SCRATCH = range(12)
+    ERR_WORKSPACE, ERR_DEVICE, ERR_LAUNCH, ERR_SCRATCH, ERR_PLAN = range(13)
+PLAN_TAG = 0x51534150  # QSA_PLAN_TAG
 NOALLOC_SCRATCH_BYTES = 64 << 20  # QSA_NOALLOC_SCRATCH_BYTES
 
 _lib = None
@@ -41,6 +42,12 @@ class Dims(ctypes.Structure):
                 ("flags", ctypes.c_int32)]
 
 
+class PlanStruct(ctypes.Structure):
+    """``qsa_plan``: the host record of a built route plan."""
+    _fields_ = [("dims", Dims), ("mem", ctypes.c_void_p), ("bytes", ctypes.c_size_t),
+                ("device", ctypes.c_int32), ("tag", ctypes.c_uint32)]
+
+
 def library() -> ctypes.CDLL:
     """The loaded HIP library; raises if it has not been built."""
     global _lib
@@ -51,7 +58,9 @@ def library() -> ctypes.CDLL:
         lib = ctypes.CDLL(LIB_PATH)
         P, S, D = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Dims)
         for name in ("qsa_forward_workspace_bytes", "qsa_backward_workspace_bytes",
-                     "qsa_preprocess_workspace_bytes"):
+                     "qsa_preprocess_workspace_bytes", "qsa_plan_bytes",
+                     "qsa_forward_planned_workspace_bytes",
+                     "qsa_backward_planned_workspace_bytes"):
             getattr(lib, name).restype = S
             getattr(lib, name).argtypes = [D]
         lib.qsa_forward.restype = ctypes.c_int
@@ -62,6 +71,16 @@ def library() -> ctypes.CDLL:
         lib.qsa_backward.argtypes = [D, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, S, P]
         lib.qsa_preprocess.restype = ctypes.c_int
         lib.qsa_preprocess.argtypes = [D] + [P] * 15 + [S, P]
+        PL = ctypes.POINTER(PlanStruct)
+        lib.qsa_plan_build.restype = ctypes.c_int
+        lib.qsa_plan_build.argtypes = [D, P, P, S, PL, P]
+        lib.qsa_forward_planned.restype = ctypes.c_int
+        lib.qsa_forward_planned.argtypes = [PL, P, P, P, ctypes.c_float, P, P, P, P, S, P]
+        lib.qsa_backward_planned.restype = ctypes.c_int
+        lib.qsa_backward_planned.argtypes = [PL, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, S,
+                                             P]
+        lib.qsa_plan_tables.restype = ctypes.c_int
+        lib.qsa_plan_tables.argtypes = [PL] + [P] * 12 + [P]
         lib.qsa_status_string.restype = ctypes.c_char_p
         lib.qsa_status_string.argtypes = [ctypes.c_int]
         lib.qsa_version.restype = ctypes.c_int32
@@ -75,7 +94,7 @@ def _raise(status: int) -> None:
         return
     msg = library().qsa_status_string(status).decode()
     if status in (ERR_SHAPE, ERR_HEADS, ERR_HEADDIM, ERR_SCALE, ERR_NULL, ERR_ALIGN,
-                  ERR_SCRATCH):
+                  ERR_SCRATCH, ERR_PLAN):
         raise ValueError(f"QSA status {status}: {msg}")
     if status == ERR_ROUTE_DTYPE:
         raise TypeError(f"QSA status {status}: {msg}")
@@ -268,5 +287,134 @@ def preprocess(routes: torch.Tensor, Skv: int, *, with_row_keys: bool = True) ->
                             *[out[n].data_ptr() for n in order],
                             _ptr(out.get("row_keys")), _ptr(out.get("row_cnt")),
                             ws.data_ptr(), need, _stream())
+    _raise(st)
+    return out
+
+
+class Plan:
+    """A built route plan: the ``qsa_plan`` record and the device buffer it names.
+
+    Keep the object alive while planned calls may still run on the stream: it
+    owns the buffer."""
+
+    def __init__(self, struct: PlanStruct, mem: torch.Tensor):
+        self.struct = struct
+        self.mem = mem
+
+    @property
+    def dims(self) -> Dims:
+        return self.struct.dims
+
+
+def plan_bytes(dims: Dims) -> int:
+    return int(library().qsa_plan_bytes(ctypes.byref(dims)))
+
+
+def plan_build(routes: torch.Tensor, Skv: int, *, Hkv: int = 1, deterministic: bool = False,
+               plan_mem: Optional[torch.Tensor] = None) -> Plan:
+    """Build the route plan of ``routes`` [B, Sq, W] for ``Skv`` keys and ``Hkv`` KV heads
+    (``qsa_plan_build``); forward_planned and backward_planned reuse it."""
+    routes = routes.contiguous()
+    if not routes.is_cuda:
+        raise ValueError("routes must be a GPU tensor")
+    if routes.dtype not in (torch.int32, torch.int64):
+        raise TypeError("routes must be int32 or int64")
+    if routes.dim() != 3:
+        raise ValueError("routes must be [B, Sq, W]")
+    B, Sq, W = routes.shape
+    dims = make_dims(B, Sq, Skv, GROUP * Hkv, Hkv, HEAD_DIM, W, routes.dtype == torch.int64,
+                     deterministic)
+    lib = library()
+    need = lib.qsa_plan_bytes(ctypes.byref(dims))
+    mem = _workspace(need, routes.device, plan_mem)
+    struct = PlanStruct()
+    st = lib.qsa_plan_build(ctypes.byref(dims), routes.data_ptr(), mem.data_ptr(),
+                            mem.numel() * mem.element_size(), ctypes.byref(struct), _stream())
+    _raise(st)
+    return Plan(struct, mem)
+
+
+def _plan_shapes(plan: Plan):
+    d = plan.dims
+    return (d.B, d.Sq, d.Hq, d.D), (d.B, d.Skv, d.Hkv, d.D), (d.B, d.Hq, d.Sq)
+
+
+def forward_planned(plan: Plan, q, k, v, scale: Optional[float] = None, *, out=None,
+                    out_fp32=None, lse=None, workspace=None):
+    """QSA forward on a built plan (``qsa_forward_planned``): no route preprocessing."""
+    q = _check(q, torch.bfloat16, "q")
+    k = _check(k, torch.bfloat16, "k")
+    v = _check(v, torch.bfloat16, "v")
+    qs, ks, ls = _plan_shapes(plan)
+    if tuple(q.shape) != qs or tuple(k.shape) != ks or tuple(v.shape) != ks:
+        raise ValueError(f"q must be {qs} and k, v {ks} for this plan")
+    if scale is None:
+        scale = 1.0 / (q.shape[-1] ** 0.5)
+    out = torch.empty_like(q) if out is None else out
+    out_fp32 = torch.empty(qs, dtype=torch.float32, device=q.device) if out_fp32 is None \
+        else out_fp32
+    lse = torch.empty(ls, dtype=torch.float32, device=q.device) if lse is None else lse
+    lib = library()
+    need = lib.qsa_forward_planned_workspace_bytes(ctypes.byref(plan.dims))
+    ws = _workspace(need, q.device, workspace)
+    st = lib.qsa_forward_planned(ctypes.byref(plan.struct), q.data_ptr(), k.data_ptr(),
+                                 v.data_ptr(), float(scale), out.data_ptr(), out_fp32.data_ptr(),
+                                 lse.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                 _stream())
+    _raise(st)
+    return out, out_fp32, lse
+
+
+def backward_planned(plan: Plan, grad_out, q, k, v, out_fp32, lse, scale: Optional[float] = None,
+                     *, dq=None, dk=None, dv=None, workspace=None):
+    """QSA backward on a built plan (``qsa_backward_planned``): no route preprocessing."""
+    grad_out = _check(grad_out, torch.bfloat16, "grad_out")
+    q = _check(q, torch.bfloat16, "q")
+    k = _check(k, torch.bfloat16, "k")
+    v = _check(v, torch.bfloat16, "v")
+    out_fp32 = _check(out_fp32, torch.float32, "out_fp32")
+    lse = _check(lse, torch.float32, "lse")
+    qs, ks, ls = _plan_shapes(plan)
+    if tuple(q.shape) != qs or tuple(grad_out.shape) != qs or tuple(out_fp32.shape) != qs:
+        raise ValueError(f"q, grad_out and out_fp32 must be {qs} for this plan")
+    if tuple(k.shape) != ks or tuple(v.shape) != ks:
+        raise ValueError(f"k and v must be {ks} for this plan")
+    if tuple(lse.shape) != ls:
+        raise ValueError(f"lse must be {ls} for this plan")
+    if scale is None:
+        scale = 1.0 / (q.shape[-1] ** 0.5)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    lib = library()
+    need = lib.qsa_backward_planned_workspace_bytes(ctypes.byref(plan.dims))
+    ws = _workspace(need, q.device, workspace)
+    st = lib.qsa_backward_planned(ctypes.byref(plan.struct), grad_out.data_ptr(), q.data_ptr(),
+                                  k.data_ptr(), v.data_ptr(), out_fp32.data_ptr(),
+                                  lse.data_ptr(), float(scale), dq.data_ptr(), dk.data_ptr(),
+                                  dv.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                  _stream())
+    _raise(st)
+    return dq, dk, dv
+
+
+def plan_tables(plan: Plan) -> dict:
+    """Copies of a plan's tables (``qsa_plan_tables``) as GPU tensors."""
+    d = plan.dims
+    nqt, nkt = -(-d.Sq // TILE), -(-d.Skv // TILE)
+    dev = plan.mem.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = {
+        "mbits": torch.empty((d.B, d.Sq, nkt * TILE // 32), **i32),
+        "kinds": torch.empty((d.B, nqt, nkt), **i32),
+        "fwd_p_cnt": torch.empty((d.B, nqt), **i32), "fwd_p_idx": torch.empty((d.B, nqt, nkt), **i32),
+        "fwd_f_cnt": torch.empty((d.B, nqt), **i32), "fwd_f_idx": torch.empty((d.B, nqt, nkt), **i32),
+        "rev_p_cnt": torch.empty((d.B, nkt), **i32), "rev_p_idx": torch.empty((d.B, nkt, nqt), **i32),
+        "rev_f_cnt": torch.empty((d.B, nkt), **i32), "rev_f_idx": torch.empty((d.B, nkt, nqt), **i32),
+        "row_keys": torch.empty((d.B, d.Sq, d.W), **i32),
+        "row_cnt": torch.empty((d.B, d.Sq), **i32),
+    }
+    st = library().qsa_plan_tables(ctypes.byref(plan.struct), *[t.data_ptr() for t in out.values()],
+                                   _stream())
     _raise(st)
     return out
