@@ -57,6 +57,8 @@ def _load():
         lib.orc_route_set.argtypes = [P, ctypes.c_int32, I, I, I, P]
         lib.orc_membership.restype = None
         lib.orc_membership.argtypes = [P, ctypes.c_int32, I, I, I, I, I, P, P]
+        lib.orc_block_membership.restype = None
+        lib.orc_block_membership.argtypes = [P, I, I, P, P, P, P, I, I, P, P]
         lib.orc_tiles.restype = None
         lib.orc_tiles.argtypes = [P, I, I, I, I, I, I] + [P] * 9
         for name in ("orc_forward", "orc_backward_dq"):
@@ -117,6 +119,38 @@ def membership(routes: np.ndarray, Skv: int) -> tuple[np.ndarray, np.ndarray]:
     has = np.empty((B, Sq), dtype=np.uint8)
     _load().orc_membership(_ptr(r), i64, B, Sq, W, Skv, stride, _ptr(memb), _ptr(has))
     return memb, has
+
+
+def block_membership(sel_blocks: np.ndarray, lo: np.ndarray, hi: np.ndarray,
+                     blk_base: np.ndarray, tok_base: np.ndarray,
+                     block_size: int = 4) -> tuple[np.ndarray, np.ndarray]:
+    """Byte membership ``[1, T, stride]`` and ``has_routes`` ``[1, T]`` of a block-bitmap
+    selection over T packed tokens (the lookup of the cuDNN Frontend QSA page,
+    "Selection and components"); ``sel_blocks`` is uint8 ``[T, NB]``, the rest int32."""
+    sel = np.ascontiguousarray(sel_blocks, dtype=np.uint8)
+    T, NB = sel.shape
+    meta = [np.ascontiguousarray(a, dtype=np.int32) for a in (lo, hi, blk_base, tok_base)]
+    assert all(a.shape == (T,) for a in meta)
+    stride = row_stride(T)
+    memb = np.empty((1, T, stride), dtype=np.uint8)
+    has = np.empty((1, T), dtype=np.uint8)
+    _load().orc_block_membership(_ptr(sel), T, NB, *[_ptr(a) for a in meta], block_size, stride,
+                                 _ptr(memb), _ptr(has))
+    return memb, has
+
+
+def routes_from_membership(memb: np.ndarray, Skv: int) -> np.ndarray:
+    """Route rows listing each row's members in ascending order, -1 padded: the same
+    sets as ``memb``, for building a :class:`Problem`."""
+    B, Sq, _ = memb.shape
+    m = memb[:, :, :Skv].reshape(B * Sq, Skv) != 0
+    cnt = m.sum(axis=1)
+    W = max(int(cnt.max()) if cnt.size else 0, 1)
+    routes = np.full((B * Sq, W), -1, dtype=np.int32)
+    rows, cols = np.nonzero(m)
+    pos = np.arange(rows.size) - np.repeat(np.cumsum(cnt) - cnt, cnt)
+    routes[rows, pos] = cols
+    return routes.reshape(B, Sq, W)
 
 
 def tiles(memb: np.ndarray, Skv: int, tq: int = TILE, tk: int = TILE) -> dict:

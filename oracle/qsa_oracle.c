@@ -18,6 +18,13 @@
  *    per tile row and per tile column, the partial and the full tile indices in
  *    ascending order. ("fa4_qsa" page, `_block_kinds`, `_compact_blocks`;
  *    "flex_qsa" page, `_dense_blocks_to_ordered`.)
+ *  - Block-bitmap selection. For packed tokens t, j in [0, T): key j is
+ *    allowed for query t iff lo[t] <= j <= hi[t], 0 <= b < NB and
+ *    sel_blocks[t, b] != 0, with b = blk_base[t] + floor((j - tok_base[t]) /
+ *    block_size) (floor division, so a key before the query's token origin
+ *    maps to an earlier block). This is the lookup of the cuDNN Frontend QSA
+ *    page, section "Selection and components"; the per-block token spans
+ *    (block_first, block_last) do not enter it.
  *  - Forward. For every query head h of KV group g = h / (Hq / Hkv):
  *    s_j = scale * <q, k_j> over j in R, lse = log sum_j exp(s_j),
  *    o = sum_j exp(s_j - lse) v_j; an empty R gives o = 0 and lse = -inf.
@@ -110,6 +117,37 @@ void orc_membership(const void *routes, int32_t is_i64, int64_t B, int64_t Sq, i
  * the table); kind 0 if cnt == 0, 2 if cnt == tq * tk, else 1. Lists hold the
  * matching tile indices in ascending order, then -1.
  */
+/* floor(a / d) for d > 0, also for negative a. */
+static int64_t floor_div(int64_t a, int64_t d)
+{
+    int64_t q = a / d;
+    if ((a % d) != 0 && a < 0) q -= 1;
+    return q;
+}
+
+/* Byte membership [1, T, stride] and has_routes [1, T] of a block-bitmap
+ * selection: every (t, j) evaluated with the lookup above. */
+void orc_block_membership(const uint8_t *sel, int64_t T, int64_t NB, const int32_t *lo,
+                          const int32_t *hi, const int32_t *blk_base, const int32_t *tok_base,
+                          int64_t block_size, int64_t stride, uint8_t *memb, uint8_t *has)
+{
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < T; ++t) {
+        uint8_t *row = memb + t * stride;
+        int any = 0;
+        for (int64_t j = 0; j < stride; ++j) {
+            int allowed = 0;
+            if (j < T && lo[t] <= j && j <= hi[t]) {
+                const int64_t b = (int64_t)blk_base[t] + floor_div(j - (int64_t)tok_base[t], block_size);
+                allowed = b >= 0 && b < NB && sel[t * NB + b] != 0;
+            }
+            row[j] = (uint8_t)allowed;
+            any |= allowed;
+        }
+        has[t] = (uint8_t)any;
+    }
+}
+
 void orc_tiles(const uint8_t *memb, int64_t B, int64_t Sq, int64_t Skv, int64_t stride,
                int64_t tq, int64_t tk, int32_t *kinds, int32_t *fwd_p_cnt, int32_t *fwd_p_idx,
                int32_t *fwd_f_cnt, int32_t *fwd_f_idx, int32_t *rev_p_cnt, int32_t *rev_p_idx,

@@ -89,8 +89,10 @@ WORKLOADS: Dict[int, Workload] = {
 }
 
 
-def _row(out: np.ndarray, n_max: int, doc_start: int, pos: int, chosen: np.ndarray) -> None:
-    """Write one route row for a query at ``pos`` in a document starting at ``doc_start``."""
+def _row(out: np.ndarray, n_max: int, doc_start: int, pos: int, chosen: np.ndarray,
+         record: Optional[list] = None) -> None:
+    """Write one route row for a query at ``pos`` in a document starting at ``doc_start``;
+    with ``record``, also append (doc_start, chosen block numbers, own block number)."""
     out.fill(-1)
     chosen = np.sort(np.asarray(chosen, dtype=np.int64))
     n = chosen.shape[0]
@@ -100,6 +102,8 @@ def _row(out: np.ndarray, n_max: int, doc_start: int, pos: int, chosen: np.ndarr
     c = (pos - doc_start) // 4
     own = np.arange(doc_start + 4 * c, pos + 1, dtype=np.int64)
     out[4 * n_max: 4 * n_max + own.shape[0]] = own
+    if record is not None:
+        record.append((doc_start, chosen, c))
 
 
 def _choose(rng: np.random.Generator, population: int, k: int) -> np.ndarray:
@@ -109,18 +113,26 @@ def _choose(rng: np.random.Generator, population: int, k: int) -> np.ndarray:
     return rng.choice(population, k, replace=False)
 
 
-def make_routes(wl: Workload, rng: np.random.Generator) -> tuple[np.ndarray, dict]:
-    """Draw the route tensor ``[B, Sq, W]`` (int32) for ``wl``; return it and the structure."""
+def make_routes(wl: Workload, rng: np.random.Generator,
+                record_blocks: bool = False) -> tuple[np.ndarray, dict]:
+    """Draw the route tensor ``[B, Sq, W]`` (int32) for ``wl``; return it and the structure.
+
+    With ``record_blocks``, ``info["row_blocks"][b * Sq + i]`` holds the row's
+    (doc_start, chosen complete block numbers, own block number), None for a row
+    without routes; the draws are the same either way."""
     B, Sq, W, n_max = wl.B, wl.Sq, wl.W, wl.n_max
     routes = np.full((B, Sq, W), -1, dtype=np.int32)
     row = np.empty(W, dtype=np.int64)
     info: dict = {}
+    rec: Optional[list] = [] if record_blocks else None
+    if rec is not None:
+        info["row_blocks"] = rec
     if wl.kind == "single":
         for b in range(B):
             for i in range(Sq):
                 p = wl.q_offset + i
                 c = p // 4
-                _row(row, n_max, 0, p, _choose(rng, c, min(n_max, c)))
+                _row(row, n_max, 0, p, _choose(rng, c, min(n_max, c)), rec)
                 routes[b, i] = row
     elif wl.kind == "docs":
         assert B == 1 and wl.q_offset == 0
@@ -131,7 +143,7 @@ def make_routes(wl: Workload, rng: np.random.Generator) -> tuple[np.ndarray, dic
         for i in range(Sq):
             s = int(starts[doc_of[i]])
             c = (i - s) // 4
-            _row(row, n_max, s, i, _choose(rng, c, min(n_max, c)))
+            _row(row, n_max, s, i, _choose(rng, c, min(n_max, c)), rec)
             routes[0, i] = row
     elif wl.kind == "padded":
         lengths = np.array([rng.integers(wl.len_lo, wl.len_hi, endpoint=True) for _ in range(B)],
@@ -140,8 +152,10 @@ def make_routes(wl: Workload, rng: np.random.Generator) -> tuple[np.ndarray, dic
         for b in range(B):
             for i in range(int(lengths[b])):
                 c = i // 4
-                _row(row, n_max, 0, i, _choose(rng, c, min(n_max, c)))
+                _row(row, n_max, 0, i, _choose(rng, c, min(n_max, c)), rec)
                 routes[b, i] = row
+            if rec is not None:
+                rec.extend([None] * (Sq - int(lengths[b])))
     elif wl.kind == "recent_earlier":
         R = wl.recent_blocks
         for b in range(B):
@@ -150,7 +164,7 @@ def make_routes(wl: Workload, rng: np.random.Generator) -> tuple[np.ndarray, dic
                 lo = max(0, c - R)
                 recent = np.arange(lo, c, dtype=np.int64)
                 earlier = _choose(rng, lo, min(n_max - R, lo))
-                _row(row, n_max, 0, i, np.concatenate([earlier, recent]))
+                _row(row, n_max, 0, i, np.concatenate([earlier, recent]), rec)
                 routes[b, i] = row
     else:
         raise ValueError(f"unknown route recipe {wl.kind!r}")
@@ -168,10 +182,10 @@ class Inputs:
     info: dict
 
 
-def make_inputs(wl: Workload, with_grad: bool = True) -> Inputs:
+def make_inputs(wl: Workload, with_grad: bool = True, record_blocks: bool = False) -> Inputs:
     """All inputs of workload ``wl``, drawn from ``numpy.random.default_rng(wl.seed)``."""
     rng = np.random.default_rng(wl.seed)
-    routes, info = make_routes(wl, rng)
+    routes, info = make_routes(wl, rng, record_blocks)
     q = bf16_bits(rng.standard_normal((wl.B, wl.Sq, wl.Hq, wl.D), dtype=np.float32))
     k = bf16_bits(rng.standard_normal((wl.B, wl.Skv, wl.Hkv, wl.D), dtype=np.float32))
     v = bf16_bits(rng.standard_normal((wl.B, wl.Skv, wl.Hkv, wl.D), dtype=np.float32))
@@ -281,3 +295,91 @@ def tiled_case(seed: int, B: int, Sq: int, Skv: int, Hq: int, Hkv: int, p_full: 
     go = bf16_bits(rng.standard_normal((B, Sq, Hq, D), dtype=np.float32))
     wl = Workload(f"tiled_{seed}", B, Sq, Skv, Hq, Hkv, D, 0, "tiled", seed)
     return Inputs(wl, routes, q, k, v, go, {"W": W})
+
+
+@dataclasses.dataclass
+class BlockInputs:
+    """A workload in the packed block-bitmap form: T packed tokens, NB blocks."""
+    T: int
+    NB: int
+    sel_blocks: np.ndarray   # uint8 [T, NB]
+    lo: np.ndarray           # int32 [T], inclusive allowed key-token bounds
+    hi: np.ndarray
+    blk_base: np.ndarray     # int32 [T], first block of the query's sequence
+    tok_base: np.ndarray     # int32 [T], first token of the query's sequence
+    block_first: np.ndarray  # int32 [NB], inclusive token span of each block
+    block_last: np.ndarray
+    q: np.ndarray            # uint16 [1, T, Hq, D]
+    k: np.ndarray            # uint16 [1, T, Hkv, D]
+    v: np.ndarray
+    grad_out: np.ndarray
+    routes: np.ndarray       # int32 [1, T, W]: the same selection as packed route rows
+
+
+def block_inputs(inp: Inputs) -> BlockInputs:
+    """Re-express a workload drawn with ``record_blocks`` as packed sequences with a
+    block-selection bitmap (the Miles packed-training layout of the cuDNN Frontend
+    QSA page, "Tensors"): batch b's positions become tokens b * Sq + i; every
+    document of a batch row is a sequence with its own block numbering (four
+    tokens per block from the document's first token, the last block possibly
+    shorter); a row selects the blocks its routes were drawn from, including its
+    own incomplete block; lo is its sequence's first token and hi its own token.
+    Rows without routes get lo = 0, hi = -1 and no selected block. The bitmap is
+    built from the drawn block numbers, never from the route values."""
+    wl = inp.wl
+    rec = inp.info.get("row_blocks")
+    if rec is None:
+        raise ValueError("draw the workload with record_blocks=True")
+    if wl.Sq != wl.Skv or wl.q_offset != 0:
+        raise ValueError("the packed form needs as many keys as queries and no query offset")
+    B, Sq = wl.B, wl.Sq
+    T = B * Sq
+    starts = [int(x) for x in inp.info.get("doc_starts", [0])]
+    # sequences: (batch, start, end) in token order, with their first block
+    seqs = []
+    nb = 0
+    for b in range(B):
+        bounds = starts + [Sq]
+        for s0, s1 in zip(bounds[:-1], bounds[1:]):
+            seqs.append((b, s0, s1, nb))
+            nb += -(-(s1 - s0) // 4)
+    NB = nb
+    block_first = np.empty(NB, np.int32)
+    block_last = np.empty(NB, np.int32)
+    base_of = {}
+    for b, s0, s1, bb in seqs:
+        n = -(-(s1 - s0) // 4)
+        first = b * Sq + s0 + 4 * np.arange(n)
+        block_first[bb:bb + n] = first
+        block_last[bb:bb + n] = np.minimum(first + 3, b * Sq + s1 - 1)
+        base_of[(b, s0)] = bb
+    sel = np.zeros((T, NB), np.uint8)
+    lo = np.zeros(T, np.int32)
+    hi = np.full(T, -1, np.int32)
+    blk_base = np.zeros(T, np.int32)
+    tok_base = np.zeros(T, np.int32)
+    for t in range(T):
+        b, i = divmod(t, Sq)
+        s0 = max(x for x in starts if x <= i)
+        bb = base_of[(b, s0)]
+        blk_base[t] = bb
+        tok_base[t] = b * Sq + s0
+        r = rec[t]
+        if r is None:
+            continue
+        doc_start, chosen, own = r
+        assert doc_start == s0
+        sel[t, bb + chosen] = 1
+        sel[t, bb + own] = 1
+        lo[t] = b * Sq + s0
+        hi[t] = t
+    W = inp.routes.shape[2]
+    off = (np.arange(B, dtype=np.int64) * Sq)[:, None, None]
+    r = inp.routes.astype(np.int64)
+    packed = np.where((r >= 0) & (r < wl.Skv), r + off, -1).reshape(1, T, W).astype(np.int32)
+    shape_q = (1, T) + inp.q.shape[2:]
+    shape_k = (1, T) + inp.k.shape[2:]
+    go = inp.grad_out.reshape(shape_q) if inp.grad_out is not None else None
+    return BlockInputs(T, NB, sel, lo, hi, blk_base, tok_base, block_first, block_last,
+                       inp.q.reshape(shape_q), inp.k.reshape(shape_k), inp.v.reshape(shape_k),
+                       go, packed)
