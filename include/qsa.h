@@ -222,6 +222,70 @@ qsa_status qsa_backward_planned(const qsa_plan *plan, const void *grad_out, cons
                                 const float *lse, float scale, void *dq, void *dk, void *dv,
                                 void *workspace, size_t workspace_bytes, void *stream);
 /*
+ * Block-bitmap selection over packed sequences: the Miles packed-training
+ * interface of the cuDNN Frontend QSA page (sections "API" for the two
+ * calls, "Tensors" for the layouts, "Selection and components" for the
+ * lookup). T packed tokens are both the queries and the keys; NB blocks
+ * cover all sequences. Key j is allowed for query t iff
+ *     lo[t] <= j <= hi[t], 0 <= b < NB and sel_blocks[t, b] != 0,
+ *     with b = blk_base[t] + floor((j - tok_base[t]) / block_size),
+ * floor division for any sign. Everything else (forward, backward, empty
+ * rows, no gradient for the selection) is as for route rows: a block
+ * selection is expanded on the device into the same per-row key sets.
+ *
+ * Layouts (device pointers; int32 metadata 4-byte aligned, tensors as
+ * above): q, out, grad_out, dq [T, Hq, 256]; k, v, dk, dv [T, Hkv, 256];
+ * out_fp32 [T, Hq, 256]; lse [Hq, T]; sel_blocks uint8 [T, NB] (nonzero
+ * selects); lo, hi, blk_base, tok_base int32 [T]; block_first, block_last
+ * int32 [NB]. These are the shapes of qsa_dims with B = 1 and Sq = Skv = T.
+ *
+ * block_size must be 4. The metadata are a caller contract, as on that
+ * page: nothing is read on the host, and invalid metadata give the
+ * selection the lookup defines for them. The block spans block_first and
+ * block_last are validated as pointers but not read: for a valid partition
+ * they are what the lookup implies (block b of a sequence holds its tokens
+ * tok_base + 4 (b - blk_base) .. + 3), and the lookup alone decides
+ * membership.
+ *
+ * Memory: a row of a block selection can hold up to min(T, 4 NB) keys, and
+ * the per-row key lists are sized for that (about 8 T min(T, 4 NB) bytes
+ * in the plan, 8.6 GB at T = 32768 with NB = 8192).
+ *
+ * qsa_block_plan_build builds an ordinary qsa_plan (dims B = 1, Sq = Skv =
+ * T, W = min(T, 4 NB), route_is_i64 = 0) for the planned calls and
+ * qsa_plan_tables. qsa_block_forward and qsa_block_backward are the one-call
+ * forms: each builds the plan at the start of its workspace, then runs the
+ * planned call (so each call reads the current selection, as on that page).
+ */
+typedef struct qsa_block_dims {
+    int64_t T;          /* packed tokens */
+    int64_t NB;         /* blocks across all sequences, 1 <= NB <= 2^31 - 1 */
+    int64_t Hq, Hkv, D; /* as in qsa_dims */
+    int32_t block_size; /* must be 4 */
+    int32_t flags;      /* QSA_FLAG_* bits */
+} qsa_block_dims;
+size_t qsa_block_plan_bytes(const qsa_block_dims *dims);
+size_t qsa_block_forward_workspace_bytes(const qsa_block_dims *dims);
+size_t qsa_block_backward_workspace_bytes(const qsa_block_dims *dims);
+qsa_status qsa_block_plan_build(const qsa_block_dims *dims, const uint8_t *sel_blocks,
+                                const int32_t *lo, const int32_t *hi, const int32_t *blk_base,
+                                const int32_t *tok_base, const int32_t *block_first,
+                                const int32_t *block_last, void *plan_mem, size_t plan_bytes,
+                                qsa_plan *plan, void *stream);
+qsa_status qsa_block_forward(const qsa_block_dims *dims, const void *q, const void *k,
+                             const void *v, const uint8_t *sel_blocks, const int32_t *lo,
+                             const int32_t *hi, const int32_t *blk_base, const int32_t *tok_base,
+                             const int32_t *block_first, const int32_t *block_last, float scale,
+                             void *out, float *out_fp32, float *lse, void *workspace,
+                             size_t workspace_bytes, void *stream);
+qsa_status qsa_block_backward(const qsa_block_dims *dims, const void *grad_out, const void *q,
+                              const void *k, const void *v, const float *out_fp32,
+                              const float *lse, const uint8_t *sel_blocks, const int32_t *lo,
+                              const int32_t *hi, const int32_t *blk_base, const int32_t *tok_base,
+                              const int32_t *block_first, const int32_t *block_last, float scale,
+                              void *dq, void *dk, void *dv, void *workspace,
+                              size_t workspace_bytes, void *stream);
+/*
  * Copies of a built plan's tables, for inspection and bit-exact checks, in
  * the layouts qsa_preprocess documents, except that the membership comes bit
  * packed: mbits uint32 [B, Sq, stride / 32], bit (j % 32) of word j / 32 set

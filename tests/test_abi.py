@@ -34,7 +34,10 @@ def test_header_declares_the_entry_points():
               "qsa_forward_timed", "qsa_backward_timed", "qsa_bench_gather",
               "qsa_plan_bytes", "qsa_plan_build", "qsa_forward_planned", "qsa_backward_planned",
               "qsa_forward_planned_workspace_bytes", "qsa_backward_planned_workspace_bytes",
-              "qsa_plan_tables", "qsa_forward_planned_timed", "qsa_backward_planned_timed"):
+              "qsa_plan_tables", "qsa_forward_planned_timed", "qsa_backward_planned_timed",
+              "qsa_block_plan_bytes", "qsa_block_plan_build", "qsa_block_forward",
+              "qsa_block_backward", "qsa_block_forward_workspace_bytes",
+              "qsa_block_backward_workspace_bytes"):
         assert n in names
 
 
@@ -224,3 +227,61 @@ def test_planned_calls_reject_unbuilt_or_edited_plans(lib):
         assert fwd(ctypes.byref(ok)) == 9
         assert bwd(ctypes.byref(ok)) == 9
         assert tables(ctypes.byref(ok)) == 9
+
+
+def test_block_entries_validate_before_touching_the_device(lib):
+    import torch
+    from token_indexed_sparse_amd import qsa
+    a = ctypes.c_void_p(4096)
+    bd = qsa.block_dims(300, 80)
+    need_f = lib.qsa_block_forward_workspace_bytes(ctypes.byref(bd))
+    need_b = lib.qsa_block_backward_workspace_bytes(ctypes.byref(bd))
+    plan = lib.qsa_block_plan_bytes(ctypes.byref(bd))
+    # the per-row key capacity is min(T, 4 NB): the plan equals a route plan of that width
+    d = _dims(Sq=300, Skv=300, W=300)
+    assert plan == lib.qsa_plan_bytes(ctypes.byref(d))
+    assert lib.qsa_block_plan_bytes(ctypes.byref(qsa.block_dims(300, 20))) == \
+        lib.qsa_plan_bytes(ctypes.byref(_dims(Sq=300, Skv=300, W=80)))
+    assert need_f == plan + lib.qsa_forward_planned_workspace_bytes(ctypes.byref(d))
+    assert need_b == plan + lib.qsa_backward_planned_workspace_bytes(ctypes.byref(d))
+
+    def fwd(bd, meta=(a,) * 7, ws=need_f, scale=0.0625):
+        return lib.qsa_block_forward(ctypes.byref(bd), a, a, a, *meta, scale, a, a, a, a, ws, None)
+
+    def bwd(bd, meta=(a,) * 7, ws=need_b, scale=0.0625):
+        return lib.qsa_block_backward(ctypes.byref(bd), a, a, a, a, a, a, *meta, scale, a, a, a, a,
+                                      ws, None)
+
+    def build(bd, meta=(a,) * 7, nbytes=plan):
+        pl = qsa.PlanStruct(tag=5)
+        st = lib.qsa_block_plan_build(ctypes.byref(bd), *meta, a, nbytes, ctypes.byref(pl), None)
+        assert pl.tag == 0
+        return st
+
+    for call in (fwd, bwd, build):
+        assert call(qsa.block_dims(300, 80, block_size=2)) == 2
+        assert call(qsa.block_dims(0, 80)) == 2
+        assert call(qsa.block_dims(300, 0)) == 2
+        assert call(qsa.block_dims(300, 1 << 31)) == 2
+        assert call(qsa.BlockDims(300, 80, 16, 1, 256, 4, 0)) == 3
+        assert call(qsa.BlockDims(300, 80, 12, 1, 128, 4, 0)) == 4
+        assert call(qsa.block_dims(300, 80, deterministic=True)) != 7
+        assert call(qsa.BlockDims(300, 80, 12, 1, 256, 4, 2)) == 7
+        for x in range(7):  # every metadata pointer is required
+            meta = [a] * 7
+            meta[x] = None
+            assert call(bd, meta=tuple(meta)) == 1
+        for x in range(1, 7):  # int32 metadata are 4-byte aligned; the uint8 bitmap is not
+            meta = [a] * 7
+            meta[x] = ctypes.c_void_p(4098)
+            assert call(bd, meta=tuple(meta)) == 6
+    assert fwd(bd, ws=need_f - 1) == 8
+    assert bwd(bd, ws=need_b - 1) == 8
+    assert build(bd, nbytes=plan - 1) == 8
+    assert fwd(bd, scale=float("inf")) == 5
+    assert lib.qsa_block_plan_build(ctypes.byref(bd), *([a] * 7), a, plan, None, None) == 1
+    if not torch.cuda.is_available():
+        unaligned_sel = (ctypes.c_void_p(4097),) + (a,) * 6
+        assert fwd(bd, meta=unaligned_sel) == 9
+        assert bwd(bd) == 9
+        assert build(bd) == 9

@@ -4,6 +4,7 @@
 #include "../../include/qsa_bench.h"
 
 #include <cmath>
+#include <climits>
 #include <cstring>
 #include <mutex>
 
@@ -317,6 +318,64 @@ qsa_status check_plan_device(const qsa_plan *plan)
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return QSA_ERR_DEVICE;
     return dev == plan->device ? QSA_OK : QSA_ERR_PLAN;
+}
+
+// The route-set dims of a block-bitmap call: one batch of T packed tokens as
+// queries and keys, and a per-row key capacity that no selection can exceed
+// (a block holds at most four keys of a row's range, so at most 4 NB keys,
+// and there are T keys in all).
+qsa_status block_dims(const qsa_block_dims *bd, qsa_dims *d)
+{
+    if (!bd) return QSA_ERR_NULL;
+    if (bd->block_size != 4 || bd->T < 1 || bd->NB < 1 || bd->NB > INT32_MAX)
+        return QSA_ERR_SHAPE;
+    d->B = 1;
+    d->Sq = d->Skv = bd->T;
+    d->Hq = bd->Hq;
+    d->Hkv = bd->Hkv;
+    d->D = bd->D;
+    d->W = bd->T < 4 * bd->NB ? bd->T : 4 * bd->NB;
+    d->route_is_i64 = 0;
+    d->flags = bd->flags;
+    return check_dims(d);
+}
+
+qsa_status check_block_meta(const uint8_t *sel, const int32_t *lo, const int32_t *hi,
+                            const int32_t *blk_base, const int32_t *tok_base,
+                            const int32_t *block_first, const int32_t *block_last)
+{
+    if (!sel || !lo || !hi || !blk_base || !tok_base || !block_first || !block_last)
+        return QSA_ERR_NULL;
+    if (!aligned(lo, 4) || !aligned(hi, 4) || !aligned(blk_base, 4) || !aligned(tok_base, 4) ||
+        !aligned(block_first, 4) || !aligned(block_last, 4))
+        return QSA_ERR_ALIGN;
+    return QSA_OK;
+}
+
+// Build a plan from a block selection into plan_mem (validated by the caller).
+qsa_status build_block_plan(const qsa_dims *d, int64_t NB, const uint8_t *sel, const int32_t *lo,
+                            const int32_t *hi, const int32_t *blk_base, const int32_t *tok_base,
+                            void *plan_mem, size_t plan_bytes, qsa_plan *plan, hipStream_t s)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QSA_ERR_DEVICE;
+    Problem p;
+    fill_common(p, d, nullptr, 1.f);
+    p.sel = sel;
+    p.sel_lo = lo;
+    p.sel_hi = hi;
+    p.sel_blk_base = blk_base;
+    p.sel_tok_base = tok_base;
+    p.NB = NB;
+    carve(p, layout(d, kPlanParts), plan_mem);
+    if (launch_preprocess(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (launch_partial_keys(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    plan->dims = *d;
+    plan->mem = plan_mem;
+    plan->bytes = plan_bytes;
+    plan->device = dev;
+    plan->tag = QSA_PLAN_TAG;
+    return QSA_OK;
 }
 
 // Forward launches after validation. With `prep` the route preprocessing
@@ -664,6 +723,113 @@ qsa_status qsa_plan_tables(const qsa_plan *plan, uint32_t *mbits, int32_t *kinds
         if (hipMemcpyAsync(c.dst, m + c.at, c.bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
             return QSA_ERR_DEVICE;
     return QSA_OK;
+}
+
+size_t qsa_block_plan_bytes(const qsa_block_dims *dims)
+{
+    qsa_dims d;
+    return block_dims(dims, &d) == QSA_OK ? layout(&d, kPlanParts).total : 0;
+}
+
+size_t qsa_block_forward_workspace_bytes(const qsa_block_dims *dims)
+{
+    qsa_dims d;
+    if (block_dims(dims, &d) != QSA_OK) return 0;
+    return layout(&d, kPlanParts).total + layout(&d, kFwd | kWalk).total;
+}
+
+size_t qsa_block_backward_workspace_bytes(const qsa_block_dims *dims)
+{
+    qsa_dims d;
+    if (block_dims(dims, &d) != QSA_OK) return 0;
+    return layout(&d, kPlanParts).total + layout(&d, kBwd | kWalk).total;
+}
+
+qsa_status qsa_block_plan_build(const qsa_block_dims *dims, const uint8_t *sel_blocks,
+                                const int32_t *lo, const int32_t *hi, const int32_t *blk_base,
+                                const int32_t *tok_base, const int32_t *block_first,
+                                const int32_t *block_last, void *plan_mem, size_t plan_bytes,
+                                qsa_plan *plan, void *stream)
+{
+    if (!plan) return QSA_ERR_NULL;
+    std::memset(plan, 0, sizeof(*plan));
+    qsa_dims d;
+    qsa_status st = block_dims(dims, &d);
+    if (st != QSA_OK) return st;
+    if ((st = check_block_meta(sel_blocks, lo, hi, blk_base, tok_base, block_first, block_last)) !=
+        QSA_OK)
+        return st;
+    if ((st = check_workspace(plan_mem, plan_bytes, layout(&d, kPlanParts).total)) != QSA_OK)
+        return st;
+    if ((st = check_device(&d)) != QSA_OK) return st;
+    return build_block_plan(&d, dims->NB, sel_blocks, lo, hi, blk_base, tok_base, plan_mem,
+                            plan_bytes, plan, static_cast<hipStream_t>(stream));
+}
+
+qsa_status qsa_block_forward(const qsa_block_dims *dims, const void *q, const void *k,
+                             const void *v, const uint8_t *sel_blocks, const int32_t *lo,
+                             const int32_t *hi, const int32_t *blk_base, const int32_t *tok_base,
+                             const int32_t *block_first, const int32_t *block_last, float scale,
+                             void *out, float *out_fp32, float *lse, void *workspace,
+                             size_t workspace_bytes, void *stream)
+{
+    qsa_dims d;
+    qsa_status st = block_dims(dims, &d);
+    if (st != QSA_OK) return st;
+    if ((st = check_block_meta(sel_blocks, lo, hi, blk_base, tok_base, block_first, block_last)) !=
+        QSA_OK)
+        return st;
+    if ((st = check_forward_args(q, k, v, scale, out, out_fp32, lse)) != QSA_OK) return st;
+    const size_t plan_bytes = layout(&d, kPlanParts).total;
+    const Layout L = layout(&d, kFwd | kWalk);
+    if ((st = check_workspace(workspace, workspace_bytes, plan_bytes + L.total)) != QSA_OK)
+        return st;
+    if ((st = check_device(&d)) != QSA_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    qsa_plan plan;
+    std::memset(&plan, 0, sizeof(plan));
+    if ((st = build_block_plan(&d, dims->NB, sel_blocks, lo, hi, blk_base, tok_base, workspace,
+                               plan_bytes, &plan, s)) != QSA_OK)
+        return st;
+    Problem p;
+    fill_common(p, &d, nullptr, scale);
+    carve(p, layout(&d, kPlanParts), workspace);
+    carve(p, L, static_cast<char *>(workspace) + plan_bytes);
+    return run_forward(p, q, k, v, out, out_fp32, lse, s, nullptr, false);
+}
+
+qsa_status qsa_block_backward(const qsa_block_dims *dims, const void *grad_out, const void *q,
+                              const void *k, const void *v, const float *out_fp32,
+                              const float *lse, const uint8_t *sel_blocks, const int32_t *lo,
+                              const int32_t *hi, const int32_t *blk_base, const int32_t *tok_base,
+                              const int32_t *block_first, const int32_t *block_last, float scale,
+                              void *dq, void *dk, void *dv, void *workspace,
+                              size_t workspace_bytes, void *stream)
+{
+    qsa_dims d;
+    qsa_status st = block_dims(dims, &d);
+    if (st != QSA_OK) return st;
+    if ((st = check_block_meta(sel_blocks, lo, hi, blk_base, tok_base, block_first, block_last)) !=
+        QSA_OK)
+        return st;
+    if ((st = check_backward_args(grad_out, q, k, v, out_fp32, lse, scale, dq, dk, dv)) != QSA_OK)
+        return st;
+    const size_t plan_bytes = layout(&d, kPlanParts).total;
+    const Layout L = layout(&d, kBwd | kWalk);
+    if ((st = check_workspace(workspace, workspace_bytes, plan_bytes + L.total)) != QSA_OK)
+        return st;
+    if ((st = check_device(&d)) != QSA_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    qsa_plan plan;
+    std::memset(&plan, 0, sizeof(plan));
+    if ((st = build_block_plan(&d, dims->NB, sel_blocks, lo, hi, blk_base, tok_base, workspace,
+                               plan_bytes, &plan, s)) != QSA_OK)
+        return st;
+    Problem p;
+    fill_common(p, &d, nullptr, scale);
+    carve(p, layout(&d, kPlanParts), workspace);
+    carve(p, L, static_cast<char *>(workspace) + plan_bytes);
+    return run_backward(p, grad_out, q, k, v, out_fp32, lse, dq, dk, dv, s, nullptr, false);
 }
 
 const char *qsa_status_string(qsa_status status)

@@ -28,8 +28,13 @@ struct Problem {
     int64_t stride;  // membership row stride = nKT * 128
     int64_t nQT, nKT;
     float scale;
-    // inputs
+    // inputs: route rows, or (routes == nullptr) a block-selection bitmap
+    // sel [Sq, NB] with per-query lo, hi, blk_base, tok_base over packed
+    // tokens (B == 1, Sq == Skv)
     const void *routes;
+    const uint8_t *sel;
+    const int32_t *sel_lo, *sel_hi, *sel_blk_base, *sel_tok_base;
+    int64_t NB;
     const uint16_t *q, *k, *v, *dout;
     const float *out_fp32_in, *lse_in;
     // preprocessing results (workspace or caller buffers)

@@ -42,20 +42,12 @@ __global__ void k_fill_i32(int32_t *__restrict__ p, int64_t n, int32_t value)
         p[x] = value;
 }
 
+// Row `row`'s routes into its LDS bitmap (bm cleared, then one bit set per
+// member key).
 template <typename RouteT>
-__global__ __launch_bounds__(kPrepThreads) void k_prep_rows(Problem p)
+__device__ __forceinline__ void fill_from_routes(const Problem &p, uint32_t *bm, int64_t row,
+                                                 int tid)
 {
-    extern __shared__ uint32_t lds[];
-    const int64_t row = blockIdx.x;  // flat b * Sq + i
-    const int64_t b = row / p.Sq, i = row - b * p.Sq;
-    const int tid = threadIdx.x;
-    const int64_t nwords = p.stride >> 5;
-    uint32_t *bm = lds;
-    uint32_t *scan = lds + nwords;  // one total per wave
-
-    for (int64_t w = tid; w < nwords; w += kPrepThreads) bm[w] = 0u;
-    __syncthreads();
-
     // The loads of a round are all issued before its LDS atomics, so a row
     // waits for one or two memory latencies, not one per route.
     const RouteT *routes = static_cast<const RouteT *>(p.routes) + row * p.W;
@@ -104,7 +96,60 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_rows(Problem p)
                 if (r[u] >= 0 && r[u] < p.Skv) atomicOr(&bm[r[u] >> 5], 1u << (r[u] & 31));
         }
     }
-    __syncthreads();
+}
+
+// floor(a / 4) for any sign (arithmetic shift).
+__device__ __forceinline__ int64_t floor_div4(int64_t a) { return a >> 2; }
+
+// Row t's block selection into its LDS bitmap (cuDNN Frontend QSA page,
+// section "Selection and components"): key j is a member iff
+// lo[t] <= j <= hi[t], 0 <= j < Skv, and its block
+// b = blk_base[t] + floor((j - tok_base[t]) / 4) lies in [0, NB) with
+// sel[t, b] != 0. Only the blocks that keys of [lo, hi] map to are read:
+// block b holds the keys tok_base + 4 (b - blk_base) + 0..3.
+__device__ __forceinline__ void fill_from_blocks(const Problem &p, uint32_t *bm, int64_t row,
+                                                 int tid)
+{
+    const int64_t lo = max((int64_t)p.sel_lo[row], (int64_t)0);
+    const int64_t hi = min((int64_t)p.sel_hi[row], p.Skv - 1);
+    if (lo > hi) return;
+    const int64_t bb = p.sel_blk_base[row], tb = p.sel_tok_base[row];
+    const int64_t b0 = max(bb + floor_div4(lo - tb), (int64_t)0);
+    const int64_t b1 = min(bb + floor_div4(hi - tb), p.NB - 1);
+    const uint8_t *sel = p.sel + row * p.NB;
+    constexpr int kUnroll = 8;
+    for (int64_t c0 = b0; c0 <= b1; c0 += (int64_t)kPrepThreads * kUnroll) {
+        uint8_t v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t bk = c0 + u * kPrepThreads + tid;
+            v[u] = bk <= b1 ? sel[bk] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (!v[u]) continue;
+            const int64_t bk = c0 + u * kPrepThreads + tid;
+            const int64_t first = tb + 4 * (bk - bb);
+            const int64_t j0 = max(first, lo), j1 = min(first + 3, hi);
+            // at most four keys, in at most two words
+            for (int64_t j = j0; j <= j1;) {
+                const int64_t w = j >> 5;
+                const int64_t je = min(j1, 32 * w + 31);
+                const uint32_t n = (uint32_t)(je - j + 1);
+                atomicOr(&bm[w], ((1u << n) - 1u) << (j & 31));
+                j = je + 1;
+            }
+        }
+    }
+}
+
+// Everything after the row's bitmap is built: membership outputs, key list,
+// count and tile counts.
+__device__ __forceinline__ void finish_row(const Problem &p, uint32_t *bm, uint32_t *scan,
+                                           int64_t row, int tid)
+{
+    const int64_t b = row / p.Sq, i = row - b * p.Sq;
+    const int64_t nwords = p.stride >> 5;
 
     // Byte row of the membership table, 16 bytes per store.
     if (p.memb) {
@@ -192,6 +237,37 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_rows(Problem p)
                       __popc(bm[4 * t + 3]);
         if (c) atomicAdd(&tc[t], c);
     }
+}
+
+template <typename RouteT>
+__global__ __launch_bounds__(kPrepThreads) void k_prep_rows(Problem p)
+{
+    extern __shared__ uint32_t lds[];
+    const int64_t row = blockIdx.x;  // flat b * Sq + i
+    const int tid = threadIdx.x;
+    const int64_t nwords = p.stride >> 5;
+    uint32_t *bm = lds;
+    uint32_t *scan = lds + nwords;  // one total per wave
+    for (int64_t w = tid; w < nwords; w += kPrepThreads) bm[w] = 0u;
+    __syncthreads();
+    fill_from_routes<RouteT>(p, bm, row, tid);
+    __syncthreads();
+    finish_row(p, bm, scan, row, tid);
+}
+
+__global__ __launch_bounds__(kPrepThreads) void k_prep_rows_blocks(Problem p)
+{
+    extern __shared__ uint32_t lds[];
+    const int64_t row = blockIdx.x;  // packed token t
+    const int tid = threadIdx.x;
+    const int64_t nwords = p.stride >> 5;
+    uint32_t *bm = lds;
+    uint32_t *scan = lds + nwords;
+    for (int64_t w = tid; w < nwords; w += kPrepThreads) bm[w] = 0u;
+    __syncthreads();
+    fill_from_blocks(p, bm, row, tid);
+    __syncthreads();
+    finish_row(p, bm, scan, row, tid);
 }
 
 __device__ __forceinline__ int32_t tile_kind(int32_t cnt)
@@ -344,7 +420,10 @@ hipError_t launch_preprocess(const Problem &p, hipStream_t s)
     const hipError_t e = launch_walk_reset(p, s);
     if (e != hipSuccess) return e;
     const size_t lds = prep_lds_base(p) + (prep_stage_keys(p) ? (size_t)p.W * 4 : 0);
-    if (p.route_is_i64)
+    if (!p.routes)
+        hipLaunchKernelGGL(k_prep_rows_blocks, dim3((unsigned)(p.B * p.Sq)), dim3(kPrepThreads),
+                           lds, s, p);
+    else if (p.route_is_i64)
         hipLaunchKernelGGL(k_prep_rows<int64_t>, dim3((unsigned)(p.B * p.Sq)), dim3(kPrepThreads),
                            lds, s, p);
     else

@@ -42,6 +42,13 @@ class Dims(ctypes.Structure):
                 ("flags", ctypes.c_int32)]
 
 
+class BlockDims(ctypes.Structure):
+    """``qsa_block_dims``: packed tokens T, blocks NB, heads, block size, flags."""
+    _fields_ = [("T", ctypes.c_int64), ("NB", ctypes.c_int64), ("Hq", ctypes.c_int64),
+                ("Hkv", ctypes.c_int64), ("D", ctypes.c_int64), ("block_size", ctypes.c_int32),
+                ("flags", ctypes.c_int32)]
+
+
 class PlanStruct(ctypes.Structure):
     """``qsa_plan``: the host record of a built route plan."""
     _fields_ = [("dims", Dims), ("mem", ctypes.c_void_p), ("bytes", ctypes.c_size_t),
@@ -79,6 +86,17 @@ def library() -> ctypes.CDLL:
         lib.qsa_backward_planned.restype = ctypes.c_int
         lib.qsa_backward_planned.argtypes = [PL, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, S,
                                              P]
+        BD = ctypes.POINTER(BlockDims)
+        for name in ("qsa_block_plan_bytes", "qsa_block_forward_workspace_bytes",
+                     "qsa_block_backward_workspace_bytes"):
+            getattr(lib, name).restype = S
+            getattr(lib, name).argtypes = [BD]
+        lib.qsa_block_plan_build.restype = ctypes.c_int
+        lib.qsa_block_plan_build.argtypes = [BD] + [P] * 7 + [P, S, PL, P]
+        lib.qsa_block_forward.restype = ctypes.c_int
+        lib.qsa_block_forward.argtypes = [BD] + [P] * 10 + [ctypes.c_float] + [P] * 4 + [S, P]
+        lib.qsa_block_backward.restype = ctypes.c_int
+        lib.qsa_block_backward.argtypes = [BD] + [P] * 13 + [ctypes.c_float] + [P] * 4 + [S, P]
         lib.qsa_plan_tables.restype = ctypes.c_int
         lib.qsa_plan_tables.argtypes = [PL] + [P] * 12 + [P]
         lib.qsa_status_string.restype = ctypes.c_char_p
@@ -418,3 +436,115 @@ def plan_tables(plan: Plan) -> dict:
                                    _stream())
     _raise(st)
     return out
+
+
+def _block_meta(sel_blocks, lo, hi, blk_base, tok_base, block_first, block_last):
+    sel = _check(sel_blocks, torch.uint8, "sel_blocks")
+    meta = [_check(t, torch.int32, n) for t, n in ((lo, "lo"), (hi, "hi"), (blk_base, "blk_base"),
+                                                  (tok_base, "tok_base"))]
+    spans = [_check(t, torch.int32, n) for t, n in ((block_first, "block_first"),
+                                                   (block_last, "block_last"))]
+    if sel.dim() != 2:
+        raise ValueError("sel_blocks must be [T, NB]")
+    T, NB = sel.shape
+    if any(tuple(t.shape) != (T,) for t in meta) or any(tuple(t.shape) != (NB,) for t in spans):
+        raise ValueError("lo, hi, blk_base, tok_base must be [T] and block_first, block_last [NB]")
+    return sel, meta, spans
+
+
+def block_dims(T: int, NB: int, Hkv: int = 1, block_size: int = 4,
+               deterministic: bool = False) -> BlockDims:
+    return BlockDims(T, NB, GROUP * Hkv, Hkv, HEAD_DIM, block_size,
+                     FLAG_DETERMINISTIC if deterministic else 0)
+
+
+def block_plan_build(sel_blocks, lo, hi, blk_base, tok_base, block_first, block_last, *,
+                     Hkv: int = 1, block_size: int = 4, deterministic: bool = False,
+                     plan_mem: Optional[torch.Tensor] = None) -> Plan:
+    """Build a route plan from a block-selection bitmap (``qsa_block_plan_build``)."""
+    sel, meta, spans = _block_meta(sel_blocks, lo, hi, blk_base, tok_base, block_first,
+                                   block_last)
+    bd = block_dims(sel.shape[0], sel.shape[1], Hkv, block_size, deterministic)
+    lib = library()
+    need = lib.qsa_block_plan_bytes(ctypes.byref(bd))
+    mem = _workspace(need, sel.device, plan_mem)
+    struct = PlanStruct()
+    st = lib.qsa_block_plan_build(ctypes.byref(bd), sel.data_ptr(),
+                                  *[t.data_ptr() for t in meta + spans], mem.data_ptr(),
+                                  mem.numel() * mem.element_size(), ctypes.byref(struct),
+                                  _stream())
+    _raise(st)
+    return Plan(struct, mem)
+
+
+def block_forward(q, k, v, sel_blocks, lo, hi, blk_base, tok_base, block_first, block_last,
+                  scale: Optional[float] = None, *, block_size: int = 4, out=None, out_fp32=None,
+                  lse=None, workspace=None, deterministic: bool = False):
+    """QSA forward on packed tokens with a block-selection bitmap (``qsa_block_forward``).
+    q [T, Hq, 256], k, v [T, Hkv, 256]; returns ``(out, out_fp32, lse [Hq, T])``."""
+    q = _check(q, torch.bfloat16, "q")
+    k = _check(k, torch.bfloat16, "k")
+    v = _check(v, torch.bfloat16, "v")
+    sel, meta, spans = _block_meta(sel_blocks, lo, hi, blk_base, tok_base, block_first,
+                                   block_last)
+    T, NB = sel.shape
+    if q.dim() != 3 or q.shape[0] != T or k.shape != v.shape or k.dim() != 3 or k.shape[0] != T:
+        raise ValueError("q must be [T, Hq, 256] and k, v [T, Hkv, 256]")
+    Hq, Hkv = q.shape[1], k.shape[1]
+    bd = BlockDims(T, NB, Hq, Hkv, q.shape[2], block_size, FLAG_DETERMINISTIC if deterministic
+                   else 0)
+    if scale is None:
+        scale = 1.0 / (q.shape[-1] ** 0.5)
+    out = torch.empty_like(q) if out is None else out
+    out_fp32 = torch.empty(q.shape, dtype=torch.float32, device=q.device) if out_fp32 is None \
+        else out_fp32
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    lib = library()
+    ws = _workspace(lib.qsa_block_forward_workspace_bytes(ctypes.byref(bd)), q.device, workspace)
+    st = lib.qsa_block_forward(ctypes.byref(bd), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                               sel.data_ptr(), *[t.data_ptr() for t in meta + spans],
+                               float(scale), out.data_ptr(), out_fp32.data_ptr(), lse.data_ptr(),
+                               ws.data_ptr(), ws.numel() * ws.element_size(), _stream())
+    _raise(st)
+    return out, out_fp32, lse
+
+
+def block_backward(grad_out, q, k, v, out_fp32, lse, sel_blocks, lo, hi, blk_base, tok_base,
+                   block_first, block_last, scale: Optional[float] = None, *,
+                   block_size: int = 4, dq=None, dk=None, dv=None, workspace=None,
+                   deterministic: bool = False):
+    """QSA backward on packed tokens with a block-selection bitmap (``qsa_block_backward``).
+    Returns ``(dq, dk, dv)``."""
+    grad_out = _check(grad_out, torch.bfloat16, "grad_out")
+    q = _check(q, torch.bfloat16, "q")
+    k = _check(k, torch.bfloat16, "k")
+    v = _check(v, torch.bfloat16, "v")
+    out_fp32 = _check(out_fp32, torch.float32, "out_fp32")
+    lse = _check(lse, torch.float32, "lse")
+    sel, meta, spans = _block_meta(sel_blocks, lo, hi, blk_base, tok_base, block_first,
+                                   block_last)
+    T, NB = sel.shape
+    if q.dim() != 3 or q.shape[0] != T or k.shape != v.shape or k.dim() != 3 or k.shape[0] != T:
+        raise ValueError("q must be [T, Hq, 256] and k, v [T, Hkv, 256]")
+    if grad_out.shape != q.shape or out_fp32.shape != q.shape:
+        raise ValueError("grad_out and out_fp32 must have q's shape")
+    Hq, Hkv = q.shape[1], k.shape[1]
+    if tuple(lse.shape) != (Hq, T):
+        raise ValueError("lse must be [Hq, T]")
+    bd = BlockDims(T, NB, Hq, Hkv, q.shape[2], block_size, FLAG_DETERMINISTIC if deterministic
+                   else 0)
+    if scale is None:
+        scale = 1.0 / (q.shape[-1] ** 0.5)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    lib = library()
+    ws = _workspace(lib.qsa_block_backward_workspace_bytes(ctypes.byref(bd)), q.device,
+                    workspace)
+    st = lib.qsa_block_backward(ctypes.byref(bd), grad_out.data_ptr(), q.data_ptr(),
+                                k.data_ptr(), v.data_ptr(), out_fp32.data_ptr(), lse.data_ptr(),
+                                sel.data_ptr(), *[t.data_ptr() for t in meta + spans],
+                                float(scale), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                ws.data_ptr(), ws.numel() * ws.element_size(), _stream())
+    _raise(st)
+    return dq, dk, dv
