@@ -33,11 +33,16 @@
  *  - Alignment: 16 bytes for q, k, v, grad_out, out, out_fp32, dq, dk, dv and
  *    the workspace; 4 bytes for lse and int32 routes, 8 for int64 routes
  *    (QSA page, "Tensors": layouts are rejected before launch).
- *  - Shapes: B, Sq, Skv, W >= 1; D == 256; Hkv >= 1 and Hq == 12 * Hkv, so
- *    24Q/2KV runs as two independent 12Q/1KV groups; Skv <= 2^19 (the per-row
- *    route scatter holds one bit per key on chip); W <= 2^20. scale must be
- *    finite and > 0. All offsets are 64-bit, so B * Sq * Skv beyond 2^31 is
- *    supported ("flex_qsa" page, `_membership_flat_offset`).
+ *  - Shapes: B, Sq, Skv, W >= 1; D == 256; 1 <= Hkv <= 4096 and Hq == 12 *
+ *    Hkv, so 24Q/2KV runs as two independent 12Q/1KV groups; Skv <= 2^19 (the
+ *    per-row route scatter holds one bit per key on chip); W <= 2^20. scale
+ *    must be finite and > 0. Grid and addressing limits: B, Sq and B * Sq <=
+ *    2^24, B * Sq * Hq <= 2^26, B * Hkv * ceil(Skv / 128) * 128 <= 2^30; one
+ *    batch row of Q (Sq * Hq * 512 bytes) and of K (Skv * Hkv * 512 bytes)
+ *    each below 2^31 bytes, since the gathers use 32-bit offsets inside a
+ *    batch row. Offsets across batch rows and tables are 64-bit, so B * Sq *
+ *    Skv beyond 2^31 is supported ("flex_qsa" page,
+ *    `_membership_flat_offset`). Larger shapes return QSA_ERR_SHAPE.
  *  - Route VALUES are never read on the host and the host never waits on the
  *    device: every count stays on the device ("fa4_qsa" page, `_block_kinds`).
  *  - Ownership: the caller allocates every output and the workspace, whose

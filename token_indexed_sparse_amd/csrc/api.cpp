@@ -834,7 +834,12 @@ qsa_status qsa_block_backward(const qsa_block_dims *dims, const void *grad_out, 
 
 const char *qsa_status_string(qsa_status status)
 {
-    switch (status) {
+    // A C caller may pass any int: read the bits as an integer, since a C++
+    // enum object holding a value outside its enumerators' range is undefined.
+    int32_t code;
+    static_assert(sizeof(code) == sizeof(status), "qsa_status is 32 bits");
+    std::memcpy(&code, &status, sizeof(code));
+    switch (code) {
     case QSA_OK: return "ok";
     case QSA_ERR_NULL: return "a required pointer is NULL";
     case QSA_ERR_SHAPE: return "a dimension is < 1 or beyond the supported limits";
