@@ -60,12 +60,15 @@ qsa_status qsa_backward_planned_timed(const qsa_plan *plan, const void *grad_out
  * discards them. row_bytes is 512 (K or V rows, two per load instruction,
  * as the gathered forward and dQ stage them; n_rows even) or 6144 (the 12
  * heads of one Q or dO row, as the gathered dK/dV stages them). `blocks` work
- * groups of four waves share the rows. Row indices must lie inside `src`
+ * groups share the rows; `shape` picks the launch shape, 0 .. 3: four waves
+ * with 32 KB of LDS each, eight with 16 KB, eight with 20 KB, four with
+ * 16 KB (two work groups per CU). Row indices must lie inside `src`
  * (out-of-range offsets read zeros). Timing is the caller's (events around
  * the call).
  */
 qsa_status qsa_bench_gather(const void *src, size_t src_bytes, const int32_t *rows,
-                            int64_t n_rows, int32_t row_bytes, int32_t blocks, void *stream);
+                            int64_t n_rows, int32_t row_bytes, int32_t blocks, int32_t shape,
+                            void *stream);
 
 #ifdef __cplusplus
 }

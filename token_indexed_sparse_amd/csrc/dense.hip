@@ -182,21 +182,28 @@ __device__ __forceinline__ void forward_dense_item(const Problem &p, lds_char *b
         constexpr bool kRescale = decltype(rescale_tag)::value;
         const lds_char *ks = (const lds_char *)(uintptr_t)cb;
         const lds_char *vs = ks + kHalf;
-        // S^T one key block at a time (eight K reads live, not sixteen).
+        // S^T for both key blocks: all sixteen K reads are issued first, and
+        // the two blocks' products alternate (two independent chains).
         f32x4 st[kVecBlocks][2];
+        uint4 kr[2][8];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            uint4 kr[8];
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int t = 0; t < 8; ++t)
-                kr[t] = lds_read16(ks + col * 1024 + 512 * kb + (((4 * t + quad) ^ kmask) << 4));
+                kr[kb][t] = lds_read16(ks + col * 1024 + 512 * kb + (((4 * t + quad) ^ kmask) << 4));
+        // keep the reads ahead of the products (the scheduler would otherwise
+        // trade them for registers and keep two in flight)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int x = 0; x < kVecBlocks; ++x) {
-                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        for (int x = 0; x < kVecBlocks; ++x) {
+            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
-                for (int t = 0; t < 8; ++t) a = mfma_16x16x32(as_bf16x8(kr[t]), qf[x][t], a);
-                st[x][kb] = a;
+            for (int t = 0; t < 8; ++t) {
+                a0 = mfma_16x16x32(as_bf16x8(kr[0][t]), qf[x][t], a0);
+                a1 = mfma_16x16x32(as_bf16x8(kr[1][t]), qf[x][t], a1);
             }
+            st[x][0] = a0;
+            st[x][1] = a1;
         }
         bf16x8 pb_hi[kVecBlocks], pb_lo[kVecBlocks];
 #pragma unroll
@@ -211,12 +218,18 @@ __device__ __forceinline__ void forward_dense_item(const Problem &p, lds_char *b
                     tv[kb * 4 + e] = st[x][kb][e] * c;
                     mx = fmaxf(mx, tv[kb * 4 + e]);
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            // The column maximum (over the four lane groups) is needed only
+            // to fix or raise the reference; the overflow test is a ballot of
+            // the lanes' own maxima, the same answer without the exchange.
+            auto column_max = [&](float v) {
+                v = fmaxf(v, __shfl_xor(v, 16));
+                return fmaxf(v, __shfl_xor(v, 32));
+            };
             // The first chunk fixes the reference (the sums are still zero;
             // the hand-over is added at the end, scaled to the reference).
-            if (first) m_ref[x] = fmaxf(m_hand[x], mx);
+            if (first) m_ref[x] = fmaxf(m_hand[x], column_max(mx));
             if (__builtin_amdgcn_ballot_w64(mx > m_ref[x] + kSlack) != 0) {
+                mx = column_max(mx);
                 if constexpr (kRescale) {
                     const float mn = fmaxf(m_ref[x], mx);
                     const float f = __builtin_amdgcn_exp2f(m_ref[x] - mn);
@@ -255,6 +268,7 @@ __device__ __forceinline__ void forward_dense_item(const Problem &p, lds_char *b
                 va[0][j] = lds_read_tr(vs + o);
                 va[1][j] = lds_read_tr(vs + o + 512);
             }
+            __builtin_amdgcn_sched_barrier(0);  // all sixteen reads in flight
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int db = 8 * h + j;
@@ -437,6 +451,7 @@ __device__ __forceinline__ void dq_dense_item(const Problem &p, lds_char *buf)
                 kr[t] = lds_read16(ks + o);
                 vr[t] = lds_read16(vs + o);
             }
+            __builtin_amdgcn_sched_barrier(0);  // all sixteen reads in flight
 #pragma unroll
             for (int x = 0; x < kVecBlocks; ++x) {
                 f32x4 a = {0.f, 0.f, 0.f, 0.f}, d = {0.f, 0.f, 0.f, 0.f};
@@ -475,6 +490,7 @@ __device__ __forceinline__ void dq_dense_item(const Problem &p, lds_char *buf)
                 kt[0][j] = lds_read_tr(ks + o);
                 kt[1][j] = lds_read_tr(ks + o + 512);
             }
+            __builtin_amdgcn_sched_barrier(0);  // all sixteen reads in flight
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int db = 8 * h + j;
