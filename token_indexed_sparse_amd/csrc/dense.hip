@@ -615,7 +615,8 @@ __device__ __forceinline__ void dkdv_dense_item(const Problem &p, lds_char *buf)
         adv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Staging of chunk c: query tile ridx[c / 48], vectors 32 (c % 48) + j.
+    // Staging of chunk c: query tile ridx[(c / 48 + rot) mod fcnt], vectors
+    // 32 (c % 48) + j.
     // Instruction s puts vectors s (lanes 0..31) and s + 16 (lanes 32..63) at
     // s * 1024, lane l taking chunk (l & 31) ^ swz_mask(s) of its vector; wave
     // w issues s = 4w .. 4w+3 for Q and for dO, wave 0 also lse and delta
@@ -625,8 +626,28 @@ __device__ __forceinline__ void dkdv_dense_item(const Problem &p, lds_char *buf)
     const uint32_t base = lds_addr(buf);
     const uint32_t chunk16 = (uint32_t)(lane & 31) << 4;
     auto vec_off = [&](int v) { return (uint32_t)(((v / kGroup) * p.Hq + v % kGroup) * kD * 2); };
+    // The walk over the tile column's full query tiles starts at the first
+    // entry whose tile index is a multiple of the list length (else at the
+    // first entry). Columns whose lists are the same-length windows shifted
+    // by one tile (the recent-window part of causal routes) then visit the
+    // same query tile at the same step, so the work groups of neighbouring
+    // columns on one XCD stream each tile through its L2 together. The order
+    // depends on the list only: results stay reproducible.
+    int32_t rot = 0;
+    for (int32_t j0 = 0; j0 < fcnt; j0 += 64) {
+        const int32_t j = j0 + lane;
+        const bool start = j < fcnt && (p.rev_f_idx[(b * p.nKT + t) * p.nQT + j] % fcnt) == 0;
+        const uint64_t ball = __ballot(start);
+        if (ball != 0ull) {
+            rot = j0 + (int32_t)__builtin_ctzll(ball);
+            break;
+        }
+    }
+    rot = __builtin_amdgcn_readfirstlane(rot);
     auto issue = [&](int c) {
-        const int64_t r = ridx[c / kChunksPerTile];
+        int32_t tj = c / kChunksPerTile + rot;
+        tj = tj >= fcnt ? tj - fcnt : tj;
+        const int64_t r = ridx[tj];
         const int cc = c % kChunksPerTile;
         const int64_t tb = ((b * p.Sq + r * kTile) * p.Hq + g * kGroup) * (int64_t)kD;
         const i32x4 rq = rsrc_words(p.q + tb, tile_bytes);
