@@ -600,15 +600,35 @@ __global__ __launch_bounds__(256) void k_dkdv_reduce(Problem p)
     if (key >= p.Skv) return;
     const int64_t ngroups = p.stride >> 4;
     const uint8_t *flag = p.kv_flag + bg * p.nslot * ngroups + (key >> 4);
+    const float *src = p.kv_part + (bg * p.nslot * p.stride + key) * (int64_t)(2 * kD) + 4 * f4;
+    const int64_t slot_floats = p.stride * (int64_t)(2 * kD);
+    // A wave covers half of one key, so the flags are the same for all its
+    // lanes. Eight slots at a time: their flags, then the loads of the
+    // flagged ones (all in flight together), then the sums in slot order.
+    constexpr int kU = 8;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int64_t seg = 0; seg < p.nslot; ++seg) {
-        if (!flag[seg * ngroups]) continue;
-        const float4 v = *reinterpret_cast<const float4 *>(
-            p.kv_part + ((bg * p.nslot + seg) * p.stride + key) * (int64_t)(2 * kD) + 4 * f4);
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
+    for (int64_t s0 = 0; s0 < p.nslot; s0 += kU) {
+        bool on[kU];
+        float4 v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            // every flag load in range (the last slot's flag stands in past the
+            // end), so the eight loads fly together
+            const int64_t su = s0 + u < p.nslot ? s0 + u : p.nslot - 1;
+            on[u] = flag[su * ngroups] != 0 && s0 + u < p.nslot;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            v[u] = on[u] ? *reinterpret_cast<const float4 *>(src + (s0 + u) * slot_floats)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            if (!on[u]) continue;  // skipped, not added as zero: signed zeros stay
+            acc.x += v[u].x;
+            acc.y += v[u].y;
+            acc.z += v[u].z;
+            acc.w += v[u].w;
+        }
     }
     const bool is_k = f4 < kD / 4;
     const int d = 4 * (is_k ? f4 : f4 - kD / 4);
