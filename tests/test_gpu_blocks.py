@@ -130,3 +130,27 @@ def test_workloads_as_bitmaps_match_route_calls_bitwise(idx):
     if bi.T <= 16384:
         memb, _ = oracle.block_membership(bi.sel_blocks, bi.lo, bi.hi, bi.blk_base, bi.tok_base)
         _check_block_tables(qsa.block_plan_build(*meta), memb, bi.T)
+
+
+@pytest.mark.parametrize("seed,T,NB", [(81, 300, 90), (82, 700, 40), (83, 129, 200)])
+def test_random_metadata_against_oracle(seed, T, NB):
+    """Arbitrary metadata (the page leaves it a caller contract): lo > hi, bounds past
+    the tokens, block bases below 0 and past NB, token origins off the four-token
+    grid. The block calls must select exactly what the oracle's lookup selects."""
+    rng = np.random.default_rng(seed)
+    sel = (rng.random((T, NB)) < 0.3).astype(np.uint8) * rng.integers(1, 256, (T, NB),
+                                                                      dtype=np.uint8)
+    lo = rng.integers(-20, T + 20, T).astype(np.int32)
+    hi = rng.integers(-20, T + 20, T).astype(np.int32)
+    bb = rng.integers(-10, NB + 10, T).astype(np.int32)
+    tb = rng.integers(-30, T + 30, T).astype(np.int32)
+    bf = np.arange(NB, dtype=np.int32) * 4
+    bl = bf + 3
+    x = [synth.bf16_bits(rng.standard_normal(s, dtype=np.float32))
+         for s in ((T, 12, 256), (T, 1, 256), (T, 1, 256), (T, 12, 256))]
+    q, k, v, g = (to_gpu_bf16(a) for a in x)
+    meta = _meta_gpu(sel, lo, hi, bb, tb, bf, bl)
+    got = _run_block(q, k, v, g, meta, 0.0625)
+    memb, _ = oracle.block_membership(sel, lo, hi, bb, tb)
+    _check_block_tables(qsa.block_plan_build(*meta), memb, T)
+    _oracle_compare(*x, memb, 0.0625, got)
