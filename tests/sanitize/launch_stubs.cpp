@@ -8,6 +8,10 @@ namespace qsa {
 hipError_t launch_preprocess(const Problem &, hipStream_t) { return hipErrorLaunchFailure; }
 hipError_t launch_walk_reset(const Problem &, hipStream_t) { return hipErrorLaunchFailure; }
 hipError_t launch_partial_keys(const Problem &, hipStream_t) { return hipErrorLaunchFailure; }
+hipError_t launch_row_keys(const Problem &, int32_t *, int32_t *, hipStream_t)
+{
+    return hipErrorLaunchFailure;
+}
 hipError_t launch_forward(const Problem &, hipStream_t) { return hipErrorLaunchFailure; }
 hipError_t launch_forward_dense(const Problem &, hipStream_t) { return hipErrorLaunchFailure; }
 hipError_t launch_dq_dense(const Problem &, hipStream_t) { return hipErrorLaunchFailure; }

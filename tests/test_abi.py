@@ -138,8 +138,10 @@ def test_noalloc_validates_before_touching_the_device(lib):
 
 def test_plan_sizes_split_the_plain_workspaces(lib):
     """The plan holds the preprocessing of both calls; the planned calls' scratch is
-    the rest, so plan + planned scratch covers the plain backward exactly and the
-    plain forward plus the membership bits only the backward reads."""
+    the rest. Plan and backward keep the membership bits and build the partial-tile
+    key lists from them, the plain forward keeps the full key lists instead: plan +
+    planned scratch is the plain backward exactly, and the plain forward with the
+    bits in place of the full key lists."""
     from token_indexed_sparse_amd import qsa
     for kw in (dict(), dict(Sq=32768, Skv=32768, W=2052), dict(B=4, Sq=4096, Skv=4096, Hq=24,
                                                               Hkv=2, W=260)):
@@ -150,8 +152,11 @@ def test_plan_sizes_split_the_plain_workspaces(lib):
         f, b = qsa.forward_workspace_bytes(d), qsa.backward_workspace_bytes(d)
         assert 0 < pf < f and 0 < pb < b
         assert plan + pb == b
-        bits = -(-d.B * d.Sq * (-(-d.Skv // 128) * 4) * 4 // 256) * 256
-        assert plan + pf == f + bits
+        def r256(n):
+            return -(-n // 256) * 256
+        bits = r256(d.B * d.Sq * (-(-d.Skv // 128) * 4) * 4)
+        keys = r256(d.B * d.Sq * d.W * 4) + r256(d.B * d.Sq * 4)
+        assert plan + pf == f + bits - keys
     bad = _dims(D=128)
     for n in ("qsa_plan_bytes", "qsa_forward_planned_workspace_bytes",
               "qsa_backward_planned_workspace_bytes"):

@@ -73,16 +73,22 @@ struct Layout {
 // the forward's hand-over state (fwd), the backward's delta, partial sums and
 // flags (bwd), and the walk clocks of the gathered passes (walk).
 enum Part : unsigned {
-    kCore = 1u,
+    kKeys = 1u,
     kBits = 2u,
     kPkeys = 4u,
     kLists = 8u,
     kFwd = 16u,
     kBwd = 32u,
     kWalk = 64u,
-    kPlanParts = kCore | kBits | kPkeys | kLists,
+    kTiles = 128u,
+    kCore = kKeys | kTiles,
+    // Plans and backward calls keep the membership bits, from which the
+    // partial-tile lists are built directly (no full key lists); the plain
+    // forward keeps the full key lists instead, which are the smaller of the
+    // two when Skv is large against W.
+    kPlanParts = kTiles | kBits | kPkeys | kLists,
     kForwardParts = kCore | kPkeys | kLists | kFwd | kWalk,
-    kBackwardParts = kCore | kBits | kPkeys | kLists | kBwd | kWalk,
+    kBackwardParts = kTiles | kBits | kPkeys | kLists | kBwd | kWalk,
 };
 
 Layout layout(const qsa_dims *d, unsigned parts)
@@ -104,11 +110,11 @@ Layout layout(const qsa_dims *d, unsigned parts)
     // only (caller buffers): no forward or backward kernel reads them, so those
     // calls do not materialise them.
     L.mbits = take(parts & kBits, (size_t)(rows * (stride / 32)) * 4);
-    L.row_keys = take(parts & kCore, (size_t)(rows * d->W) * 4);
-    L.row_cnt = take(parts & kCore, (size_t)rows * 4);
+    L.row_keys = take(parts & kKeys, (size_t)(rows * d->W) * 4);
+    L.row_cnt = take(parts & kKeys, (size_t)rows * 4);
     L.pkeys = take(parts & kPkeys, (size_t)(rows * d->W) * 4);
     L.pcnt = take(parts & kPkeys, (size_t)rows * 4);
-    L.tile_cnt = take(parts & kCore, (size_t)(d->B * nQT * nKT) * 4);
+    L.tile_cnt = take(parts & kTiles, (size_t)(d->B * nQT * nKT) * 4);
     const bool lists = parts & kLists;
     L.kinds = take(lists, (size_t)(d->B * nQT * nKT) * 4);
     L.fpc = take(lists, (size_t)(d->B * nQT) * 4);
@@ -214,8 +220,8 @@ void carve(Problem &p, const Layout &L, void *ws)
     if (L.row_keys != none) {
         p.row_keys = reinterpret_cast<int32_t *>(w + L.row_keys);
         p.row_cnt = reinterpret_cast<int32_t *>(w + L.row_cnt);
-        p.tile_cnt = reinterpret_cast<int32_t *>(w + L.tile_cnt);
     }
+    if (L.tile_cnt != none) p.tile_cnt = reinterpret_cast<int32_t *>(w + L.tile_cnt);
     if (L.pkeys != none) {
         p.pkeys = reinterpret_cast<int32_t *>(w + L.pkeys);
         p.pcnt = reinterpret_cast<int32_t *>(w + L.pcnt);
@@ -716,12 +722,15 @@ qsa_status qsa_plan_tables(const qsa_plan *plan, uint32_t *mbits, int32_t *kinds
         {rev_p_idx, L.rpi, (size_t)(d->B * nKT * nQT) * 4},
         {rev_f_cnt, L.rfc, (size_t)(d->B * nKT) * 4},
         {rev_f_idx, L.rfi, (size_t)(d->B * nKT * nQT) * 4},
-        {row_keys, L.row_keys, (size_t)(rows * d->W) * 4},
-        {row_cnt, L.row_cnt, (size_t)rows * 4},
     };
     for (const Copy &c : copies)
         if (hipMemcpyAsync(c.dst, m + c.at, c.bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
             return QSA_ERR_DEVICE;
+    // The plan holds no full key lists: they are built from its membership bits.
+    Problem p;
+    fill_common(p, d, nullptr, 1.f);
+    carve(p, L, plan->mem);
+    if (launch_row_keys(p, row_keys, row_cnt, s) != hipSuccess) return QSA_ERR_LAUNCH;
     return QSA_OK;
 }
 

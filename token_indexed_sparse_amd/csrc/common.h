@@ -83,6 +83,9 @@ constexpr int kWalkRounds = 8;
 hipError_t launch_preprocess(const Problem &p, hipStream_t s);
 hipError_t launch_walk_reset(const Problem &p, hipStream_t s);
 hipError_t launch_partial_keys(const Problem &p, hipStream_t s);
+// The full per-row key lists from the bit-packed membership, into keys [B*Sq, W]
+// and cnt [B*Sq].
+hipError_t launch_row_keys(const Problem &p, int32_t *keys, int32_t *cnt, hipStream_t s);
 hipError_t launch_forward(const Problem &p, hipStream_t s);
 hipError_t launch_forward_dense(const Problem &p, hipStream_t s);
 hipError_t launch_dq_dense(const Problem &p, hipStream_t s);

@@ -177,57 +177,61 @@ __device__ __forceinline__ void finish_row(const Problem &p, uint32_t *bm, uint3
     // window of consecutive keys) spreads over the lanes instead of falling on
     // one thread. Positions: the words before the wave's quarter (wave totals
     // through LDS), then, inside the quarter, the earlier 64-word blocks and
-    // the earlier lanes of the word's own block (wave scans).
-    const int lane = tid & 63, wv = tid >> 6;
-    const int64_t qw = (nwords + kPrepThreads / 64 - 1) / (kPrepThreads / 64);
-    const int64_t wbeg = wv * qw, wend = (wbeg + qw < nwords) ? wbeg + qw : nwords;
-    int mine = 0;
-    for (int64_t w = wbeg + lane; w < wend; w += 64) mine += __popc(bm[w]);
-    int wave_total = mine;
+    // the earlier lanes of the word's own block (wave scans). Calls that keep
+    // only the bit-packed membership build their lists from it later
+    // (k_row_lists); then there is no list and no count here.
+    if (p.row_keys) {
+        const int lane = tid & 63, wv = tid >> 6;
+        const int64_t qw = (nwords + kPrepThreads / 64 - 1) / (kPrepThreads / 64);
+        const int64_t wbeg = wv * qw, wend = (wbeg + qw < nwords) ? wbeg + qw : nwords;
+        int mine = 0;
+        for (int64_t w = wbeg + lane; w < wend; w += 64) mine += __popc(bm[w]);
+        int wave_total = mine;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) wave_total += __shfl_xor(wave_total, off);
-    if (lane == 0) scan[wv] = wave_total;
-    __syncthreads();
-    int before = 0, total = 0;
-#pragma unroll
-    for (int v = 0; v < kPrepThreads / 64; ++v) {
-        const int tv = scan[v];
-        before += v < wv ? tv : 0;
-        total += tv;
-    }
-    int32_t *keys = p.row_keys + row * p.W;
-    const bool staged = prep_stage_keys(p);
-    int32_t *sk = reinterpret_cast<int32_t *>(scan + kPrepThreads + 1);
-    int run = before;  // keys before the current 64-word block
-    for (int64_t w0 = wbeg; w0 < wend; w0 += 64) {
-        const int64_t w = w0 + lane;
-        uint32_t bits = w < wend ? bm[w] : 0u;
-        const int c = __popc(bits);
-        int inc = c;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int t = __shfl_up(inc, off);
-            if (lane >= off) inc += t;
-        }
-        int pos = run + inc - c;
-        while (bits) {
-            const int bit = __ffs(bits) - 1;
-            bits &= bits - 1;
-            const int32_t key = (int32_t)(w * 32 + bit);
-            if (staged) sk[pos++] = key;  // through LDS: the list leaves in coalesced stores
-            else keys[pos++] = key;
-        }
-        run += __shfl(inc, 63);
-    }
-    if (staged) {
+        for (int off = 32; off > 0; off >>= 1) wave_total += __shfl_xor(wave_total, off);
+        if (lane == 0) scan[wv] = wave_total;
         __syncthreads();
-        for (int64_t s = tid; s < p.W; s += kPrepThreads) keys[s] = s < total ? sk[s] : -1;
-    } else {
-        for (int64_t s = total + tid; s < p.W; s += kPrepThreads) keys[s] = -1;
-    }
-    if (tid == 0) {
-        p.row_cnt[row] = total;
-        if (p.has_routes) p.has_routes[row] = total > 0 ? 1 : 0;
+        int before = 0, total = 0;
+#pragma unroll
+        for (int v = 0; v < kPrepThreads / 64; ++v) {
+            const int tv = scan[v];
+            before += v < wv ? tv : 0;
+            total += tv;
+        }
+        int32_t *keys = p.row_keys + row * p.W;
+        const bool staged = prep_stage_keys(p);
+        int32_t *sk = reinterpret_cast<int32_t *>(scan + kPrepThreads + 1);
+        int run = before;  // keys before the current 64-word block
+        for (int64_t w0 = wbeg; w0 < wend; w0 += 64) {
+            const int64_t w = w0 + lane;
+            uint32_t bits = w < wend ? bm[w] : 0u;
+            const int c = __popc(bits);
+            int inc = c;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int t = __shfl_up(inc, off);
+                if (lane >= off) inc += t;
+            }
+            int pos = run + inc - c;
+            while (bits) {
+                const int bit = __ffs(bits) - 1;
+                bits &= bits - 1;
+                const int32_t key = (int32_t)(w * 32 + bit);
+                if (staged) sk[pos++] = key;  // through LDS: the list leaves in coalesced stores
+                else keys[pos++] = key;
+            }
+            run += __shfl(inc, 63);
+        }
+        if (staged) {
+            __syncthreads();
+            for (int64_t s = tid; s < p.W; s += kPrepThreads) keys[s] = s < total ? sk[s] : -1;
+        } else {
+            for (int64_t s = total + tid; s < p.W; s += kPrepThreads) keys[s] = -1;
+        }
+        if (tid == 0) {
+            p.row_cnt[row] = total;
+            if (p.has_routes) p.has_routes[row] = total > 0 ? 1 : 0;
+        }
     }
 
     // Tile counts: tile t covers words 4t .. 4t+3.
@@ -392,12 +396,94 @@ __global__ __launch_bounds__(256) void k_partial_keys(Problem p)
     if (lane == 0) p.pcnt[row] = cnt;
 }
 
+
+// A row's ascending key list and count from its bit-packed membership, -1
+// tail to the row width W; with skip_full, without the keys of the full
+// tiles of the row's tile row (the partial-tile list of the gathered
+// passes), else all keys. One wave per row: lane l takes words l, l + 64,
+// ... four blocks of 64 words at a time (their loads in flight together);
+// a word's keys go to positions from a wave prefix sum of the popcounts.
+__global__ __launch_bounds__(256) void k_row_lists(Problem p, int32_t *out_keys,
+                                                   int32_t *out_cnt, int skip_full)
+{
+    __shared__ uint32_t fullbits[4][kFullWords];
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= p.B * p.Sq) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t b = row / p.Sq, i = row - b * p.Sq;
+    const int64_t nwords = p.stride >> 5;
+    const uint32_t *m = p.mbits + row * nwords;
+    int32_t *out = out_keys + row * p.W;
+    const int32_t *kd = p.kinds + (b * p.nQT + (i >> 7)) * p.nKT;
+    uint32_t *full = fullbits[threadIdx.x >> 6];
+    const bool in_lds = p.nKT <= 32 * kFullWords;
+    if (skip_full && in_lds) {
+        for (int64_t t0 = 0; t0 < p.nKT; t0 += 64) {
+            const int64_t t = t0 + lane;
+            const uint64_t f = __ballot(t < p.nKT && kd[t] == 2);
+            if (lane == 0) {
+                full[t0 >> 5] = (uint32_t)f;
+                if ((t0 >> 5) + 1 < kFullWords) full[(t0 >> 5) + 1] = (uint32_t)(f >> 32);
+            }
+        }
+    }
+    wave_lds_sync();
+    // word w lies in tile w / 4
+    auto tile_full = [&](int64_t t) {
+        return in_lds ? ((full[t >> 5] >> (t & 31)) & 1u) != 0u : kd[t] == 2;
+    };
+    constexpr int kR = 4;
+    int base = 0;
+    for (int64_t w0 = 0; w0 < nwords; w0 += 64 * kR) {
+        uint32_t bits[kR];
+#pragma unroll
+        for (int u = 0; u < kR; ++u) {
+            const int64_t w = w0 + 64 * u + lane;
+            bits[u] = w < nwords ? m[w] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kR; ++u) {
+            const int64_t w = w0 + 64 * u + lane;
+            uint32_t x = bits[u];
+            if (skip_full && x != 0u && tile_full(w >> 2)) x = 0u;
+            const int c = __popc(x);
+            int inc = c;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int t = __shfl_up(inc, off);
+                if (lane >= off) inc += t;
+            }
+            int pos = base + inc - c;
+            while (x) {
+                const int bit = __ffs(x) - 1;
+                x &= x - 1;
+                out[pos++] = (int32_t)(w * 32 + bit);
+            }
+            base += __shfl(inc, 63);
+        }
+    }
+    for (int64_t s2 = base + lane; s2 < p.W; s2 += 64) out[s2] = -1;
+    if (lane == 0) out_cnt[row] = base;
+}
+
 }  // namespace
 
 hipError_t launch_partial_keys(const Problem &p, hipStream_t s)
 {
     const int64_t rows = p.B * p.Sq;
-    hipLaunchKernelGGL(k_partial_keys, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);
+    if (p.row_keys)
+        hipLaunchKernelGGL(k_partial_keys, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL(k_row_lists, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p,
+                           p.pkeys, p.pcnt, 1);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_keys(const Problem &p, int32_t *keys, int32_t *cnt, hipStream_t s)
+{
+    const int64_t rows = p.B * p.Sq;
+    hipLaunchKernelGGL(k_row_lists, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, keys,
+                       cnt, 0);
     return hipGetLastError();
 }
 
