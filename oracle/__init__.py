@@ -59,6 +59,8 @@ def _load():
         lib.orc_membership.argtypes = [P, ctypes.c_int32, I, I, I, I, I, P, P]
         lib.orc_block_membership.restype = None
         lib.orc_block_membership.argtypes = [P, I, I, P, P, P, P, I, I, P, P]
+        lib.orc_doc_membership.restype = None
+        lib.orc_doc_membership.argtypes = [P, P, I, I, I, I, I, P, P]
         lib.orc_tiles.restype = None
         lib.orc_tiles.argtypes = [P, I, I, I, I, I, I] + [P] * 9
         for name in ("orc_forward", "orc_backward_dq"):
@@ -136,6 +138,25 @@ def block_membership(sel_blocks: np.ndarray, lo: np.ndarray, hi: np.ndarray,
     has = np.empty((1, T), dtype=np.uint8)
     _load().orc_block_membership(_ptr(sel), T, NB, *[_ptr(a) for a in meta], block_size, stride,
                                  _ptr(memb), _ptr(has))
+    return memb, has
+
+
+def doc_membership(q_doc: np.ndarray, kv_doc: np.ndarray,
+                   q_global_start: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """Byte membership ``[B, Sq, stride]`` and ``has_routes`` ``[B, Sq]`` of causal
+    attention within documents: query i (global position q_global_start + i) sees key
+    j iff its document id is nonzero, equals key j's, and j <= its position ("fa4"
+    page, ``document_causal_fa4_attention``)."""
+    qd = np.ascontiguousarray(q_doc, dtype=np.int32)
+    kd = np.ascontiguousarray(kv_doc, dtype=np.int32)
+    B, Sq = qd.shape
+    Skv = kd.shape[1]
+    assert kd.shape[0] == B
+    stride = row_stride(Skv)
+    memb = np.empty((B, Sq, stride), dtype=np.uint8)
+    has = np.empty((B, Sq), dtype=np.uint8)
+    _load().orc_doc_membership(_ptr(qd), _ptr(kd), B, Sq, Skv, q_global_start, stride,
+                               _ptr(memb), _ptr(has))
     return memb, has
 
 

@@ -25,6 +25,12 @@
  *    maps to an earlier block). This is the lookup of the cuDNN Frontend QSA
  *    page, section "Selection and components"; the per-block token spans
  *    (block_first, block_last) do not enter it.
+ *  - Document-causal selection. Query i of batch row b, at global position
+ *    p = q_global_start + i, is allowed key j iff q_doc[b, i] != 0,
+ *    kv_doc[b, j] == q_doc[b, i] and j <= p: causal attention within the
+ *    query's document, padding queries (document 0) attending to nothing.
+ *    This is the "fa4" page's `document_causal_fa4_attention`, a query shard
+ *    against the global keys.
  *  - Forward. For every query head h of KV group g = h / (Hq / Hkv):
  *    s_j = scale * <q, k_j> over j in R, lse = log sum_j exp(s_j),
  *    o = sum_j exp(s_j - lse) v_j; an empty R gives o = 0 and lse = -inf.
@@ -145,6 +151,28 @@ void orc_block_membership(const uint8_t *sel, int64_t T, int64_t NB, const int32
             any |= allowed;
         }
         has[t] = (uint8_t)any;
+    }
+}
+
+/* Byte membership [B, Sq, stride] and has_routes [B, Sq] of document-causal
+ * selection: every (b, i, j) tested as above. */
+void orc_doc_membership(const int32_t *q_doc, const int32_t *kv_doc, int64_t B, int64_t Sq,
+                        int64_t Skv, int64_t q_global_start, int64_t stride, uint8_t *memb,
+                        uint8_t *has)
+{
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < B * Sq; ++r) {
+        const int64_t b = r / Sq, i = r % Sq;
+        const int32_t d = q_doc[r];
+        const int64_t p = q_global_start + i;
+        uint8_t *row = memb + r * stride;
+        int any = 0;
+        for (int64_t j = 0; j < stride; ++j) {
+            const int allowed = j < Skv && d != 0 && kv_doc[b * Skv + j] == d && j <= p;
+            row[j] = (uint8_t)allowed;
+            any |= allowed;
+        }
+        has[r] = (uint8_t)any;
     }
 }
 
