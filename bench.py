@@ -277,6 +277,55 @@ def gather_ceiling(torch, lib, hip, stream, row_bytes: int, footprint_bytes: int
     return n_items * item_bytes / (best * 1e-3) / 1e9
 
 
+def doc_causal_step(torch, qsa, hip, stream, wl, n_docs: int = 4, steps: int = 3) -> dict:
+    """Causal attention within documents (the dense comparison workload): the same
+    token count and heads as the metric's workload, `n_docs` documents at seeded cut
+    points, one step = qsa_doc_plan_build + planned forward + planned backward,
+    timed with HIP events; sparse TFLOP/s counted like the metric (14 * Hq * 256 per
+    (query, key) pair)."""
+    T = wl.Sq
+    rng = np.random.default_rng(1000 + n_docs)
+    cuts = np.sort(rng.choice(np.arange(1, T), n_docs - 1, replace=False))
+    starts = np.concatenate([[0], cuts]).astype(np.int64)
+    ids = np.zeros(T, np.int32)
+    for n, s0 in enumerate(starts):
+        ids[s0:] = n + 1
+    lens = np.diff(np.concatenate([starts, [T]]))
+    pairs = int((lens * (lens + 1) // 2).sum())
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(11)
+
+    def rnd(*shape):
+        return torch.randn(*shape, generator=g).to(torch.bfloat16).to(dev)
+
+    q, k, v, go = rnd(1, T, wl.Hq, 256), rnd(1, T, wl.Hkv, 256), rnd(1, T, wl.Hkv, 256), \
+        rnd(1, T, wl.Hq, 256)
+    qd = torch.from_numpy(ids[None]).to(dev)
+    plan = qsa.doc_plan_build(qd, qd, Hkv=wl.Hkv)
+    out, out32, lse = qsa.forward_planned(plan, q, k, v, wl.scale)
+    dq, dk, dv = qsa.backward_planned(plan, go, q, k, v, out32, lse, wl.scale)
+    torch.cuda.synchronize()
+    ev = Events(hip, 4)
+    times = []
+    for _ in range(steps):
+        hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), ctypes.c_void_p(stream))
+        qsa.doc_plan_build(qd, qd, Hkv=wl.Hkv, plan_mem=plan.mem)
+        hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), ctypes.c_void_p(stream))
+        qsa.forward_planned(plan, q, k, v, wl.scale, out=out, out_fp32=out32, lse=lse)
+        hip.hipEventRecord(ctypes.c_void_p(ev.ev[2]), ctypes.c_void_p(stream))
+        qsa.backward_planned(plan, go, q, k, v, out32, lse, wl.scale, dq=dq, dk=dk, dv=dv)
+        hip.hipEventRecord(ctypes.c_void_p(ev.ev[3]), ctypes.c_void_p(stream))
+        torch.cuda.synchronize()
+        times.append([ev.elapsed(0, 1), ev.elapsed(1, 2), ev.elapsed(2, 3)])
+    t = np.median(np.array(times), axis=0)
+    ms = float(t.sum())
+    return {"workload": f"doc_causal_t{T}_{n_docs}docs_12q{wl.Hkv}kv", "T": T,
+            "documents": n_docs, "pairs": pairs, "ms_per_step": ms,
+            "plan_ms": float(t[0]), "forward_ms": float(t[1]), "backward_ms": float(t[2]),
+            "tflops": (COUNTED_FWD + COUNTED_BWD) * wl.Hq * pairs / (ms * 1e-3) / 1e12,
+            "steps": steps, "note": "median of the timed steps (HIP events), after one warm-up"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -286,6 +335,8 @@ def main() -> int:
                     help="workload name or index 1-5 (default: the 32k-token long-context one)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-doc-causal", action="store_true",
+                    help="skip the document-causal (dense) comparison step")
     ap.add_argument("--plain", action="store_true",
                     help="time qsa_forward + qsa_backward (preprocessing in each call) instead "
                          "of one plan build and the planned calls")
@@ -538,6 +589,9 @@ def main() -> int:
         "kernels": {n: {k2: v2 for k2, v2 in r.items() if k2 != "kernel"}
                     for n, r in per_kernel.items()},
     }
+    if not args.no_doc_causal:
+        print("[bench] document-causal comparison", file=sys.stderr, flush=True)
+        res["doc_causal"] = doc_causal_step(torch, qsa, hip, stream, wl)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(inp, wl, nnz_row, args.cpu_seconds)

@@ -291,6 +291,49 @@ qsa_status qsa_block_backward(const qsa_block_dims *dims, const void *grad_out, 
                               void *dq, void *dk, void *dv, void *workspace,
                               size_t workspace_bytes, void *stream);
 /*
+ * Document-causal attention: causal attention within documents, for a
+ * contiguous query shard against the global keys (the "fa4" page,
+ * `document_causal_fa4_attention`, and its module summary: packed documents
+ * and context parallelism with contiguous shards). Query i of batch row b sits
+ * at global position q_global_start + i and attends to key j iff
+ *     q_doc_ids[b, i] != 0, kv_doc_ids[b, j] == q_doc_ids[b, i] and
+ *     j <= q_global_start + i.
+ * Document ids are 1-based; 0 marks padding: a padding query gets zero output
+ * and gradients and lse = -inf, and a padding key is never attended. Any id
+ * layout is taken as written (a document need not be one contiguous run).
+ * Everything else is as for route rows: the document ids are expanded on the
+ * device into the same per-row key sets, and a plan built from them serves
+ * the planned calls and qsa_plan_tables.
+ *
+ * Layouts: q_doc_ids int32 [B, Sq], kv_doc_ids int32 [B, Skv] (device, 4-byte
+ * aligned); tensors as for qsa_forward. q_global_start >= 0 (a shard's first
+ * query position; 0 for self-attention over the whole sequence). The plan's
+ * dims are B, Sq, Skv, Hq, Hkv, D with W = min(Skv, q_global_start + Sq), the
+ * most keys a row can hold (per-row key lists sized for that: 4 bytes per key
+ * slot and row).
+ */
+typedef struct qsa_doc_dims {
+    int64_t B, Sq, Skv, Hq, Hkv, D; /* as in qsa_dims */
+    int64_t q_global_start;         /* global position of query 0, >= 0 */
+    int32_t flags;                  /* QSA_FLAG_* bits */
+    int32_t reserved;               /* must be 0 (else QSA_ERR_ROUTE_DTYPE, as an unknown flag) */
+} qsa_doc_dims;
+size_t qsa_doc_plan_bytes(const qsa_doc_dims *dims);
+size_t qsa_doc_forward_workspace_bytes(const qsa_doc_dims *dims);
+size_t qsa_doc_backward_workspace_bytes(const qsa_doc_dims *dims);
+qsa_status qsa_doc_plan_build(const qsa_doc_dims *dims, const int32_t *q_doc_ids,
+                              const int32_t *kv_doc_ids, void *plan_mem, size_t plan_bytes,
+                              qsa_plan *plan, void *stream);
+qsa_status qsa_doc_forward(const qsa_doc_dims *dims, const void *q, const void *k, const void *v,
+                           const int32_t *q_doc_ids, const int32_t *kv_doc_ids, float scale,
+                           void *out, float *out_fp32, float *lse, void *workspace,
+                           size_t workspace_bytes, void *stream);
+qsa_status qsa_doc_backward(const qsa_doc_dims *dims, const void *grad_out, const void *q,
+                            const void *k, const void *v, const float *out_fp32,
+                            const float *lse, const int32_t *q_doc_ids,
+                            const int32_t *kv_doc_ids, float scale, void *dq, void *dk, void *dv,
+                            void *workspace, size_t workspace_bytes, void *stream);
+/*
  * Copies of a built plan's tables, for inspection and bit-exact checks, in
  * the layouts qsa_preprocess documents, except that the membership comes bit
  * packed: mbits uint32 [B, Sq, stride / 32], bit (j % 32) of word j / 32 set

@@ -37,7 +37,9 @@ def test_header_declares_the_entry_points():
               "qsa_plan_tables", "qsa_forward_planned_timed", "qsa_backward_planned_timed",
               "qsa_block_plan_bytes", "qsa_block_plan_build", "qsa_block_forward",
               "qsa_block_backward", "qsa_block_forward_workspace_bytes",
-              "qsa_block_backward_workspace_bytes"):
+              "qsa_block_backward_workspace_bytes", "qsa_doc_plan_bytes", "qsa_doc_plan_build",
+              "qsa_doc_forward", "qsa_doc_backward", "qsa_doc_forward_workspace_bytes",
+              "qsa_doc_backward_workspace_bytes"):
         assert n in names
 
 
@@ -290,3 +292,55 @@ def test_block_entries_validate_before_touching_the_device(lib):
         assert fwd(bd, meta=unaligned_sel) == 9
         assert bwd(bd) == 9
         assert build(bd) == 9
+
+
+def test_doc_entries_validate_before_touching_the_device(lib):
+    import torch
+    from token_indexed_sparse_amd import qsa
+    a = ctypes.c_void_p(4096)
+
+    def dd(**kw):
+        base = dict(B=1, Sq=300, Skv=700, Hq=12, Hkv=1, D=256, q_global_start=400, flags=0,
+                    reserved=0)
+        base.update(kw)
+        return qsa.DocDims(**base)
+
+    d = dd()
+    plan = lib.qsa_doc_plan_bytes(ctypes.byref(d))
+    # per-row capacity min(Skv, q_global_start + Sq): a route plan of that width
+    assert plan == lib.qsa_plan_bytes(ctypes.byref(_dims(Sq=300, Skv=700, W=700)))
+    assert lib.qsa_doc_plan_bytes(ctypes.byref(dd(q_global_start=0))) == \
+        lib.qsa_plan_bytes(ctypes.byref(_dims(Sq=300, Skv=700, W=300)))
+    pf = lib.qsa_doc_forward_workspace_bytes(ctypes.byref(d))
+    pb = lib.qsa_doc_backward_workspace_bytes(ctypes.byref(d))
+    assert pf > plan and pb > pf
+
+    def fwd(d, ids=(a, a), ws=pf, scale=0.0625):
+        return lib.qsa_doc_forward(ctypes.byref(d), a, a, a, *ids, scale, a, a, a, a, ws, None)
+
+    def bwd(d, ids=(a, a), ws=pb, scale=0.0625):
+        return lib.qsa_doc_backward(ctypes.byref(d), a, a, a, a, a, a, *ids, scale, a, a, a, a,
+                                    ws, None)
+
+    def build(d, ids=(a, a), nbytes=plan):
+        pl = qsa.PlanStruct(tag=5)
+        st = lib.qsa_doc_plan_build(ctypes.byref(d), *ids, a, nbytes, ctypes.byref(pl), None)
+        assert pl.tag == 0
+        return st
+
+    for call in (fwd, bwd, build):
+        assert call(dd(q_global_start=-1)) == 2
+        assert call(dd(Sq=0)) == 2
+        assert call(dd(D=128)) == 4
+        assert call(dd(Hq=16)) == 3
+        assert call(dd(flags=4)) == 7
+        assert call(dd(reserved=1)) == 7
+        assert call(d, ids=(None, a)) == 1
+        assert call(d, ids=(a, None)) == 1
+        assert call(d, ids=(ctypes.c_void_p(4098), a)) == 6
+    assert fwd(d, ws=pf - 1) == 8
+    assert bwd(d, ws=pb - 1) == 8
+    assert build(d, nbytes=plan - 1) == 8
+    assert fwd(d, scale=float("nan")) == 5
+    if not torch.cuda.is_available():
+        assert fwd(d) == 9 and bwd(d) == 9 and build(d) == 9

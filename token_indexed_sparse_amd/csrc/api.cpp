@@ -384,6 +384,58 @@ qsa_status build_block_plan(const qsa_dims *d, int64_t NB, const uint8_t *sel, c
     return QSA_OK;
 }
 
+// The route-set dims of a document-causal call: a row holds at most the keys
+// up to its global position, so min(Skv, q_global_start + Sq) per row.
+qsa_status doc_dims(const qsa_doc_dims *dd, qsa_dims *d)
+{
+    if (!dd) return QSA_ERR_NULL;
+    if (dd->reserved != 0) return QSA_ERR_ROUTE_DTYPE;
+    if (dd->q_global_start < 0 || dd->Sq < 1 || dd->Skv < 1 ||
+        dd->q_global_start > (int64_t(1) << 40))
+        return QSA_ERR_SHAPE;
+    d->B = dd->B;
+    d->Sq = dd->Sq;
+    d->Skv = dd->Skv;
+    d->Hq = dd->Hq;
+    d->Hkv = dd->Hkv;
+    d->D = dd->D;
+    const int64_t reach = dd->q_global_start + dd->Sq;
+    d->W = dd->Skv < reach ? dd->Skv : reach;
+    d->route_is_i64 = 0;
+    d->flags = dd->flags;
+    return check_dims(d);
+}
+
+qsa_status check_doc_ids(const int32_t *q_doc, const int32_t *kv_doc)
+{
+    if (!q_doc || !kv_doc) return QSA_ERR_NULL;
+    if (!aligned(q_doc, 4) || !aligned(kv_doc, 4)) return QSA_ERR_ALIGN;
+    return QSA_OK;
+}
+
+// Build a plan from document ids into plan_mem (validated by the caller).
+qsa_status build_doc_plan(const qsa_dims *d, const int32_t *q_doc, const int32_t *kv_doc,
+                          int64_t q_global_start, void *plan_mem, size_t plan_bytes,
+                          qsa_plan *plan, hipStream_t s)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QSA_ERR_DEVICE;
+    Problem p;
+    fill_common(p, d, nullptr, 1.f);
+    p.q_doc = q_doc;
+    p.kv_doc = kv_doc;
+    p.q_global_start = q_global_start;
+    carve(p, layout(d, kPlanParts), plan_mem);
+    if (launch_preprocess(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (launch_partial_keys(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    plan->dims = *d;
+    plan->mem = plan_mem;
+    plan->bytes = plan_bytes;
+    plan->device = dev;
+    plan->tag = QSA_PLAN_TAG;
+    return QSA_OK;
+}
+
 // Forward launches after validation. With `prep` the route preprocessing
 // runs first into the workspace; otherwise a plan supplies its results and
 // only the walk clocks are reset.
@@ -833,6 +885,101 @@ qsa_status qsa_block_backward(const qsa_block_dims *dims, const void *grad_out, 
     std::memset(&plan, 0, sizeof(plan));
     if ((st = build_block_plan(&d, dims->NB, sel_blocks, lo, hi, blk_base, tok_base, workspace,
                                plan_bytes, &plan, s)) != QSA_OK)
+        return st;
+    Problem p;
+    fill_common(p, &d, nullptr, scale);
+    carve(p, layout(&d, kPlanParts), workspace);
+    carve(p, L, static_cast<char *>(workspace) + plan_bytes);
+    return run_backward(p, grad_out, q, k, v, out_fp32, lse, dq, dk, dv, s, nullptr, false);
+}
+
+size_t qsa_doc_plan_bytes(const qsa_doc_dims *dims)
+{
+    qsa_dims d;
+    return doc_dims(dims, &d) == QSA_OK ? layout(&d, kPlanParts).total : 0;
+}
+
+size_t qsa_doc_forward_workspace_bytes(const qsa_doc_dims *dims)
+{
+    qsa_dims d;
+    if (doc_dims(dims, &d) != QSA_OK) return 0;
+    return layout(&d, kPlanParts).total + layout(&d, kFwd | kWalk).total;
+}
+
+size_t qsa_doc_backward_workspace_bytes(const qsa_doc_dims *dims)
+{
+    qsa_dims d;
+    if (doc_dims(dims, &d) != QSA_OK) return 0;
+    return layout(&d, kPlanParts).total + layout(&d, kBwd | kWalk).total;
+}
+
+qsa_status qsa_doc_plan_build(const qsa_doc_dims *dims, const int32_t *q_doc_ids,
+                              const int32_t *kv_doc_ids, void *plan_mem, size_t plan_bytes,
+                              qsa_plan *plan, void *stream)
+{
+    if (!plan) return QSA_ERR_NULL;
+    std::memset(plan, 0, sizeof(*plan));
+    qsa_dims d;
+    qsa_status st = doc_dims(dims, &d);
+    if (st != QSA_OK) return st;
+    if ((st = check_doc_ids(q_doc_ids, kv_doc_ids)) != QSA_OK) return st;
+    if ((st = check_workspace(plan_mem, plan_bytes, layout(&d, kPlanParts).total)) != QSA_OK)
+        return st;
+    if ((st = check_device(&d)) != QSA_OK) return st;
+    return build_doc_plan(&d, q_doc_ids, kv_doc_ids, dims->q_global_start, plan_mem, plan_bytes,
+                          plan, static_cast<hipStream_t>(stream));
+}
+
+qsa_status qsa_doc_forward(const qsa_doc_dims *dims, const void *q, const void *k, const void *v,
+                           const int32_t *q_doc_ids, const int32_t *kv_doc_ids, float scale,
+                           void *out, float *out_fp32, float *lse, void *workspace,
+                           size_t workspace_bytes, void *stream)
+{
+    qsa_dims d;
+    qsa_status st = doc_dims(dims, &d);
+    if (st != QSA_OK) return st;
+    if ((st = check_doc_ids(q_doc_ids, kv_doc_ids)) != QSA_OK) return st;
+    if ((st = check_forward_args(q, k, v, scale, out, out_fp32, lse)) != QSA_OK) return st;
+    const size_t plan_bytes = layout(&d, kPlanParts).total;
+    const Layout L = layout(&d, kFwd | kWalk);
+    if ((st = check_workspace(workspace, workspace_bytes, plan_bytes + L.total)) != QSA_OK)
+        return st;
+    if ((st = check_device(&d)) != QSA_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    qsa_plan plan;
+    std::memset(&plan, 0, sizeof(plan));
+    if ((st = build_doc_plan(&d, q_doc_ids, kv_doc_ids, dims->q_global_start, workspace,
+                             plan_bytes, &plan, s)) != QSA_OK)
+        return st;
+    Problem p;
+    fill_common(p, &d, nullptr, scale);
+    carve(p, layout(&d, kPlanParts), workspace);
+    carve(p, L, static_cast<char *>(workspace) + plan_bytes);
+    return run_forward(p, q, k, v, out, out_fp32, lse, s, nullptr, false);
+}
+
+qsa_status qsa_doc_backward(const qsa_doc_dims *dims, const void *grad_out, const void *q,
+                            const void *k, const void *v, const float *out_fp32,
+                            const float *lse, const int32_t *q_doc_ids,
+                            const int32_t *kv_doc_ids, float scale, void *dq, void *dk, void *dv,
+                            void *workspace, size_t workspace_bytes, void *stream)
+{
+    qsa_dims d;
+    qsa_status st = doc_dims(dims, &d);
+    if (st != QSA_OK) return st;
+    if ((st = check_doc_ids(q_doc_ids, kv_doc_ids)) != QSA_OK) return st;
+    if ((st = check_backward_args(grad_out, q, k, v, out_fp32, lse, scale, dq, dk, dv)) != QSA_OK)
+        return st;
+    const size_t plan_bytes = layout(&d, kPlanParts).total;
+    const Layout L = layout(&d, kBwd | kWalk);
+    if ((st = check_workspace(workspace, workspace_bytes, plan_bytes + L.total)) != QSA_OK)
+        return st;
+    if ((st = check_device(&d)) != QSA_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    qsa_plan plan;
+    std::memset(&plan, 0, sizeof(plan));
+    if ((st = build_doc_plan(&d, q_doc_ids, kv_doc_ids, dims->q_global_start, workspace,
+                             plan_bytes, &plan, s)) != QSA_OK)
         return st;
     Problem p;
     fill_common(p, &d, nullptr, scale);

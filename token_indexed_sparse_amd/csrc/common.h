@@ -28,13 +28,18 @@ struct Problem {
     int64_t stride;  // membership row stride = nKT * 128
     int64_t nQT, nKT;
     float scale;
-    // inputs: route rows, or (routes == nullptr) a block-selection bitmap
+    // inputs: route rows, or (routes == nullptr, sel set) a block-selection bitmap
     // sel [Sq, NB] with per-query lo, hi, blk_base, tok_base over packed
     // tokens (B == 1, Sq == Skv)
     const void *routes;
     const uint8_t *sel;
     const int32_t *sel_lo, *sel_hi, *sel_blk_base, *sel_tok_base;
     int64_t NB;
+    // or (routes == sel == nullptr) document-causal selection: query i of batch
+    // row b at global position q_global_start + i sees key j of its document
+    // (q_doc [B, Sq], kv_doc [B, Skv], 0 = padding) with j <= that position
+    const int32_t *q_doc, *kv_doc;
+    int64_t q_global_start;
     const uint16_t *q, *k, *v, *dout;
     const float *out_fp32_in, *lse_in;
     // preprocessing results (workspace or caller buffers)

@@ -143,6 +143,40 @@ __device__ __forceinline__ void fill_from_blocks(const Problem &p, uint32_t *bm,
     }
 }
 
+// Row (b, i)'s document-causal selection into its LDS bitmap ("fa4" page,
+// `document_causal_fa4_attention`): key j is a member iff the query's
+// document id d is nonzero, kv_doc[b, j] == d and j <= q_global_start + i.
+// Wave v takes the 64-key blocks v, v + 4, ... (four in flight): one ballot
+// per block gives its two bitmap words, written without atomics.
+__device__ __forceinline__ void fill_from_docs(const Problem &p, uint32_t *bm, int64_t row,
+                                               int tid)
+{
+    const int64_t b = row / p.Sq, i = row - b * p.Sq;
+    const int32_t d = p.q_doc[row];
+    const int64_t hi = min(p.q_global_start + i, p.Skv - 1);
+    if (d == 0 || hi < 0) return;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int32_t *kd = p.kv_doc + b * p.Skv;
+    constexpr int kU = 4;
+    for (int64_t c0 = 64 * wave; c0 <= hi; c0 += 64 * 4 * kU) {
+        int32_t v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t j = c0 + 64 * 4 * u + lane;
+            v[u] = j <= hi ? kd[j] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t j0 = c0 + 64 * 4 * u;
+            const uint64_t ball = __ballot(j0 + lane <= hi && v[u] == d);
+            if (j0 <= hi && lane == 0) {
+                bm[j0 >> 5] = (uint32_t)ball;
+                if ((j0 >> 5) + 1 < (p.stride >> 5)) bm[(j0 >> 5) + 1] = (uint32_t)(ball >> 32);
+            }
+        }
+    }
+}
+
 // Everything after the row's bitmap is built: membership outputs, key list,
 // count and tile counts.
 __device__ __forceinline__ void finish_row(const Problem &p, uint32_t *bm, uint32_t *scan,
@@ -255,6 +289,21 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_rows(Problem p)
     for (int64_t w = tid; w < nwords; w += kPrepThreads) bm[w] = 0u;
     __syncthreads();
     fill_from_routes<RouteT>(p, bm, row, tid);
+    __syncthreads();
+    finish_row(p, bm, scan, row, tid);
+}
+
+__global__ __launch_bounds__(kPrepThreads) void k_prep_rows_docs(Problem p)
+{
+    extern __shared__ uint32_t lds[];
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t nwords = p.stride >> 5;
+    uint32_t *bm = lds;
+    uint32_t *scan = lds + nwords;
+    for (int64_t w = tid; w < nwords; w += kPrepThreads) bm[w] = 0u;
+    __syncthreads();
+    fill_from_docs(p, bm, row, tid);
     __syncthreads();
     finish_row(p, bm, scan, row, tid);
 }
@@ -506,8 +555,11 @@ hipError_t launch_preprocess(const Problem &p, hipStream_t s)
     const hipError_t e = launch_walk_reset(p, s);
     if (e != hipSuccess) return e;
     const size_t lds = prep_lds_base(p) + (prep_stage_keys(p) ? (size_t)p.W * 4 : 0);
-    if (!p.routes)
+    if (!p.routes && p.sel)
         hipLaunchKernelGGL(k_prep_rows_blocks, dim3((unsigned)(p.B * p.Sq)), dim3(kPrepThreads),
+                           lds, s, p);
+    else if (!p.routes)
+        hipLaunchKernelGGL(k_prep_rows_docs, dim3((unsigned)(p.B * p.Sq)), dim3(kPrepThreads),
                            lds, s, p);
     else if (p.route_is_i64)
         hipLaunchKernelGGL(k_prep_rows<int64_t>, dim3((unsigned)(p.B * p.Sq)), dim3(kPrepThreads),

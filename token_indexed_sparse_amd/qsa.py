@@ -49,6 +49,14 @@ class BlockDims(ctypes.Structure):
                 ("flags", ctypes.c_int32)]
 
 
+class DocDims(ctypes.Structure):
+    """``qsa_doc_dims``: shapes, the query shard's global start, flags."""
+    _fields_ = [("B", ctypes.c_int64), ("Sq", ctypes.c_int64), ("Skv", ctypes.c_int64),
+                ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64), ("D", ctypes.c_int64),
+                ("q_global_start", ctypes.c_int64), ("flags", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
 class PlanStruct(ctypes.Structure):
     """``qsa_plan``: the host record of a built route plan."""
     _fields_ = [("dims", Dims), ("mem", ctypes.c_void_p), ("bytes", ctypes.c_size_t),
@@ -97,6 +105,17 @@ def library() -> ctypes.CDLL:
         lib.qsa_block_forward.argtypes = [BD] + [P] * 10 + [ctypes.c_float] + [P] * 4 + [S, P]
         lib.qsa_block_backward.restype = ctypes.c_int
         lib.qsa_block_backward.argtypes = [BD] + [P] * 13 + [ctypes.c_float] + [P] * 4 + [S, P]
+        DD = ctypes.POINTER(DocDims)
+        for name in ("qsa_doc_plan_bytes", "qsa_doc_forward_workspace_bytes",
+                     "qsa_doc_backward_workspace_bytes"):
+            getattr(lib, name).restype = S
+            getattr(lib, name).argtypes = [DD]
+        lib.qsa_doc_plan_build.restype = ctypes.c_int
+        lib.qsa_doc_plan_build.argtypes = [DD, P, P, P, S, PL, P]
+        lib.qsa_doc_forward.restype = ctypes.c_int
+        lib.qsa_doc_forward.argtypes = [DD] + [P] * 5 + [ctypes.c_float] + [P] * 4 + [S, P]
+        lib.qsa_doc_backward.restype = ctypes.c_int
+        lib.qsa_doc_backward.argtypes = [DD] + [P] * 8 + [ctypes.c_float] + [P] * 4 + [S, P]
         lib.qsa_plan_tables.restype = ctypes.c_int
         lib.qsa_plan_tables.argtypes = [PL] + [P] * 12 + [P]
         lib.qsa_status_string.restype = ctypes.c_char_p
@@ -546,5 +565,98 @@ def block_backward(grad_out, q, k, v, out_fp32, lse, sel_blocks, lo, hi, blk_bas
                                 sel.data_ptr(), *[t.data_ptr() for t in meta + spans],
                                 float(scale), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                 ws.data_ptr(), ws.numel() * ws.element_size(), _stream())
+    _raise(st)
+    return dq, dk, dv
+
+
+def _doc_args(q, k, q_doc_ids, kv_doc_ids, q_global_start, deterministic):
+    qd = _check(q_doc_ids, torch.int32, "q_doc_ids")
+    kd = _check(kv_doc_ids, torch.int32, "kv_doc_ids")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, Sq, Hq, 256] and k, v [B, Skv, Hkv, 256]")
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if tuple(qd.shape) != (B, Sq) or tuple(kd.shape) != (B, Skv):
+        raise ValueError("q_doc_ids must be [B, Sq] and kv_doc_ids [B, Skv]")
+    dd = DocDims(B, Sq, Skv, Hq, Hkv, D, int(q_global_start),
+                 FLAG_DETERMINISTIC if deterministic else 0, 0)
+    return dd, qd, kd
+
+
+def doc_plan_build(q_doc_ids, kv_doc_ids, *, Hkv: int = 1, q_global_start: int = 0,
+                   deterministic: bool = False, plan_mem: Optional[torch.Tensor] = None) -> Plan:
+    """Build a route plan of causal attention within documents (``qsa_doc_plan_build``):
+    q_doc_ids [B, Sq], kv_doc_ids [B, Skv], 1-based, 0 = padding."""
+    qd = _check(q_doc_ids, torch.int32, "q_doc_ids")
+    kd = _check(kv_doc_ids, torch.int32, "kv_doc_ids")
+    if qd.dim() != 2 or kd.dim() != 2 or qd.shape[0] != kd.shape[0]:
+        raise ValueError("q_doc_ids must be [B, Sq] and kv_doc_ids [B, Skv]")
+    dd = DocDims(qd.shape[0], qd.shape[1], kd.shape[1], GROUP * Hkv, Hkv, HEAD_DIM,
+                 int(q_global_start), FLAG_DETERMINISTIC if deterministic else 0, 0)
+    lib = library()
+    mem = _workspace(lib.qsa_doc_plan_bytes(ctypes.byref(dd)), qd.device, plan_mem)
+    struct = PlanStruct()
+    st = lib.qsa_doc_plan_build(ctypes.byref(dd), qd.data_ptr(), kd.data_ptr(), mem.data_ptr(),
+                                mem.numel() * mem.element_size(), ctypes.byref(struct),
+                                _stream())
+    _raise(st)
+    return Plan(struct, mem)
+
+
+def doc_forward(q, k, v, q_doc_ids, kv_doc_ids, scale: Optional[float] = None, *,
+                q_global_start: int = 0, out=None, out_fp32=None, lse=None, workspace=None,
+                deterministic: bool = False):
+    """Causal attention within documents (``qsa_doc_forward``); returns
+    ``(out, out_fp32, lse [B, Hq, Sq])``."""
+    q = _check(q, torch.bfloat16, "q")
+    k = _check(k, torch.bfloat16, "k")
+    v = _check(v, torch.bfloat16, "v")
+    if v.shape != k.shape:
+        raise ValueError("v must have k's shape")
+    dd, qd, kd = _doc_args(q, k, q_doc_ids, kv_doc_ids, q_global_start, deterministic)
+    if scale is None:
+        scale = 1.0 / (q.shape[-1] ** 0.5)
+    out = torch.empty_like(q) if out is None else out
+    out_fp32 = torch.empty(q.shape, dtype=torch.float32, device=q.device) if out_fp32 is None \
+        else out_fp32
+    lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32,
+                      device=q.device) if lse is None else lse
+    lib = library()
+    ws = _workspace(lib.qsa_doc_forward_workspace_bytes(ctypes.byref(dd)), q.device, workspace)
+    st = lib.qsa_doc_forward(ctypes.byref(dd), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                             qd.data_ptr(), kd.data_ptr(), float(scale), out.data_ptr(),
+                             out_fp32.data_ptr(), lse.data_ptr(), ws.data_ptr(),
+                             ws.numel() * ws.element_size(), _stream())
+    _raise(st)
+    return out, out_fp32, lse
+
+
+def doc_backward(grad_out, q, k, v, out_fp32, lse, q_doc_ids, kv_doc_ids,
+                 scale: Optional[float] = None, *, q_global_start: int = 0, dq=None, dk=None,
+                 dv=None, workspace=None, deterministic: bool = False):
+    """Backward of causal attention within documents (``qsa_doc_backward``)."""
+    grad_out = _check(grad_out, torch.bfloat16, "grad_out")
+    q = _check(q, torch.bfloat16, "q")
+    k = _check(k, torch.bfloat16, "k")
+    v = _check(v, torch.bfloat16, "v")
+    out_fp32 = _check(out_fp32, torch.float32, "out_fp32")
+    lse = _check(lse, torch.float32, "lse")
+    dd, qd, kd = _doc_args(q, k, q_doc_ids, kv_doc_ids, q_global_start, deterministic)
+    if grad_out.shape != q.shape or out_fp32.shape != q.shape:
+        raise ValueError("grad_out and out_fp32 must have q's shape")
+    if lse.shape != (q.shape[0], q.shape[2], q.shape[1]):
+        raise ValueError("lse must be [B, Hq, Sq]")
+    if scale is None:
+        scale = 1.0 / (q.shape[-1] ** 0.5)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    lib = library()
+    ws = _workspace(lib.qsa_doc_backward_workspace_bytes(ctypes.byref(dd)), q.device, workspace)
+    st = lib.qsa_doc_backward(ctypes.byref(dd), grad_out.data_ptr(), q.data_ptr(), k.data_ptr(),
+                              v.data_ptr(), out_fp32.data_ptr(), lse.data_ptr(), qd.data_ptr(),
+                              kd.data_ptr(), float(scale), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                              _stream())
     _raise(st)
     return dq, dk, dv
