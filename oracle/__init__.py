@@ -5,9 +5,10 @@ CPU-baseline leg of ``bench.py`` are the only callers. The product library
 never imports, links or runs anything in this package, and this package never
 imports the product.
 
-The arithmetic lives in ``qsa_oracle.c`` (plain loops, double precision,
-OpenMP over rows); this module compiles it with gcc on first use, widens the
-bf16 inputs exactly to float64 and marshals arrays through ctypes.
+The attention arithmetic lives in ``qsa_oracle.c`` (plain loops, double
+precision, OpenMP over rows); this module compiles it with gcc on first use,
+widens the bf16 inputs exactly to float64 and marshals arrays through ctypes.
+The block selector (``select_*``) is plain numpy in float64 in this module.
 """
 from __future__ import annotations
 
@@ -304,3 +305,93 @@ class Problem:
         """dq [B, Sq, Hq, D], dk, dv [B, Skv, Hkv, D]."""
         dq, dk, dv = self.backward_rows()
         return dq.reshape(self.B, self.Sq, self.Hq, self.D), dk, dv
+
+
+
+# ---- block selector (cuDNN Frontend QSA page, "Finding QSA attention and its
+# indexer"; route format: NeMo AutoModel QSA page, `cudnn_sparse_gqa_attention`
+# and the routes parameter of the packed-coordinate translation) ----
+
+def _select_meta(B: int, Sq: int, doc_start, blk_base):
+    s = np.zeros((B, Sq), np.int64) if doc_start is None else np.asarray(doc_start, np.int64)
+    base = np.zeros((B, Sq), np.int64) if blk_base is None else np.asarray(blk_base, np.int64)
+    return s, base
+
+
+def select_visible(B: int, Sq: int, NB: int, q_offset: int = 0, doc_start=None,
+                   blk_base=None) -> tuple[np.ndarray, np.ndarray]:
+    """Which compressed blocks each query may score. Query t of batch row b sits at
+    position p = q_offset + t; its document starts at s = doc_start[b, t] (0 without
+    metadata) and block j of the document (tokens s + 4j .. s + 4j + 3) is row
+    blk_base[b, t] + j of kbar[b] (j without metadata). A block is visible when it is
+    complete before the query's own block, j < (p - s) // 4, and its row exists,
+    0 <= row < NB. A query with s < 0 or s > p is padding and sees nothing.
+    Returns (visible [B, Sq, NB] bool over kbar rows, c [B, Sq] = (p - s) // 4 or -1
+    for padding)."""
+    s, base = _select_meta(B, Sq, doc_start, blk_base)
+    p = q_offset + np.arange(Sq, dtype=np.int64)[None, :]
+    pad = (s < 0) | (s > p)
+    c = np.where(pad, -1, (p - s) // 4)
+    r = np.arange(NB, dtype=np.int64)[None, None, :]
+    j = r - base[:, :, None]
+    vis = (j >= 0) & (j < c[:, :, None])
+    return vis, c
+
+
+def select_scores(q_idx: np.ndarray, kbar: np.ndarray, scale: float, q_offset: int = 0,
+                  doc_start=None, blk_base=None) -> np.ndarray:
+    """Block scores in FP64: scale * sum over heads h of relu(q_idx[b, t, h] . kbar[b, r])
+    for every visible kbar row r (see select_visible), -inf elsewhere. q_idx [B, Sq, H, d]
+    and kbar [B, NB, d], bf16 bit patterns (widened exactly) or float arrays; returns
+    [B, Sq, NB] indexed by kbar row."""
+    q = widen(q_idx) if q_idx.dtype == np.uint16 else np.asarray(q_idx, np.float64)
+    k = widen(kbar) if kbar.dtype == np.uint16 else np.asarray(kbar, np.float64)
+    B, Sq = q.shape[:2]
+    NB = k.shape[1]
+    vis, _ = select_visible(B, Sq, NB, q_offset, doc_start, blk_base)
+    out = np.full((B, Sq, NB), -np.inf)
+    for b in range(B):
+        dots = np.matmul(q[b], k[b].T)                     # [Sq, H, NB]: every head's dot
+        score = scale * np.maximum(dots, 0.0).sum(axis=1)   # relu per head, then the sum
+        out[b] = np.where(vis[b], score, -np.inf)
+    return out
+
+
+def select_blocks(scores: np.ndarray, top_k: int, q_offset: int = 0, doc_start=None,
+                  blk_base=None) -> np.ndarray:
+    """The selector's output, local block numbers [B, Sq, top_k]: per query the top_k
+    visible blocks by score (all of them when fewer are visible), listed in ascending
+    order and padded with -1. Blocks of equal score rank by block number, the lower
+    first (the pages leave the tie rule open)."""
+    B, Sq, NB = scores.shape
+    vis, _ = select_visible(B, Sq, NB, q_offset, doc_start, blk_base)
+    _, base = _select_meta(B, Sq, doc_start, blk_base)
+    out = np.full((B, Sq, top_k), -1, np.int32)
+    for b in range(B):
+        for t in range(Sq):
+            rows = np.nonzero(vis[b, t])[0]
+            ranked = sorted(rows.tolist(), key=lambda r: (-scores[b, t, r], r))
+            chosen = np.sort(np.array(ranked[:top_k], np.int64)) - base[b, t]
+            out[b, t, :len(chosen)] = chosen
+    return out
+
+
+def select_routes(blocks: np.ndarray, q_offset: int = 0, doc_start=None) -> np.ndarray:
+    """Expansion of the selector's block numbers to route rows [B, Sq, 4 top_k + 4]: the
+    chosen blocks' token IDs s + 4j .. s + 4j + 3 in the order given, -1 for unused
+    slots, then the query's own incomplete block, tokens s + 4((p - s) // 4) .. p,
+    padded with -1 to four slots. Padding queries get a row of -1."""
+    B, Sq, top_k = blocks.shape
+    s, _ = _select_meta(B, Sq, doc_start, None)
+    out = np.full((B, Sq, 4 * top_k + 4), -1, np.int32)
+    for b in range(B):
+        for t in range(Sq):
+            p, st = q_offset + t, int(s[b, t])
+            if st < 0 or st > p:
+                continue
+            for n, j in enumerate(blocks[b, t]):
+                if j >= 0:
+                    out[b, t, 4 * n:4 * n + 4] = st + 4 * j + np.arange(4)
+            own = np.arange(st + 4 * ((p - st) // 4), p + 1)
+            out[b, t, 4 * top_k:4 * top_k + len(own)] = own
+    return out
