@@ -366,6 +366,64 @@ qsa_status qsa_forward_noalloc(const qsa_dims *dims, const void *q, const void *
                                const void *routes, float scale, void *out, float *out_fp32,
                                float *lse, void *stream);
 
+/*
+ * Block selector (cuDNN Frontend QSA page, "Finding QSA attention and its
+ * indexer"): the step that produces the route rows the calls above consume.
+ *
+ * Query t (0 <= t < Sq) of batch row b sits at position p = q_offset + t.
+ * Its document starts at s = doc_start[b, t] and block j of the document
+ * (tokens s + 4j .. s + 4j + 3, compression ratio four) is row
+ * blk_base[b, t] + j of kbar[b]; with doc_start NULL every s is 0, with
+ * blk_base NULL every base is 0. Block j is visible when it is complete
+ * before the query's own block, j < (p - s) / 4 (integer division), and its
+ * kbar row lies in [0, NB). A query with s < 0 or s > p is padding.
+ *
+ * Each visible block scores scale * sum over h < H of
+ * relu(q_idx[b, t, h, :] . kbar[b, row, :]); each query keeps its top_k
+ * visible blocks (all of them when fewer are visible), larger score first and,
+ * between equal scores, the lower block number first (the pages leave the tie
+ * rule open).
+ *
+ * Layouts (device memory, contiguous):
+ *   q_idx      bf16 [B, Sq, H, D], 16-byte aligned
+ *   kbar       bf16 [B, NB, D], 16-byte aligned
+ *   doc_start  int32 [B, Sq] or NULL, 4-byte aligned
+ *   blk_base   int32 [B, Sq] or NULL, 4-byte aligned
+ * Outputs, each optional (NULL = not written), at least one not NULL:
+ *   blocks     int32 [B, Sq, top_k]: the kept block numbers j in ascending
+ *              order, then -1; padding queries: all -1. 4-byte aligned.
+ *   routes     int32 [B, Sq, 4 top_k + 4], 16-byte aligned: route rows in the
+ *              form qsa_forward takes (NeMo AutoModel QSA page,
+ *              cudnn_sparse_gqa_attention): for the n-th kept block j, slots
+ *              4n .. 4n+3 hold tokens s + 4j .. s + 4j + 3; slots up to 4 top_k
+ *              hold -1; slots 4 top_k .. 4 top_k + 3 hold the query's own
+ *              incomplete block, tokens s + 4((p - s) / 4) .. p, then -1.
+ *              Padding queries: all -1.
+ *   scores     float [B, Sq, NB] by kbar row: the score of every visible row,
+ *              -inf elsewhere.
+ * Shapes: B, Sq, NB >= 1; NB <= 32768; B * Sq < 2^31; 1 <= H <= 64; D = 128
+ * (else QSA_ERR_HEADDIM); 1 <= top_k <= 4096; q_offset >= 0 and
+ * q_offset + Sq < 2^31; flags = 0 (else QSA_ERR_ROUTE_DTYPE). scale finite and
+ * > 0 (QSA_ERR_SCALE).
+ * Workspace: qsa_select_workspace_bytes(dims) bytes (16-byte aligned; the
+ * scores of every query, B * Sq * NB floats), or none when `scores` is given,
+ * which then serves as that buffer. Work is enqueued on `stream`; the caller
+ * owns every buffer; errors are returned before anything is enqueued.
+ */
+typedef struct {
+    int64_t B, Sq, NB;
+    int64_t q_offset;  /* position of query 0 of every batch row */
+    int32_t H, D;      /* indexer heads and width */
+    int32_t top_k;
+    int32_t flags;
+} qsa_select_dims;
+
+size_t qsa_select_workspace_bytes(const qsa_select_dims *dims);
+qsa_status qsa_select(const qsa_select_dims *dims, const void *q_idx, const void *kbar,
+                      const int32_t *doc_start, const int32_t *blk_base, float scale,
+                      int32_t *blocks, int32_t *routes, float *scores, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *qsa_status_string(qsa_status status);
 

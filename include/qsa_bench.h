@@ -53,6 +53,15 @@ qsa_status qsa_backward_planned_timed(const qsa_plan *plan, const void *grad_out
                                       void *dv, void *workspace, size_t workspace_bytes,
                                       void *stream, void *const *events, int32_t n_events);
 
+/* The selector with stage events: stage 0 the scores (with the -inf fill of
+ * a caller's scores buffer), stage 1 the top-k selection and the outputs. */
+#define QSA_SELECT_STAGES 2
+qsa_status qsa_select_timed(const qsa_select_dims *dims, const void *q_idx, const void *kbar,
+                            const int32_t *doc_start, const int32_t *blk_base, float scale,
+                            int32_t *blocks, int32_t *routes, float *scores, void *workspace,
+                            size_t workspace_bytes, void *stream, void *const *events,
+                            int32_t n_events);
+
 /*
  * Gather-rate probe: stages rows rows[0 .. n_rows) of `src` (device memory of
  * src_bytes < 2^31; row i occupies bytes [rows[i] * row_bytes, + row_bytes))

@@ -39,7 +39,8 @@ def test_header_declares_the_entry_points():
               "qsa_block_backward", "qsa_block_forward_workspace_bytes",
               "qsa_block_backward_workspace_bytes", "qsa_doc_plan_bytes", "qsa_doc_plan_build",
               "qsa_doc_forward", "qsa_doc_backward", "qsa_doc_forward_workspace_bytes",
-              "qsa_doc_backward_workspace_bytes"):
+              "qsa_doc_backward_workspace_bytes", "qsa_select", "qsa_select_workspace_bytes",
+              "qsa_select_timed"):
         assert n in names
 
 
@@ -344,3 +345,42 @@ def test_doc_entries_validate_before_touching_the_device(lib):
     assert fwd(d, scale=float("nan")) == 5
     if not torch.cuda.is_available():
         assert fwd(d) == 9 and bwd(d) == 9 and build(d) == 9
+
+
+def test_select_validates_before_touching_the_device(lib):
+    import torch
+    from token_indexed_sparse_amd import qsa
+    a = ctypes.c_void_p(4096)
+
+    def sd(**kw):
+        base = dict(B=2, Sq=300, NB=80, q_offset=0, H=64, D=128, top_k=16, flags=0)
+        base.update(kw)
+        return qsa.SelectDims(**base)
+
+    d = sd()
+    need = lib.qsa_select_workspace_bytes(ctypes.byref(d))
+    assert need == 2 * 300 * 80 * 4
+    assert lib.qsa_select_workspace_bytes(ctypes.byref(sd(D=64))) == 0
+
+    def call(d, q=a, kb=a, meta=(None, None), scale=0.5, outs=(a, a, None), ws=a, wsb=need):
+        return lib.qsa_select(ctypes.byref(d), q, kb, *meta, scale, *outs, ws, wsb, None)
+
+    assert call(sd(D=64)) == 4
+    for bad in (dict(B=0), dict(Sq=0), dict(NB=0), dict(NB=32769), dict(H=0), dict(H=65),
+                dict(top_k=0), dict(top_k=4097), dict(q_offset=-1),
+                dict(q_offset=2 ** 31 - 300)):
+        assert call(sd(**bad)) == 2, bad
+    assert call(sd(flags=1)) == 7
+    assert call(d, q=None) == 1 and call(d, kb=None) == 1
+    assert call(d, outs=(None, None, None)) == 1
+    assert call(d, scale=0.0) == 5 and call(d, scale=float("inf")) == 5
+    assert call(d, q=ctypes.c_void_p(4104)) == 6
+    assert call(d, outs=(a, ctypes.c_void_p(4100), None)) == 6      # routes need 16 bytes
+    assert call(d, outs=(ctypes.c_void_p(4098), a, None)) == 6
+    assert call(d, meta=(ctypes.c_void_p(4098), None)) == 6
+    assert call(d, wsb=need - 1) == 8
+    assert call(d, ws=None) == 8
+    if not torch.cuda.is_available():
+        assert call(d) == 9
+        # a caller's scores buffer replaces the workspace
+        assert call(d, outs=(a, None, a), ws=None, wsb=0) == 9

@@ -500,6 +500,25 @@ qsa_status run_backward(Problem &p, const void *grad_out, const void *q, const v
     return QSA_OK;
 }
 
+// ---- block selector ----
+
+qsa_status check_select_dims(const qsa_select_dims *d)
+{
+    if (!d) return QSA_ERR_NULL;
+    if (d->flags != 0) return QSA_ERR_ROUTE_DTYPE;
+    if (d->D != kSelD) return QSA_ERR_HEADDIM;
+    if (d->B < 1 || d->Sq < 1 || d->NB < 1 || d->NB > 32768 || d->H < 1 || d->H > 64 ||
+        d->top_k < 1 || d->top_k > 4096 || d->q_offset < 0)
+        return QSA_ERR_SHAPE;
+    if (d->B > INT32_MAX / d->Sq || d->q_offset + d->Sq > (int64_t)INT32_MAX) return QSA_ERR_SHAPE;
+    return QSA_OK;
+}
+
+size_t select_scores_bytes(const qsa_select_dims *d)
+{
+    return (size_t)d->B * (size_t)d->Sq * (size_t)d->NB * sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
@@ -988,6 +1007,67 @@ qsa_status qsa_doc_backward(const qsa_doc_dims *dims, const void *grad_out, cons
     return run_backward(p, grad_out, q, k, v, out_fp32, lse, dq, dk, dv, s, nullptr, false);
 }
 
+size_t qsa_select_workspace_bytes(const qsa_select_dims *dims)
+{
+    return check_select_dims(dims) == QSA_OK ? select_scores_bytes(dims) : 0;
+}
+
+qsa_status qsa_select_timed(const qsa_select_dims *dims, const void *q_idx, const void *kbar,
+                            const int32_t *doc_start, const int32_t *blk_base, float scale,
+                            int32_t *blocks, int32_t *routes, float *scores, void *workspace,
+                            size_t workspace_bytes, void *stream, void *const *events,
+                            int32_t n_events)
+{
+    qsa_status st = check_select_dims(dims);
+    if (st != QSA_OK) return st;
+    if (!q_idx || !kbar || (!blocks && !routes && !scores)) return QSA_ERR_NULL;
+    if ((st = check_scale(scale)) != QSA_OK) return st;
+    if (!aligned(q_idx, 16) || !aligned(kbar, 16) || !aligned(doc_start, 4) ||
+        !aligned(blk_base, 4) || !aligned(blocks, 4) || !aligned(routes, 16) || !aligned(scores, 4))
+        return QSA_ERR_ALIGN;
+    if (!scores && (st = check_workspace(workspace, workspace_bytes, select_scores_bytes(dims))) !=
+                       QSA_OK)
+        return st;
+    if (events && n_events < QSA_SELECT_STAGES + 1) return QSA_ERR_NULL;
+    int dev = 0;
+    const DeviceInfo *info = device_info(dev);
+    if (!info || !info->ok) return QSA_ERR_DEVICE;
+
+    SelectProblem a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = static_cast<const uint16_t *>(q_idx);
+    a.kbar = static_cast<const uint16_t *>(kbar);
+    a.doc_start = doc_start;
+    a.blk_base = blk_base;
+    a.scores = scores ? scores : static_cast<float *>(workspace);
+    a.blocks = blocks;
+    a.routes = routes;
+    a.B = dims->B;
+    a.Sq = dims->Sq;
+    a.NB = dims->NB;
+    a.q_offset = dims->q_offset;
+    a.H = dims->H;
+    a.top_k = dims->top_k;
+    a.scale = scale;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (mark(events, 0, s) != hipSuccess) return QSA_ERR_DEVICE;
+    if (scores && launch_select_fill(a, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (launch_select_scores(a, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 1, s) != hipSuccess) return QSA_ERR_DEVICE;
+    if ((blocks || routes) && launch_select_topk(a, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (mark(events, 2, s) != hipSuccess) return QSA_ERR_DEVICE;
+    return QSA_OK;
+}
+
+qsa_status qsa_select(const qsa_select_dims *dims, const void *q_idx, const void *kbar,
+                      const int32_t *doc_start, const int32_t *blk_base, float scale,
+                      int32_t *blocks, int32_t *routes, float *scores, void *workspace,
+                      size_t workspace_bytes, void *stream)
+{
+    return qsa_select_timed(dims, q_idx, kbar, doc_start, blk_base, scale, blocks, routes, scores,
+                            workspace, workspace_bytes, stream, nullptr, 0);
+}
+
 const char *qsa_status_string(qsa_status status)
 {
     // A C caller may pass any int: read the bits as an integer, since a C++
@@ -1017,6 +1097,6 @@ const char *qsa_status_string(qsa_status status)
     return "unknown status";
 }
 
-int32_t qsa_version(void) { return (1 << 16) | 1; }
+int32_t qsa_version(void) { return (1 << 16) | 2; }
 
 }  // extern "C"

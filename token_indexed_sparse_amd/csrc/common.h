@@ -100,6 +100,25 @@ hipError_t launch_dq(const Problem &p, hipStream_t s);
 hipError_t launch_dkdv(const Problem &p, hipStream_t s);
 hipError_t launch_dkdv_reduce(const Problem &p, hipStream_t s);
 
+// Block selector: indexer queries q [B, Sq, H, kSelD] and compressed keys
+// kbar [B, NB, kSelD] (bf16), optional per-query document start and kbar row
+// base [B, Sq]; scores [B, Sq, NB] FP32 by kbar row; outputs block numbers
+// [B, Sq, top_k] and route rows [B, Sq, 4 top_k + 4] (either may be null).
+constexpr int kSelD = 128;
+struct SelectProblem {
+    const uint16_t *q, *kbar;
+    const int32_t *doc_start, *blk_base;
+    float *scores;
+    int32_t *blocks, *routes;
+    int64_t B, Sq, NB, q_offset;
+    int32_t H, top_k;
+    float scale;
+};
+
+hipError_t launch_select_fill(const SelectProblem &a, hipStream_t s);
+hipError_t launch_select_scores(const SelectProblem &a, hipStream_t s);
+hipError_t launch_select_topk(const SelectProblem &a, hipStream_t s);
+
 #if defined(__HIPCC__)
 __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
 {

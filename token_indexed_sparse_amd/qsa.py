@@ -57,6 +57,13 @@ class DocDims(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+class SelectDims(ctypes.Structure):
+    """``qsa_select_dims``: selector shapes, the query shard's position, top_k."""
+    _fields_ = [("B", ctypes.c_int64), ("Sq", ctypes.c_int64), ("NB", ctypes.c_int64),
+                ("q_offset", ctypes.c_int64), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
 class PlanStruct(ctypes.Structure):
     """``qsa_plan``: the host record of a built route plan."""
     _fields_ = [("dims", Dims), ("mem", ctypes.c_void_p), ("bytes", ctypes.c_size_t),
@@ -116,6 +123,11 @@ def library() -> ctypes.CDLL:
         lib.qsa_doc_forward.argtypes = [DD] + [P] * 5 + [ctypes.c_float] + [P] * 4 + [S, P]
         lib.qsa_doc_backward.restype = ctypes.c_int
         lib.qsa_doc_backward.argtypes = [DD] + [P] * 8 + [ctypes.c_float] + [P] * 4 + [S, P]
+        SD = ctypes.POINTER(SelectDims)
+        lib.qsa_select_workspace_bytes.restype = S
+        lib.qsa_select_workspace_bytes.argtypes = [SD]
+        lib.qsa_select.restype = ctypes.c_int
+        lib.qsa_select.argtypes = [SD, P, P, P, P, ctypes.c_float, P, P, P, P, S, P]
         lib.qsa_plan_tables.restype = ctypes.c_int
         lib.qsa_plan_tables.argtypes = [PL] + [P] * 12 + [P]
         lib.qsa_status_string.restype = ctypes.c_char_p
@@ -660,3 +672,51 @@ def doc_backward(grad_out, q, k, v, out_fp32, lse, q_doc_ids, kv_doc_ids,
                               _stream())
     _raise(st)
     return dq, dk, dv
+
+
+def select_dims(q_idx: torch.Tensor, kbar: torch.Tensor, top_k: int, q_offset: int = 0,
+                flags: int = 0) -> SelectDims:
+    """``qsa_select_dims`` for q_idx [B, Sq, H, D] and kbar [B, NB, D]."""
+    if q_idx.dim() != 4 or kbar.dim() != 3:
+        raise ValueError("q_idx must be [B, Sq, H, D] and kbar [B, NB, D]")
+    B, Sq, H, D = q_idx.shape
+    if kbar.shape[0] != B or kbar.shape[2] != D:
+        raise ValueError("kbar must be [B, NB, D] with q_idx's B and D")
+    return SelectDims(B, Sq, kbar.shape[1], q_offset, H, D, top_k, flags)
+
+
+def select(q_idx, kbar, top_k: int, scale: Optional[float] = None, *, q_offset: int = 0,
+           doc_start=None, blk_base=None, blocks: bool = True, routes: bool = True,
+           scores: bool = False, workspace=None):
+    """Block selector (``qsa_select``): scores every visible compressed block,
+    keeps each query's top_k and expands them to route rows. Returns
+    ``(blocks [B, Sq, top_k] | None, routes [B, Sq, 4 top_k + 4] | None,
+    scores [B, Sq, NB] | None)``, each only when asked for."""
+    q_idx = _check(q_idx, torch.bfloat16, "q_idx")
+    kbar = _check(kbar, torch.bfloat16, "kbar")
+    sd = select_dims(q_idx, kbar, top_k, q_offset)
+    B, Sq = q_idx.shape[:2]
+    meta = []
+    for name, m in (("doc_start", doc_start), ("blk_base", blk_base)):
+        if m is not None:
+            m = _check(m, torch.int32, name)
+            if m.shape != (B, Sq):
+                raise ValueError(f"{name} must be [B, Sq] int32")
+        meta.append(m)
+    if scale is None:
+        scale = 1.0 / (q_idx.shape[-1] ** 0.5)
+    dev = q_idx.device
+    bo = torch.empty((B, Sq, top_k), dtype=torch.int32, device=dev) if blocks else None
+    ro = torch.empty((B, Sq, 4 * top_k + 4), dtype=torch.int32, device=dev) if routes else None
+    so = torch.empty((B, Sq, kbar.shape[1]), dtype=torch.float32, device=dev) if scores else None
+    lib = library()
+    if so is None:
+        ws = _workspace(lib.qsa_select_workspace_bytes(ctypes.byref(sd)), dev, workspace)
+        ws_ptr, ws_bytes = ws.data_ptr(), ws.numel() * ws.element_size()
+    else:
+        ws_ptr, ws_bytes = None, 0
+    st = lib.qsa_select(ctypes.byref(sd), q_idx.data_ptr(), kbar.data_ptr(), _ptr(meta[0]),
+                        _ptr(meta[1]), float(scale), _ptr(bo), _ptr(ro), _ptr(so), ws_ptr,
+                        ws_bytes, _stream())
+    _raise(st)
+    return bo, ro, so
