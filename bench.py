@@ -33,6 +33,7 @@ Prints one JSON line:
 from __future__ import annotations
 
 import argparse
+import math
 import ctypes
 import json
 import os
@@ -326,6 +327,65 @@ def doc_causal_step(torch, qsa, hip, stream, wl, n_docs: int = 4, steps: int = 3
             "steps": steps, "note": "median of the timed steps (HIP events), after one warm-up"}
 
 
+def select_step(torch, qsa, lib, hip, stream, T: int, top_k: int, steps: int = 5) -> dict:
+    """Block selector at the metric workload's token count: T queries of one sequence,
+    T / 4 compressed blocks, 64 indexer heads of width 128, top_k blocks per query
+    (qsa_select_timed: stage 0 the MFMA scores, stage 1 the top-k and the block and
+    route outputs). Seeded normal inputs generated on the GPU. Returns the figures
+    and, under "_routes", the selected route rows."""
+    NB, H, D = T // 4, 64, 128
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(21)
+    qi = torch.randn((1, T, H, D), generator=gen, device=dev).to(torch.bfloat16)
+    kb = torch.randn((1, NB, D), generator=gen, device=dev).to(torch.bfloat16)
+    sd = qsa.select_dims(qi, kb, top_k)
+    ws = torch.empty(lib.qsa_select_workspace_bytes(ctypes.byref(sd)), dtype=torch.uint8,
+                     device=dev)
+    blocks = torch.empty((1, T, top_k), dtype=torch.int32, device=dev)
+    routes = torch.empty((1, T, 4 * top_k + 4), dtype=torch.int32, device=dev)
+    V, F, S, I32 = ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t, ctypes.c_int32
+    lib.qsa_select_timed.restype = ctypes.c_int
+    lib.qsa_select_timed.argtypes = [ctypes.POINTER(qsa.SelectDims)] + [V] * 4 + [F] + \
+        [V] * 4 + [S, V, V, I32]
+    scale = 1.0 / math.sqrt(D)
+
+    def call(e=None):
+        st = lib.qsa_select_timed(ctypes.byref(sd), qi.data_ptr(), kb.data_ptr(), None, None,
+                                  scale, blocks.data_ptr(), routes.data_ptr(), None,
+                                  ws.data_ptr(), ws.numel(), stream,
+                                  ctypes.cast(e.ev, ctypes.c_void_p) if e else None,
+                                  3 if e else 0)
+        assert st == 0, st
+
+    call()
+    torch.cuda.synchronize()
+    evs = [Events(hip, 3) for _ in range(steps)]
+    for e in evs:
+        call(e)
+    torch.cuda.synchronize()
+    t = np.median(np.array([[e.elapsed(0, 1), e.elapsed(1, 2)] for e in evs]), axis=0)
+    score_ms, topk_ms = float(t[0]), float(t[1])
+    pairs = int(np.minimum(np.arange(T, dtype=np.int64) // 4, NB).sum())
+    flop = 2 * H * D * pairs
+    tflops = flop / (score_ms * 1e-3) / 1e12
+    score_bytes = T * H * D * 2 + NB * D * 2 + 4 * pairs
+    topk_bytes = 4 * pairs + 4 * T * top_k + 4 * T * (4 * top_k + 4)
+    topk_gbs = topk_bytes / (topk_ms * 1e-3) / 1e9
+    return {"workload": f"select_t{T}_nb{NB}_h{H}_d{D}_top{top_k}", "T": T, "NB": NB,
+            "H": H, "D": D, "top_k": top_k, "visible_pairs": pairs,
+            "ms": score_ms + topk_ms, "steps": steps,
+            "scores": {"avg_launch_ms": score_ms, "bound": "mfma", "achieved": tflops,
+                       "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                       "frac": tflops / PEAK_BF16_TFLOPS, "flop_per_launch": flop,
+                       "algorithmic_bytes": score_bytes},
+            "topk": {"avg_launch_ms": topk_ms, "bound": "hbm", "achieved": topk_gbs,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": topk_gbs / PEAK_HBM_GBS,
+                     "algorithmic_bytes": topk_bytes},
+            "note": "median of the timed calls (HIP events), after one warm-up; workspace "
+                    "holds the scores between the two kernels",
+            "_routes": routes}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -337,6 +397,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-doc-causal", action="store_true",
                     help="skip the document-causal (dense) comparison step")
+    ap.add_argument("--no-select", action="store_true",
+                    help="skip the block selector measurement")
     ap.add_argument("--plain", action="store_true",
                     help="time qsa_forward + qsa_backward (preprocessing in each call) instead "
                          "of one plan build and the planned calls")
@@ -589,6 +651,44 @@ def main() -> int:
         "kernels": {n: {k2: v2 for k2, v2 in r.items() if k2 != "kernel"}
                     for n, r in per_kernel.items()},
     }
+    if not args.no_select:
+        print("[bench] block selector", file=sys.stderr, flush=True)
+        sel = select_step(torch, qsa, lib, hip, stream, wl.Sq, wl.n_max)
+        r_sel = sel.pop("_routes")
+        if not plain and wl.B == 1 and wl.Sq == wl.Skv and r_sel.shape == routes.shape:
+            # plan build + forward + backward over the selector's routes
+            sel_pairs = int((r_sel >= 0).sum().item())
+            times = []
+            for i in range(4):
+                hip.hipEventRecord(ctypes.c_void_p(pev[0].ev[0]), ctypes.c_void_p(stream))
+                st = lib.qsa_plan_build(ctypes.byref(dims), r_sel.data_ptr(), plan_mem.data_ptr(),
+                                        plan_mem.numel(), ctypes.byref(plan), stream)
+                assert st == 0, st
+                st = lib.qsa_forward_planned_timed(ctypes.byref(plan), q.data_ptr(), k.data_ptr(),
+                                                   v.data_ptr(), wl.scale, out.data_ptr(),
+                                                   out32.data_ptr(), lse.data_ptr(),
+                                                   ws_f.data_ptr(), ws_f.numel(), stream, None, 0)
+                assert st == 0, st
+                st = lib.qsa_backward_planned_timed(ctypes.byref(plan), g.data_ptr(),
+                                                    q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                    out32.data_ptr(), lse.data_ptr(), wl.scale,
+                                                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                                    ws_b.data_ptr(), ws_b.numel(), stream, None,
+                                                    0)
+                assert st == 0, st
+                hip.hipEventRecord(ctypes.c_void_p(pev[0].ev[1]), ctypes.c_void_p(stream))
+                torch.cuda.synchronize()
+                if i:
+                    times.append(pev[0].elapsed(0, 1))
+            att_ms = float(np.median(times))
+            sel["attention_on_selected"] = {
+                "pairs": sel_pairs, "ms_per_step": att_ms,
+                "tflops": (COUNTED_FWD + COUNTED_BWD) * wl.Hq * sel_pairs / (att_ms * 1e-3) / 1e12,
+                "select_plus_step_ms": att_ms + sel["ms"],
+                "note": "plan build + forward + backward of the metric's attention shapes over "
+                        "the route rows the selector produced (median of 3 after a warm-up)"}
+        del r_sel
+        res["select"] = sel
     if not args.no_doc_causal:
         print("[bench] document-causal comparison", file=sys.stderr, flush=True)
         res["doc_causal"] = doc_causal_step(torch, qsa, hip, stream, wl)
