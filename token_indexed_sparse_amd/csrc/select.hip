@@ -22,8 +22,8 @@ namespace {
 
 constexpr int kSelRow = kSelD * 2;                    // bytes per indexer row (bf16)
 constexpr int kSelWaves = 8;                          // waves per scoring work group
-constexpr int kSelTileRows = 64;                      // kbar rows per staged tile
-constexpr int kSelTileBytes = kSelTileRows * kSelRow;  // 16 KB
+constexpr int kSelTileRows = 128;                     // kbar rows per staged tile
+constexpr int kSelTileBytes = kSelTileRows * kSelRow;  // 32 KB, staged twice over
 
 // Position data of query t of batch row b: its document start s, the kbar row
 // base of its document and the visible kbar rows [r0, r1). A query whose
@@ -135,8 +135,8 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select_scores(SelectProblem 
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char *)tiles;
     auto stage = [&](int64_t row0, int buf) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int ins = 2 * wave + i;             // 16 instructions of 4 rows each
+        for (int i = 0; i < 4; ++i) {
+            const int ins = 4 * wave + i;  // 32 loads of 4 rows each
             const int rr = 4 * ins + (lane >> 4);
             const uint32_t off = (uint32_t)(row0 + rr) * kSelRow +
                                  (uint32_t)(((lane & 15) ^ (rr & 15)) << 4);
@@ -154,39 +154,45 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select_scores(SelectProblem 
         const int64_t row0 = R_lo + n * kSelTileRows;
         if (n + 1 < ntile) stage(row0 + kSelTileRows, buf ^ 1);
         const lds_char *tile = (const lds_char *)tiles + buf * kSelTileBytes;
-        float part[QW][4];
+        // Two halves of 64 rows, four slabs of 16 rows each.
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            uint4 Bv[4];
+        for (int hs = 0; hs < 2; ++hs) {
+            float part[QW][4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                Bv[k] = lds_read16(tile + (16 * s + col) * kSelRow + (((4 * k + quad) ^ col) << 4));
+            for (int s = 0; s < 4; ++s) {
+                uint4 Bv[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    Bv[k] = lds_read16(tile + (64 * hs + 16 * s + col) * kSelRow +
+                                       (((4 * k + quad) ^ col) << 4));
+#pragma unroll
+                for (int qi = 0; qi < QW; ++qi) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int g = 0; g < HG; ++g) {
+                        f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            c = mfma_16x16x32(A[qi][g][k], as_bf16x8(Bv[k]), c);
+                        acc += (fmaxf(c[0], 0.0f) + fmaxf(c[1], 0.0f)) +
+                               (fmaxf(c[2], 0.0f) + fmaxf(c[3], 0.0f));
+                    }
+                    part[qi][s] = acc;
+                }
+            }
+            // Reduce-scatter over the quads: lane (col, quad) ends with the sum
+            // over all heads for row row0 + 64 hs + 16 quad + col.
+            const bool upper = (quad & 2) != 0, odd = (quad & 1) != 0;
 #pragma unroll
             for (int qi = 0; qi < QW; ++qi) {
-                float acc = 0.0f;
-#pragma unroll
-                for (int g = 0; g < HG; ++g) {
-                    f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) c = mfma_16x16x32(A[qi][g][k], as_bf16x8(Bv[k]), c);
-                    acc += (fmaxf(c[0], 0.0f) + fmaxf(c[1], 0.0f)) +
-                           (fmaxf(c[2], 0.0f) + fmaxf(c[3], 0.0f));
-                }
-                part[qi][s] = acc;
+                const float s0 = upper ? part[qi][0] : part[qi][2];
+                const float s1 = upper ? part[qi][1] : part[qi][3];
+                const float w0 = (upper ? part[qi][2] : part[qi][0]) + __shfl_xor(s0, 32);
+                const float w1 = (upper ? part[qi][3] : part[qi][1]) + __shfl_xor(s1, 32);
+                const float sum = (odd ? w1 : w0) + __shfl_xor(odd ? w0 : w1, 16);
+                const int64_t r = row0 + 64 * hs + 16 * quad + col;
+                if (r >= qr0[qi] && r < qr1[qi]) srow[qi * a.NB + r] = a.scale * sum + 0.0f;
             }
-        }
-        // Reduce-scatter over the quads: lane (col, quad) ends with the sum over
-        // all heads for row row0 + 16 quad + col.
-        const bool upper = (quad & 2) != 0, odd = (quad & 1) != 0;
-#pragma unroll
-        for (int qi = 0; qi < QW; ++qi) {
-            const float s0 = upper ? part[qi][0] : part[qi][2];
-            const float s1 = upper ? part[qi][1] : part[qi][3];
-            const float w0 = (upper ? part[qi][2] : part[qi][0]) + __shfl_xor(s0, 32);
-            const float w1 = (upper ? part[qi][3] : part[qi][1]) + __shfl_xor(s1, 32);
-            const float sum = (odd ? w1 : w0) + __shfl_xor(odd ? w0 : w1, 16);
-            const int64_t r = row0 + 16 * quad + col;
-            if (r >= qr0[qi] && r < qr1[qi]) srow[qi * a.NB + r] = a.scale * sum + 0.0f;
         }
         QSA_WAIT_VM(0);
         __syncthreads();
@@ -214,31 +220,12 @@ __global__ void k_fill_f32(float *p, int64_t n, float v)
 // ---- top-k ----
 
 constexpr int kTopThreads = 256;
-
-// Exclusive prefix of v over the work group's threads in order; total in tot.
-// Ends with a barrier, so the scratch can be reused at once.
-__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t *wsum, uint32_t &tot)
-{
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    uint32_t incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-    }
-    if (lane == 63) wsum[w] = incl;
-    __syncthreads();
-    uint32_t pre = 0, t = 0;
-#pragma unroll
-    for (int i = 0; i < kTopThreads / 64; ++i) {
-        const uint32_t x = wsum[i];
-        pre += i < w ? x : 0u;
-        t += x;
-    }
-    __syncthreads();
-    tot = t;
-    return pre + incl - v;
-}
+constexpr int kBins = 2048;      // radix digit of 11 bits
+constexpr int kMaxCand = 64;     // boundary bins this small are ranked directly
+// Bin b lives at word b + b / 32: lane l of the bin search reads its 32 bins
+// at 33 l + j, 64 distinct banks for every j.
+constexpr int kHistWords = kBins + kBins / 32;
+__device__ __forceinline__ int hslot(uint32_t b) { return (int)(b + (b >> 5)); }
 
 // Order-preserving key of a score: larger score, larger key; -0 and +0 alike.
 __device__ __forceinline__ uint32_t score_key(float f)
@@ -253,6 +240,34 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m)
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Exclusive prefix sums of arr[0 .. n) in place, by one wave (lane l takes a
+// contiguous run of the entries).
+__device__ __forceinline__ void wave_scan_lds(uint32_t *arr, int n)
+{
+    const int lane = threadIdx.x & 63;
+    const int per = (n + 63) >> 6;
+    uint32_t mine = 0;
+    for (int j = 0; j < per; ++j) {
+        const int i = per * lane + j;
+        mine += i < n ? arr[i] : 0u;
+    }
+    uint32_t incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    uint32_t run = incl - mine;
+    for (int j = 0; j < per; ++j) {
+        const int i = per * lane + j;
+        if (i < n) {
+            const uint32_t x = arr[i];
+            arr[i] = run;
+            run += x;
+        }
+    }
+}
+
 // Writes -1 into out[from .. to) (int32 words), the work group together.
 __device__ __forceinline__ void fill_minus1(int32_t *out, int64_t from, int64_t to)
 {
@@ -260,14 +275,29 @@ __device__ __forceinline__ void fill_minus1(int32_t *out, int64_t from, int64_t 
 }
 
 // One work group per query row. Thread (wave w, lane l) holds the rows
-// r0 + 256 m + 64 w + l for m < KPT, so chunk m covers 256 consecutive rows
-// in thread order and ballots give each thread its place in row order.
+// r0 + 256 m + 64 w + l for m < KPT: chunk m covers 256 consecutive rows in
+// thread order, so ballots give each thread its place in row order. A key of
+// 0 marks a row past the visible ones (real keys are at least 1).
+//
+// Selection: with n visible blocks and n > top_k, the keys are rebased to
+// rel = key - (smallest key) + 1 and a radix search runs over rel, 11 bits at
+// a time from the highest bit the row's range needs, so the first histogram
+// already spreads over the row's values. need = how many keys that match the
+// current prefix are still to be taken. The search ends when the bin holding
+// the boundary is taken whole (its count equals need), or when it holds at
+// most kMaxCand keys: those are ranked directly (larger key first, then lower
+// row), which fixes the boundary key and row. When the digits run out, every
+// key of the bin is the same and the first `need` of them in row order are
+// taken. Every case ends as one rule: take key > tau, and of the keys equal
+// to tau those at rows <= tie_row.
 template <int KPT>
 __global__ __launch_bounds__(kTopThreads) void k_select_topk(SelectProblem a)
 {
-    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t hist[2][kHistWords];
     __shared__ uint32_t cnt[KPT * 4];
-    __shared__ uint32_t wsum[4];
+    __shared__ uint32_t red[8];
+    __shared__ uint32_t cand_key[kMaxCand], cand_row[kMaxCand];
+    __shared__ uint32_t ncand;
     __shared__ uint32_t pick[4];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t row = blockIdx.x;
@@ -282,151 +312,203 @@ __global__ __launch_bounds__(kTopThreads) void k_select_topk(SelectProblem a)
         if (ro) fill_minus1(ro, 0, W);
         return;
     }
-    const int64_t n = q.r1 - q.r0;
-    const int nsel = n < k ? (int)n : k;
+    const int n = (int)(q.r1 - q.r0);
+    const int nsel = n < k ? n : k;
     const float *sr = a.scores + row * a.NB;
 
+    // One buffer descriptor over the visible scores; chunk m at a scalar offset.
+    const rsrc_t srs = make_rsrc(sr + q.r0, (uint32_t)n * 4u);
     uint32_t key[KPT];
-    bool valid[KPT];
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
     for (int m = 0; m < KPT; ++m) {
-        const int64_t r = q.r0 + 256 * m + threadIdx.x;
-        valid[m] = r < q.r1;
-        key[m] = valid[m] ? score_key(sr[r]) : 0u;
+        const bool in = (int)threadIdx.x < n - 256 * m;
+        const float f = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(srs, 4 * (int)threadIdx.x, 1024 * m, 0));
+        const uint32_t kv = score_key(f);
+        key[m] = in ? (kv > 1u ? kv : 1u) : 0u;
+        if (in) {
+            kmin = key[m] < kmin ? key[m] : kmin;
+            kmax = key[m] > kmax ? key[m] : kmax;
+        }
     }
 
-    // Radix select of the nsel-th largest key (skipped when every visible
-    // block is kept). need = how many of the keys that match the prefix so far
-    // are still to be taken.
-    bool all = n <= k;      // take every valid key
-    bool ge_only = false;   // take the keys >= prefix
-    uint32_t prefix = 0, pmask = 0;
-    uint32_t need = (uint32_t)k, eq_cnt = 0;
-    if (!all) {
+    uint32_t tau = 0, tie_row = 0;  // with n <= top_k: every key >= 1
+    if (n > k) {
+        uint32_t need = (uint32_t)k;
+        for (int i = threadIdx.x; i < kHistWords; i += kTopThreads) hist[0][i] = 0;
+        if (threadIdx.x == 0) ncand = 0;
+#pragma unroll
+        for (int o = 32; o; o >>= 1) {
+            const uint32_t x = __shfl_xor(kmin, o), y = __shfl_xor(kmax, o);
+            kmin = x < kmin ? x : kmin;
+            kmax = y > kmax ? y : kmax;
+        }
+        if (lane == 0) {
+            red[w] = kmin;
+            red[4 + w] = kmax;
+        }
+        __syncthreads();
+        kmin = red[0];
+        kmax = red[4];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) {
+            kmin = red[i] < kmin ? red[i] : kmin;
+            kmax = red[4 + i] > kmax ? red[4 + i] : kmax;
+        }
+#pragma unroll
+        for (int m = 0; m < KPT; ++m) key[m] = key[m] ? key[m] - kmin + 1u : 0u;
+        const uint32_t range = kmax - kmin + 1u;  // largest rel
+        // Keys in play: (rel >> hi_sh) == prefix; the digit is rel >> sh
+        // (hi_sh - sh <= 11 bits).
+        int sh = range >> 11 ? 32 - __builtin_clz(range) - 11 : 0;
+        int hi_sh = sh + 11;
+        uint32_t prefix = 0;
+        int mode = 0;
 #pragma unroll 1
-        for (int pass = 0; pass < 3; ++pass) {
-            const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
-            const uint32_t nb = pass < 2 ? 2048u : 1024u;
-            for (int i = threadIdx.x; i < (int)nb; i += kTopThreads) hist[i] = 0;
-            __syncthreads();
+        for (int pass = 0;; ++pass) {
+            uint32_t *h = hist[pass & 1];
+            // Clear the other buffer for the next pass (its last reads were
+            // before the previous pass's pick barrier).
+            for (int i = threadIdx.x; i < kHistWords; i += kTopThreads) hist[(pass + 1) & 1][i] = 0;
+            const uint32_t dmask = (1u << (hi_sh - sh)) - 1u;
+            const bool all_in = hi_sh >= 32;
+            // Rows past the visible ones (key 0) stay out; the zero is hidden
+            // from the compiler so that it recomputes this test each pass
+            // instead of keeping a mask per key alive.
+            uint32_t zero_h = 0;
+            asm volatile("" : "+s"(zero_h));
 #pragma unroll
             for (int m = 0; m < KPT; ++m)
-                if (valid[m] && (key[m] & pmask) == prefix)
-                    atomicAdd(&hist[(key[m] >> shift) & (nb - 1)], 1u);
+                if (key[m] > zero_h && (all_in || (key[m] >> hi_sh) == prefix))
+                    atomicAdd(&h[hslot((key[m] >> sh) & dmask)], 1u);
             __syncthreads();
-            // Thread i sums bins [per i, per i + per); the bins of higher threads
-            // hold larger keys.
-            const int per = (int)nb / kTopThreads;
-            uint32_t mine = 0;
-            for (int j = 0; j < per; ++j) mine += hist[per * threadIdx.x + j];
-            uint32_t tot;
-            const uint32_t below = block_scan(mine, wsum, tot);
-            const uint32_t above = tot - below - mine;  // counts in higher threads' bins
-            if (above < need && above + mine >= need) {
-                uint32_t acc = above;
-                for (int j = per - 1; j >= 0; --j) {
-                    const uint32_t h = hist[per * threadIdx.x + j];
-                    if (acc + h >= need) {
-                        pick[0] = (uint32_t)(per * threadIdx.x + j);
-                        pick[1] = acc;
-                        pick[2] = h;
-                        break;
+            if (w == 0) {
+                // Bin of the boundary: lane l sums bins [32 l, 32 l + 32); the
+                // counts of higher lanes' bins come from a suffix scan.
+                uint32_t mine = 0;
+#pragma unroll 8
+                for (int j = 0; j < 32; ++j) mine += h[33 * lane + j];
+                uint32_t incl = mine;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const uint32_t y = __shfl_down(incl, o);
+                    if (lane + o < 64) incl += y;
+                }
+                uint32_t above = incl - mine;
+                if (above < need && incl >= need) {
+                    for (int j = 31; j >= 0; --j) {
+                        const uint32_t x = h[33 * lane + j];
+                        if (above + x >= need) {
+                            pick[0] = (uint32_t)(32 * lane + j);
+                            pick[1] = above;
+                            pick[2] = x;
+                            break;
+                        }
+                        above += x;
                     }
-                    acc += h;
                 }
             }
             __syncthreads();
-            const uint32_t bin = pick[0];
+            const uint32_t cbin = pick[2];
+            prefix = (prefix << (hi_sh - sh)) | pick[0];  // rel >> sh of the bin
             need -= pick[1];
-            eq_cnt = pick[2];
-            prefix |= bin << shift;
-            pmask |= (nb - 1) << shift;
-            __syncthreads();  // pick is rewritten by the next pass
-            if (eq_cnt == need) {
-                ge_only = true;
+            if (cbin == need) {  // the whole bin is taken: rel >= prefix << sh (>= 1)
+                tau = prefix << sh;
+                tie_row = 0xffffffffu;
                 break;
             }
+            if (sh == 0) {  // every key of the bin equals prefix (>= 1)
+                tau = prefix;
+                mode = 3;
+                break;
+            }
+            if (cbin <= (uint32_t)kMaxCand) {
+                // Rank the bin's keys directly: larger key first, then lower row.
+                uint32_t zero_c = 0;  // a second hidden zero: no masks kept from above
+                asm volatile("" : "+s"(zero_c));
+#pragma unroll
+                for (int m = 0; m < KPT; ++m) {
+                    if (key[m] > zero_c && (key[m] >> sh) == prefix) {
+                        const uint32_t slot = atomicAdd(&ncand, 1u);
+                        cand_key[slot] = key[m];
+                        cand_row[slot] = (uint32_t)(256 * m + threadIdx.x);
+                    }
+                }
+                __syncthreads();
+                if (w == 0 && lane < (int)cbin) {
+                    const uint32_t ck = cand_key[lane], cr = cand_row[lane];
+                    uint32_t rank = 0;
+                    for (int j = 0; j < (int)cbin; ++j) {
+                        const uint32_t ok = cand_key[j], orow = cand_row[j];
+                        rank += (ok > ck || (ok == ck && orow < cr)) ? 1u : 0u;
+                    }
+                    if (rank == need - 1) {
+                        pick[0] = ck;
+                        pick[1] = cr;
+                    }
+                }
+                __syncthreads();
+                tau = pick[0];
+                tie_row = pick[1];
+                break;
+            }
+            hi_sh = sh;
+            sh = sh >= 11 ? sh - 11 : 0;
+            __syncthreads();  // pick is rewritten by the next pass
+        }
+        if (mode == 3) {
+            // tie_row: the row of the need-th key equal to tau in row order
+#pragma unroll
+            for (int m = 0; m < KPT; ++m) {
+                const uint64_t e = __ballot(key[m] == tau);
+                if (lane == 0) cnt[4 * m + w] = (uint32_t)__builtin_popcountll(e);
+            }
+            __syncthreads();
+            if (w == 0) wave_scan_lds(cnt, KPT * 4);
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < KPT; ++m) {
+                const bool eq = key[m] == tau;
+                const uint32_t rank = cnt[4 * m + w] + lanes_below(__ballot(eq));
+                if (eq && rank == need - 1) pick[3] = (uint32_t)(256 * m + threadIdx.x);
+            }
+            __syncthreads();
+            tie_row = pick[3];
         }
     }
+    // Row 256 m + tid <= tie_row, compared as (chunk, thread) pairs.
+    const int tie_m = (int)(tie_row >> 8);
+    const bool tid_le = threadIdx.x <= (tie_row & 255u);
+    auto take = [&](int m) {
+        return key[m] > tau || (key[m] == tau && (m < tie_m || (m == tie_m && tid_le)));
+    };
 
-    // Which keys are taken; among keys equal to the final prefix (ties on the
-    // full key) only the first `need` in row order.
-    bool take[KPT];
-    const bool ties = !all && !ge_only;
-    if (ties) {
+    // Output positions in row order.
+    if (nsel > 0) {
 #pragma unroll
         for (int m = 0; m < KPT; ++m) {
-            const uint64_t e = __ballot(valid[m] && key[m] == prefix);
+            const uint64_t e = __ballot(take(m));
             if (lane == 0) cnt[4 * m + w] = (uint32_t)__builtin_popcountll(e);
         }
         __syncthreads();
-        // exclusive scan of cnt[] in (m, wave) order
-        const int per = (KPT * 4 + kTopThreads - 1) / kTopThreads;
-        uint32_t mine = 0;
-        for (int j = 0; j < per; ++j) {
-            const int i = per * threadIdx.x + j;
-            mine += i < KPT * 4 ? cnt[i] : 0u;
-        }
-        uint32_t tot;
-        uint32_t run = block_scan(mine, wsum, tot);
-        for (int j = 0; j < per; ++j) {
-            const int i = per * threadIdx.x + j;
-            if (i < KPT * 4) {
-                const uint32_t x = cnt[i];
-                cnt[i] = run;
-                run += x;
-            }
-        }
+        if (w == 0) wave_scan_lds(cnt, KPT * 4);
         __syncthreads();
+        // Recompute the rule rather than keep KPT ballot masks across the scan.
+        asm volatile("" : "+v"(tau));
 #pragma unroll
         for (int m = 0; m < KPT; ++m) {
-            const bool eq = valid[m] && key[m] == prefix;
-            const uint64_t e = __ballot(eq);
-            const uint32_t rank = cnt[4 * m + w] + lanes_below(e);
-            take[m] = valid[m] && (key[m] > prefix || (eq && rank < need));
-        }
-        __syncthreads();  // cnt is reused below
-    } else {
-#pragma unroll
-        for (int m = 0; m < KPT; ++m) take[m] = valid[m] && (all || key[m] >= prefix);
-    }
-
-    // Output positions in row order.
-#pragma unroll
-    for (int m = 0; m < KPT; ++m) {
-        const uint64_t e = __ballot(take[m]);
-        if (lane == 0) cnt[4 * m + w] = (uint32_t)__builtin_popcountll(e);
-    }
-    __syncthreads();
-    {
-        const int per = (KPT * 4 + kTopThreads - 1) / kTopThreads;
-        uint32_t mine = 0;
-        for (int j = 0; j < per; ++j) {
-            const int i = per * threadIdx.x + j;
-            mine += i < KPT * 4 ? cnt[i] : 0u;
-        }
-        uint32_t tot;
-        uint32_t run = block_scan(mine, wsum, tot);
-        for (int j = 0; j < per; ++j) {
-            const int i = per * threadIdx.x + j;
-            if (i < KPT * 4) {
-                const uint32_t x = cnt[i];
-                cnt[i] = run;
-                run += x;
-            }
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < KPT; ++m) {
-        const uint64_t e = __ballot(take[m]);
-        if (take[m]) {
-            const uint32_t pos = cnt[4 * m + w] + lanes_below(e);
-            const int64_t j = q.r0 + 256 * m + threadIdx.x - q.base;
-            if (bo) bo[pos] = (int32_t)j;
-            if (ro) {
-                const int32_t id = (int32_t)(q.s + 4 * j);
-                *reinterpret_cast<int4 *>(ro + 4 * (int64_t)pos) = make_int4(id, id + 1, id + 2, id + 3);
+            const bool tk = take(m);
+            const uint64_t e = __ballot(tk);
+            if (tk) {
+                const uint32_t pos = cnt[4 * m + w] + lanes_below(e);
+                const int64_t j = q.r0 + 256 * m + threadIdx.x - q.base;
+                if (bo) bo[pos] = (int32_t)j;
+                if (ro) {
+                    const int32_t id = (int32_t)(q.s + 4 * j);
+                    *reinterpret_cast<int4 *>(ro + 4 * (int64_t)pos) =
+                        make_int4(id, id + 1, id + 2, id + 3);
+                }
             }
         }
     }
