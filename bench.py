@@ -139,7 +139,12 @@ TRAFFIC_SOURCES = ("token_indexed_sparse_amd/csrc/common.h", "token_indexed_spar
                    "token_indexed_sparse_amd/csrc/fwd.hip", "token_indexed_sparse_amd/csrc/dense.hip")
 
 
-def measured_traffic(workload: str, kernel: str):
+# Sources of the selector's kernels, for the same check on its summary.
+SELECT_SOURCES = ("token_indexed_sparse_amd/csrc/common.h",
+                  "token_indexed_sparse_amd/csrc/select.hip")
+
+
+def measured_traffic(workload: str, kernel: str, sources=TRAFFIC_SOURCES):
     """HBM bytes per launch of `kernel` (calibrated FETCH_SIZE + WRITE_SIZE) from the
     committed rocprofv3 summary, or None if there is none or the kernels changed since."""
     import hashlib
@@ -147,7 +152,7 @@ def measured_traffic(workload: str, kernel: str):
     if not os.path.exists(path):
         return None
     h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     sha, rows = None, {}
@@ -371,16 +376,19 @@ def select_step(torch, qsa, lib, hip, stream, T: int, top_k: int, steps: int = 5
     score_bytes = T * H * D * 2 + NB * D * 2 + 4 * pairs
     topk_bytes = 4 * pairs + 4 * T * top_k + 4 * T * (4 * top_k + 4)
     topk_gbs = topk_bytes / (topk_ms * 1e-3) / 1e9
-    return {"workload": f"select_t{T}_nb{NB}_h{H}_d{D}_top{top_k}", "T": T, "NB": NB,
+    name = f"select_t{T}_nb{NB}_h{H}_d{D}_top{top_k}"
+    tr_s = measured_traffic(name, "select_scores", SELECT_SOURCES)
+    tr_k = measured_traffic(name, "select_topk", SELECT_SOURCES)
+    return {"workload": name, "T": T, "NB": NB,
             "H": H, "D": D, "top_k": top_k, "visible_pairs": pairs,
             "ms": score_ms + topk_ms, "steps": steps,
             "scores": {"avg_launch_ms": score_ms, "bound": "mfma", "achieved": tflops,
                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                        "frac": tflops / PEAK_BF16_TFLOPS, "flop_per_launch": flop,
-                       "algorithmic_bytes": score_bytes},
+                       "algorithmic_bytes": score_bytes, "traffic": tr_s},
             "topk": {"avg_launch_ms": topk_ms, "bound": "hbm", "achieved": topk_gbs,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": topk_gbs / PEAK_HBM_GBS,
-                     "algorithmic_bytes": topk_bytes},
+                     "algorithmic_bytes": topk_bytes, "traffic": tr_k},
             "note": "median of the timed calls (HIP events), after one warm-up; workspace "
                     "holds the scores between the two kernels",
             "_routes": routes}
