@@ -194,6 +194,44 @@ int main()
     EXPECT(qsa_block_plan_bytes(&bbad), 0);
 
     // status strings, in and out of range
+    // block selector
+    qsa_select_dims sd;
+    std::memset(&sd, 0, sizeof(sd));
+    sd.B = 2;
+    sd.Sq = 300;
+    sd.NB = 80;
+    sd.H = 64;
+    sd.D = 128;
+    sd.top_k = 16;
+    const size_t sw = qsa_select_workspace_bytes(&sd);
+    EXPECT(sw == size_t(2) * 300 * 80 * 4, 1);
+    EXPECT(qsa_select(&sd, a, a, nullptr, nullptr, 0.5f, ai, ai, nullptr, a, sw, nullptr),
+           QSA_ERR_DEVICE);
+    EXPECT(qsa_select(&sd, a, a, ai, ai, 0.5f, nullptr, nullptr, af, nullptr, 0, nullptr),
+           QSA_ERR_DEVICE);
+    EXPECT(qsa_select(&sd, a, a, nullptr, nullptr, 0.5f, ai, ai, nullptr, a, sw - 1, nullptr),
+           QSA_ERR_WORKSPACE);
+    EXPECT(qsa_select(&sd, a, a, nullptr, nullptr, NAN, ai, ai, nullptr, a, sw, nullptr),
+           QSA_ERR_SCALE);
+    EXPECT(qsa_select(&sd, a, a, nullptr, nullptr, 0.5f, nullptr, nullptr, nullptr, a, sw, nullptr),
+           QSA_ERR_NULL);
+    EXPECT(qsa_select(nullptr, a, a, nullptr, nullptr, 0.5f, ai, ai, nullptr, a, sw, nullptr),
+           QSA_ERR_NULL);
+    // extreme but valid: B * Sq just below 2^31, the largest NB; the workspace
+    // size is then 2^31 * 32768 * 4 bytes, no overflow
+    sd.B = 1;
+    sd.Sq = INT32_MAX;
+    sd.NB = 32768;
+    sd.top_k = 4096;
+    EXPECT(qsa_select_workspace_bytes(&sd) == size_t(INT32_MAX) * 32768 * 4, 1);
+    sd.q_offset = 1;  // q_offset + Sq beyond 2^31 - 1
+    EXPECT(qsa_select_workspace_bytes(&sd), 0);
+    sd.q_offset = 0;
+    sd.Sq = INT64_MAX;
+    EXPECT(qsa_select_workspace_bytes(&sd), 0);
+    EXPECT(qsa_select(&sd, a, a, nullptr, nullptr, 0.5f, ai, ai, nullptr, a, sw, nullptr),
+           QSA_ERR_SHAPE);
+
     for (int s = -3; s < 20; ++s) EXPECT(qsa_status_string(static_cast<qsa_status>(s)) != nullptr, 1);
     EXPECT(qsa_version() >> 16, 1);
 

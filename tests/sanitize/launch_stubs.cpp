@@ -20,4 +20,7 @@ hipError_t launch_delta(const Problem &, hipStream_t) { return hipErrorLaunchFai
 hipError_t launch_dq(const Problem &, hipStream_t) { return hipErrorLaunchFailure; }
 hipError_t launch_dkdv(const Problem &, hipStream_t) { return hipErrorLaunchFailure; }
 hipError_t launch_dkdv_reduce(const Problem &, hipStream_t) { return hipErrorLaunchFailure; }
+hipError_t launch_select_fill(const SelectProblem &, hipStream_t) { return hipErrorLaunchFailure; }
+hipError_t launch_select_scores(const SelectProblem &, hipStream_t) { return hipErrorLaunchFailure; }
+hipError_t launch_select_topk(const SelectProblem &, hipStream_t) { return hipErrorLaunchFailure; }
 }  // namespace qsa
