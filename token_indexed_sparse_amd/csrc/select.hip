@@ -484,7 +484,10 @@ __global__ __launch_bounds__(kTopThreads) void k_select_topk(SelectProblem a)
         return key[m] > tau || (key[m] == tau && (m < tie_m || (m == tie_m && tid_le)));
     };
 
-    // Output positions in row order.
+    // Output positions in row order. The kept block numbers are compacted
+    // into LDS (the histogram space, free by now: top_k <= 4096 words), then
+    // the block list and the route rows leave in coalesced stores.
+    int32_t *sel = reinterpret_cast<int32_t *>(&hist[0][0]);
     if (nsel > 0) {
 #pragma unroll
         for (int m = 0; m < KPT; ++m) {
@@ -500,25 +503,31 @@ __global__ __launch_bounds__(kTopThreads) void k_select_topk(SelectProblem a)
         for (int m = 0; m < KPT; ++m) {
             const bool tk = take(m);
             const uint64_t e = __ballot(tk);
-            if (tk) {
-                const uint32_t pos = cnt[4 * m + w] + lanes_below(e);
-                const int64_t j = q.r0 + 256 * m + threadIdx.x - q.base;
-                if (bo) bo[pos] = (int32_t)j;
-                if (ro) {
-                    const int32_t id = (int32_t)(q.s + 4 * j);
-                    *reinterpret_cast<int4 *>(ro + 4 * (int64_t)pos) =
-                        make_int4(id, id + 1, id + 2, id + 3);
-                }
-            }
+            if (tk)
+                sel[cnt[4 * m + w] + lanes_below(e)] =
+                    (int32_t)(q.r0 + 256 * m + threadIdx.x - q.base);
         }
+        __syncthreads();
     }
-    if (bo) fill_minus1(bo, nsel, k);
+    if (bo)
+        for (int i = threadIdx.x; i < k; i += kTopThreads) bo[i] = i < nsel ? sel[i] : -1;
     if (ro) {
-        fill_minus1(ro, 4 * (int64_t)nsel, 4 * (int64_t)k);
-        if (threadIdx.x < 4) {
-            const int64_t p = a.q_offset + t;
-            const int64_t id = q.s + 4 * q.c + threadIdx.x;
-            ro[4 * (int64_t)k + threadIdx.x] = id <= p ? (int32_t)id : -1;
+        // route row: slot group g < nsel holds block sel[g], then -1 groups,
+        // and group k the query's own incomplete block
+        int4 *r4 = reinterpret_cast<int4 *>(ro);
+        const int64_t p = a.q_offset + t;
+        for (int g = threadIdx.x; g <= k; g += kTopThreads) {
+            int4 v = make_int4(-1, -1, -1, -1);
+            if (g < nsel) {
+                const int32_t id = (int32_t)(q.s + 4 * (int64_t)sel[g]);
+                v = make_int4(id, id + 1, id + 2, id + 3);
+            } else if (g == k) {
+                const int64_t id = q.s + 4 * q.c;
+                v = make_int4((int32_t)id, id + 1 <= p ? (int32_t)(id + 1) : -1,
+                              id + 2 <= p ? (int32_t)(id + 2) : -1,
+                              id + 3 <= p ? (int32_t)(id + 3) : -1);
+            }
+            r4[g] = v;
         }
     }
 }
