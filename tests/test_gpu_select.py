@@ -108,6 +108,10 @@ INT_CASES = [
     dict(name="h1", seed=105, B=3, Sq=130, NB=40, H=1, k=3, q_offset=7),
     dict(name="nb8192", seed=106, B=1, Sq=48, NB=8192, H=16, k=512, q_offset=32768 - 48),
     dict(name="nb32768", seed=107, B=1, Sq=8, NB=32768, H=16, k=300, q_offset=4 * 32768 - 8),
+    # rows of 2049..4096 and 8193..16384 blocks (16 and 64 keys per thread)
+    dict(name="nb3000", seed=108, B=1, Sq=16, NB=3000, H=16, k=100, q_offset=4 * 3000 - 16),
+    dict(name="nb12000", seed=109, B=1, Sq=12, NB=12000, H=16, k=1000, q_offset=4 * 12000 - 12),
+    dict(name="top1", seed=110, B=2, Sq=90, NB=30, H=32, k=1, q_offset=0),
 ]
 
 
@@ -135,6 +139,25 @@ def test_integer_inputs_bit_exact(case):
     assert any(len(np.unique(r[np.isfinite(r)])) < np.isfinite(r).sum() for r in ref[0])
     bo2, ro2, _ = _run(q, kb, k, 0.5, off, start, base, scores=False)
     assert np.array_equal(bo2, bo) and np.array_equal(ro2, ro)
+
+
+@pytest.mark.timeout(600)
+def test_all_scores_equal_lower_blocks_win():
+    """Zero compressed keys: every visible block scores 0, so each row's selection
+    is decided by the tie rule alone (its first top_k blocks), with far more
+    equal keys than the direct ranking takes."""
+    rng = np.random.default_rng(115)
+    Sq, NB, k = 24, 8192, 512
+    off = 4 * NB - Sq
+    q = _normal(rng, (1, Sq, 64, D))
+    kb = np.zeros((1, NB, D), np.uint16)
+    bo, ro, so = _run(q, kb, k, 1.0 / np.sqrt(D), off)
+    c = np.minimum((off + np.arange(Sq)) // 4, NB)
+    vis = np.arange(NB)[None, :] < c[:, None]
+    assert (so[0][vis] == 0).all() and np.isneginf(so[0][~vis]).all()
+    want = np.where(np.arange(k)[None, :] < np.minimum(c, k)[:, None], np.arange(k)[None, :], -1)
+    assert np.array_equal(bo[0], want)
+    assert np.array_equal(ro, _expand(bo, None, off))
 
 
 def _bound(q, kb, ref, scale, H):
