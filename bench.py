@@ -217,16 +217,23 @@ def cpu_baseline(inp, wl, nnz_row: np.ndarray, seconds: float) -> dict:
     threads = oracle.num_threads()
     rng = np.random.default_rng(0)
     rows_all = np.nonzero(nnz_row > 0)[0]
-    # calibrate on one row per thread, then size the sample to the time budget
-    probe = np.sort(rng.choice(rows_all, min(threads, len(rows_all)), replace=False))
-    t = time.perf_counter()
-    P.backward_rows(probe)
-    per_round = time.perf_counter() - t
-    n = int(max(threads, min(len(rows_all), threads * seconds / max(per_round, 1e-9))))
-    rows = np.sort(rng.choice(rows_all, n, replace=False))
-    t = time.perf_counter()
-    P.backward_rows(rows)
-    dt = time.perf_counter() - t
+
+    def timed(count):
+        rows = np.sort(rng.choice(rows_all, count, replace=False))
+        t = time.perf_counter()
+        P.backward_rows(rows)
+        return rows, time.perf_counter() - t
+
+    # Calibrate on four rows per thread, size the sample to the time budget, and
+    # if that sample still ran under half the budget (a first call pays thread
+    # start-up), size it again from its own time.
+    n = min(4 * threads, len(rows_all))
+    rows, dt = timed(n)
+    for _ in range(2):
+        if dt >= 0.5 * seconds or n >= len(rows_all):
+            break
+        n = int(max(threads, min(len(rows_all), n * seconds / max(dt, 1e-9))))
+        rows, dt = timed(n)
     flop = (COUNTED_FWD + COUNTED_BWD) * wl.Hq * float(nnz_row[rows].sum())
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"forward + full backward (dq and the rows' dk/dv contributions) of {n} "
