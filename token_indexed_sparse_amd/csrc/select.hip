@@ -373,6 +373,7 @@ __global__ __launch_bounds__(kTopThreads) void k_select_topk(SelectProblem a)
             for (int i = threadIdx.x; i < kHistWords; i += kTopThreads) hist[(pass + 1) & 1][i] = 0;
             const uint32_t dmask = (1u << (hi_sh - sh)) - 1u;
             const bool all_in = hi_sh >= 32;
+            const int hs = all_in ? 31 : hi_sh;  // no shift by 32 (all_in decides then)
             // Rows past the visible ones (key 0) stay out; the zero is hidden
             // from the compiler so that it recomputes this test each pass
             // instead of keeping a mask per key alive.
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(kTopThreads) void k_select_topk(SelectProblem a)
             asm volatile("" : "+s"(zero_h));
 #pragma unroll
             for (int m = 0; m < KPT; ++m)
-                if (key[m] > zero_h && (all_in || (key[m] >> hi_sh) == prefix))
+                if (key[m] > zero_h && (all_in || (key[m] >> hs) == prefix))
                     atomicAdd(&h[hslot((key[m] >> sh) & dmask)], 1u);
             __syncthreads();
             if (w == 0) {
