@@ -85,19 +85,28 @@ def _check_format(bo, ro, start, q_offset, n_vis, top_k):
     assert np.array_equal(ro, _expand(bo, start, q_offset)), "route rows"
 
 
-def _docs_meta(rng, Sq, NB_slack=0):
-    """Packed documents over Sq tokens: per-token start and kbar row base (the
-    documents' complete blocks laid end to end), some padding tokens."""
-    cuts = np.sort(rng.choice(np.arange(1, Sq), 4, replace=False))
-    starts = np.concatenate([[0], cuts])
-    ends = np.concatenate([cuts, [Sq]])
-    nblk = (ends - starts) // 4
-    bases = np.concatenate([[0], np.cumsum(nblk)[:-1]])
-    doc = np.searchsorted(starts, np.arange(Sq), side="right") - 1
-    start = starts[doc].astype(np.int32)[None]
-    base = bases[doc].astype(np.int32)[None]
-    start[0, rng.choice(Sq, 10, replace=False)] = -1        # padding queries
-    return start, base, int(nblk.sum()) - NB_slack
+def _docs_meta(rng, Sq, NB_slack=0, B=1, T=None, q_offset=0):
+    """Packed documents over T tokens (default Sq) in each of B batch rows: for the
+    queries at positions q_offset .. q_offset + Sq - 1, their document start and
+    kbar row base (each row's documents' complete blocks laid end to end), ten
+    padding queries per row. Returns (start, base, NB) with NB the largest row's
+    block count minus NB_slack."""
+    T = Sq if T is None else T
+    start = np.zeros((B, Sq), np.int32)
+    base = np.zeros((B, Sq), np.int32)
+    nb_max = 0
+    for b in range(B):
+        cuts = np.sort(rng.choice(np.arange(1, T), 4, replace=False))
+        starts = np.concatenate([[0], cuts])
+        ends = np.concatenate([cuts, [T]])
+        nblk = (ends - starts) // 4
+        bases = np.concatenate([[0], np.cumsum(nblk)[:-1]])
+        doc = np.searchsorted(starts, q_offset + np.arange(Sq), side="right") - 1
+        start[b] = starts[doc]
+        base[b] = bases[doc]
+        start[b, rng.choice(Sq, 10, replace=False)] = -1     # padding queries
+        nb_max = max(nb_max, int(nblk.sum()))
+    return start, base, nb_max - NB_slack
 
 
 INT_CASES = [
@@ -112,6 +121,10 @@ INT_CASES = [
     dict(name="nb3000", seed=108, B=1, Sq=16, NB=3000, H=16, k=100, q_offset=4 * 3000 - 16),
     dict(name="nb12000", seed=109, B=1, Sq=12, NB=12000, H=16, k=1000, q_offset=4 * 12000 - 12),
     dict(name="top1", seed=110, B=2, Sq=90, NB=30, H=32, k=1, q_offset=0),
+    # documents in two batch rows, and a query shard (positions 500..699) of
+    # packed documents over 700 tokens
+    dict(name="docs_b2", seed=116, B=2, Sq=400, NB=None, H=32, k=12, q_offset=0),
+    dict(name="docs_shard", seed=117, B=1, Sq=200, NB=None, H=64, k=24, q_offset=500, T=700),
 ]
 
 
@@ -123,8 +136,9 @@ def test_integer_inputs_bit_exact(case):
     B, Sq, H, k, off = case["B"], case["Sq"], case["H"], case["k"], case["q_offset"]
     start = base = None
     NB = case["NB"]
-    if case["name"] == "docs":
-        start, base, NB = _docs_meta(rng, Sq, NB_slack=3)     # last rows past kbar's end
+    if case["name"].startswith("docs"):
+        # the last rows of the largest batch row fall past kbar's end
+        start, base, NB = _docs_meta(rng, Sq, NB_slack=3, B=B, T=case.get("T"), q_offset=off)
     q = _ints(rng, (B, Sq, H, D))
     kb = _ints(rng, (B, NB, D))
     bo, ro, so = _run(q, kb, k, 0.5, off, start, base)
