@@ -47,11 +47,19 @@
  *    device: every count stays on the device ("fa4_qsa" page, `_block_kinds`).
  *  - Ownership: the caller allocates every output and the workspace, whose
  *    size the matching *_workspace_bytes call returns. The library keeps no
- *    state between calls and writes every output element, so outputs need no
- *    clearing. Outputs must not overlap inputs or each other.
+ *    data between calls (only per-device resources: cached device properties
+ *    and the backward's second stream and its two events) and writes every
+ *    output element, so outputs need no clearing. Outputs must not overlap inputs or each other.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and
  *    the call returns without waiting for it. Calls that share a workspace
- *    must be ordered on one stream.
+ *    must be ordered on one stream. The backward calls run their dQ passes
+ *    on a second stream of the library (one per device, default priority,
+ *    created on the first backward call and kept until the process ends),
+ *    forked from `stream` after the call's earlier work with an event and
+ *    joined back into `stream` before its last kernel: work enqueued on
+ *    `stream` after the call sees all its outputs, as if it had run on
+ *    `stream` alone. The fork and join of one call are enqueued under a
+ *    per-device lock, so calls from several host threads stay paired.
  *  - Errors: validation happens on the host before any launch and returns a
  *    status without touching the device; QSA_ERR_LAUNCH reports a failed
  *    launch. The error classes follow the "cudnn_qsa" page

@@ -64,7 +64,7 @@ qsa_status check_dims(const qsa_dims *d)
 
 struct Layout {
     size_t memb, has, mbits, row_keys, row_cnt, pkeys, pcnt, tile_cnt, kinds, fpc, fpi, ffc, ffi,
-        rpc, rpi, rfc, rfi, fstate, delta, kv_part, kv_flag, walk, total;
+        rpc, rpi, rfc, rfi, fstate, delta, kv_part, dq_part, kv_flag, walk, total;
 };
 
 // Parts of a workspace. The route plan: key lists and tile counts (core),
@@ -129,11 +129,12 @@ Layout layout(const qsa_dims *d, unsigned parts)
     L.delta = take(parts & kBwd, (size_t)(d->B * d->Hq * d->Sq) * 4);
     const int64_t seg = seg_tiles_for(d);
     const int64_t nseg = (nQT + seg - 1) / seg;
-    // The dK/dV partial sums and the dQ hand-over are never live together
-    // (dQ finishes before dK/dV starts), so they share one region.
+    // The dK/dV partial sums and the dQ hand-over each have a region: the
+    // backward runs its dQ passes beside the dK/dV passes.
     const size_t kv_bytes = (size_t)(d->B * d->Hkv * (nseg + 1) * stride) * 2 * kD * 4;
     const size_t dq_bytes = (size_t)(rows * d->Hq) * kD * 4;
-    L.kv_part = take(parts & kBwd, kv_bytes > dq_bytes ? kv_bytes : dq_bytes);
+    L.kv_part = take(parts & kBwd, kv_bytes);
+    L.dq_part = take(parts & kBwd, dq_bytes);
     L.kv_flag = take(parts & kBwd, (size_t)(d->B * d->Hkv * (nseg + 1) * (stride / 16)));
     L.walk = take(parts & kWalk, 16 * 4);
     L.memb = L.has = none;
@@ -166,6 +167,33 @@ const DeviceInfo *device_info(int &dev)
         info.ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 && info.cus > 0;
     });
     return &g_dev[dev];
+}
+
+// A second stream per device for the backward's dQ passes, which run beside
+// its dK/dV passes: the two share only read-only inputs, delta and the plan.
+// Created on first use with the default priority and kept until the process
+// ends; the mutex makes each call's fork and join one unit, so calls from
+// several host threads cannot pair their events with another call's.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    bool ok = false;
+    std::mutex m;
+};
+SideStream g_side[kMaxDevices];
+std::once_flag g_side_once[kMaxDevices];
+
+SideStream *side_stream()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::call_once(g_side_once[dev], [dev]() {
+        SideStream &x = g_side[dev];
+        x.ok = hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) == hipSuccess &&
+               hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) == hipSuccess &&
+               hipEventCreateWithFlags(&x.join, hipEventDisableTiming) == hipSuccess;
+    });
+    return g_side[dev].ok ? &g_side[dev] : nullptr;
 }
 
 qsa_status check_device(const qsa_dims *d)
@@ -239,10 +267,8 @@ void carve(Problem &p, const Layout &L, void *ws)
     }
     if (L.fstate != none) p.fstate = reinterpret_cast<float *>(w + L.fstate);
     if (L.delta != none) p.delta = reinterpret_cast<float *>(w + L.delta);
-    if (L.kv_part != none) {
-        p.kv_part = reinterpret_cast<float *>(w + L.kv_part);
-        p.dq_part = p.kv_part;
-    }
+    if (L.kv_part != none) p.kv_part = reinterpret_cast<float *>(w + L.kv_part);
+    if (L.dq_part != none) p.dq_part = reinterpret_cast<float *>(w + L.dq_part);
     if (L.kv_flag != none) p.kv_flag = reinterpret_cast<uint8_t *>(w + L.kv_flag);
     // Deterministic calls walk every key list from its start (no walk
     // clocks), and so do calls with fewer than eight rows per wave slot: their
@@ -486,6 +512,25 @@ qsa_status run_backward(Problem &p, const void *grad_out, const void *q, const v
     }
     if (mark(events, 1, s) != hipSuccess) return QSA_ERR_DEVICE;
     if (launch_delta(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+    // Without stage events the dQ passes run on the side stream, forked after
+    // delta and joined before the reduce, beside the dK/dV passes (dK/dV
+    // launched first: its items are the long ones). With stage events the
+    // passes run one after the other, so that each stage has its own time.
+    SideStream *x = events ? nullptr : side_stream();
+    if (x) {
+        std::lock_guard<std::mutex> lock(x->m);
+        if (hipEventRecord(x->fork, s) != hipSuccess ||
+            hipStreamWaitEvent(x->s, x->fork, 0) != hipSuccess)
+            return QSA_ERR_DEVICE;
+        if (launch_dkdv(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+        if (launch_dq(p, x->s) != hipSuccess) return QSA_ERR_LAUNCH;
+        if (launch_dq_dense(p, x->s) != hipSuccess) return QSA_ERR_LAUNCH;
+        if (hipEventRecord(x->join, x->s) != hipSuccess) return QSA_ERR_DEVICE;
+        if (launch_dkdv_dense(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+        if (hipStreamWaitEvent(s, x->join, 0) != hipSuccess) return QSA_ERR_DEVICE;
+        if (launch_dkdv_reduce(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+        return QSA_OK;
+    }
     if (mark(events, 2, s) != hipSuccess) return QSA_ERR_DEVICE;
     if (launch_dq(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
     if (mark(events, 3, s) != hipSuccess) return QSA_ERR_DEVICE;
