@@ -12,9 +12,12 @@
 //    one head's dot with one block; relu and the head sum happen in registers,
 //    then a reduce-scatter over the four lane quads leaves one score per lane.
 //  * k_select_topk, one work group per query row: the row's scores become
-//    order-preserving 32-bit keys held in registers, a three-pass radix select
-//    (11, 11 and 10 bits, histograms in LDS) finds the top_k-th key, and
-//    ballots place the chosen blocks in ascending order in the outputs.
+//    order-preserving 32-bit keys held in registers; a radix search over the
+//    keys relative to the row's smallest (11 bits a step from the highest bit
+//    the row's range needs, histograms in LDS) narrows the top_k-th key to one
+//    bin, whose keys are ranked directly when there are few; ballots place
+//    the chosen blocks in ascending order, and the block list and route rows
+//    leave in coalesced stores.
 #include "common.h"
 
 namespace qsa {
@@ -23,7 +26,7 @@ namespace {
 constexpr int kSelRow = kSelD * 2;                    // bytes per indexer row (bf16)
 constexpr int kSelWaves = 8;                          // waves per scoring work group
 constexpr int kSelTileRows = 128;                     // kbar rows per staged tile
-constexpr int kSelTileBytes = kSelTileRows * kSelRow;  // 32 KB, staged twice over
+constexpr int kSelTileBytes = kSelTileRows * kSelRow;  // 32 KB per buffer, two buffers
 
 // Position data of query t of batch row b: its document start s, the kbar row
 // base of its document and the visible kbar rows [r0, r1). A query whose
