@@ -24,7 +24,7 @@ namespace qsa {
 namespace {
 
 constexpr int kSelRow = kSelD * 2;                    // bytes per indexer row (bf16)
-constexpr int kSelWaves = 8;                          // waves per scoring work group
+constexpr int kSelWaves = 4;                          // waves per scoring work group
 constexpr int kSelTileRows = 128;                     // kbar rows per staged tile
 constexpr int kSelTileBytes = kSelTileRows * kSelRow;  // 32 KB per buffer, two buffers
 
@@ -138,8 +138,8 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select_scores(SelectProblem 
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char *)tiles;
     auto stage = [&](int64_t row0, int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ins = 4 * wave + i;  // 32 loads of 4 rows each
+        for (int i = 0; i < 32 / kSelWaves; ++i) {
+            const int ins = (32 / kSelWaves) * wave + i;  // 32 loads of 4 rows each
             const int rr = 4 * ins + (lane >> 4);
             const uint32_t off = (uint32_t)(row0 + rr) * kSelRow +
                                  (uint32_t)(((lane & 15) ^ (rr & 15)) << 4);
