@@ -513,20 +513,23 @@ qsa_status run_backward(Problem &p, const void *grad_out, const void *q, const v
     if (mark(events, 1, s) != hipSuccess) return QSA_ERR_DEVICE;
     if (launch_delta(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
     // Without stage events the dQ passes run on the side stream, forked after
-    // delta and joined before the reduce, beside the dK/dV passes (dK/dV
-    // launched first: its items are the long ones). With stage events the
-    // passes run one after the other, so that each stage has its own time.
+    // delta and joined before the reduce, beside the dK/dV passes. The dense
+    // dK/dV pass goes first, so that each stream's gathered pass meets the
+    // other's dense (matrix-core-bound) pass: the gathered dQ beside the dense
+    // dK/dV, then the dense dQ beside the gathered dK/dV (measured 0.35 ms
+    // faster per 32k step than the gathered dK/dV first). With stage events
+    // the passes run one after the other, so that each has its own time.
     SideStream *x = events ? nullptr : side_stream();
     if (x) {
         std::lock_guard<std::mutex> lock(x->m);
         if (hipEventRecord(x->fork, s) != hipSuccess ||
             hipStreamWaitEvent(x->s, x->fork, 0) != hipSuccess)
             return QSA_ERR_DEVICE;
-        if (launch_dkdv(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+        if (launch_dkdv_dense(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
         if (launch_dq(p, x->s) != hipSuccess) return QSA_ERR_LAUNCH;
         if (launch_dq_dense(p, x->s) != hipSuccess) return QSA_ERR_LAUNCH;
         if (hipEventRecord(x->join, x->s) != hipSuccess) return QSA_ERR_DEVICE;
-        if (launch_dkdv_dense(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
+        if (launch_dkdv(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
         if (hipStreamWaitEvent(s, x->join, 0) != hipSuccess) return QSA_ERR_DEVICE;
         if (launch_dkdv_reduce(p, s) != hipSuccess) return QSA_ERR_LAUNCH;
         return QSA_OK;
