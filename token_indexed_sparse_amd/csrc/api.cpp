@@ -64,7 +64,7 @@ qsa_status check_dims(const qsa_dims *d)
 
 struct Layout {
     size_t memb, has, mbits, row_keys, row_cnt, pkeys, pcnt, tile_cnt, kinds, fpc, fpi, ffc, ffi,
-        rpc, rpi, rfc, rfi, fstate, delta, kv_part, dq_part, kv_flag, walk, total;
+        rpc, rpi, rfc, rfi, fstate, delta, kv_part, dq_part, kv_flag, kv_split, walk, total;
 };
 
 // Parts of a workspace. The route plan: key lists and tile counts (core),
@@ -136,6 +136,8 @@ Layout layout(const qsa_dims *d, unsigned parts)
     L.kv_part = take(parts & kBwd, kv_bytes);
     L.dq_part = take(parts & kBwd, dq_bytes);
     L.kv_flag = take(parts & kBwd, (size_t)(d->B * d->Hkv * (nseg + 1) * (stride / 16)));
+    const int64_t merge = seg < kMergeTiles ? kMergeTiles / seg : 1;
+    L.kv_split = take(parts & kBwd, (size_t)(d->B * d->Hkv * ((nseg + merge - 1) / merge) * (stride / 16)));
     L.walk = take(parts & kWalk, 16 * 4);
     L.memb = L.has = none;
     L.total = off;
@@ -234,6 +236,7 @@ void fill_common(Problem &p, const qsa_dims *d, const void *routes, float scale)
     p.seg_tiles = seg_tiles_for(d);
     p.nseg = (p.nQT + p.seg_tiles - 1) / p.seg_tiles;
     p.nslot = p.nseg + 1;
+    p.merge = p.seg_tiles < kMergeTiles ? kMergeTiles / p.seg_tiles : 1;
     p.scale = scale;
     p.routes = routes;
 }
@@ -270,6 +273,7 @@ void carve(Problem &p, const Layout &L, void *ws)
     if (L.kv_part != none) p.kv_part = reinterpret_cast<float *>(w + L.kv_part);
     if (L.dq_part != none) p.dq_part = reinterpret_cast<float *>(w + L.dq_part);
     if (L.kv_flag != none) p.kv_flag = reinterpret_cast<uint8_t *>(w + L.kv_flag);
+    if (L.kv_split != none) p.kv_split = reinterpret_cast<uint8_t *>(w + L.kv_split);
     // Deterministic calls walk every key list from its start (no walk
     // clocks), and so do calls with fewer than eight rows per wave slot: their
     // rows run in a few nearly simultaneous rounds, already in step, and the

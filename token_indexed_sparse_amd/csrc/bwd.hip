@@ -19,8 +19,15 @@
 //    low bf16 parts of dS go through one 16x16x32 MFMA whose K = 32 covers
 //    the 16 key slots twice, as the forward does with P.
 //  * k_dkdv: key-major. One wave owns 16 consecutive keys of one KV head and
-//    one segment of query tiles (8 by default, more when the partial sums
-//    would not fit the workspace budget), keeps the 16 K and V rows in registers and
+//    one segment of query tiles (2 by default, more when the partial sums
+//    would not fit the workspace budget). Segments are grouped 8 tiles at a
+//    time: k_dkdv_split counts, per group and 16-key group, the rows that
+//    select one of the keys, and a group with at most 256 such rows is one
+//    work item (its first segment's; the others exit), while a heavier group
+//    runs each segment as its own item. Light groups thus keep few partial
+//    sums, and the heavy groups of rows near the start of a document (which
+//    select every earlier block) no longer leave one wave with a thousand
+//    rows. The wave keeps the 16 K and V rows in registers and
 //    their dK, dV accumulators for the whole item. It walks the partial
 //    entries of the reverse tile list of its 128-key tile column inside the
 //    segment from the last query tile down (full tiles are summed by the dense
@@ -299,13 +306,12 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
     // the dense pass).
     const int64_t t = key0 >> 7;
     const int64_t bt = b * p.nKT + t;
-    const int32_t t_lo = (int32_t)(seg * p.seg_tiles);
-    const int32_t t_hi = (int32_t)((seg + 1) * p.seg_tiles);
     const int32_t *idx_p = p.rev_p_idx + bt * p.nQT;
-    // Entries of an ascending list below t_lo and below t_hi, counted by the
+    // Entries of an ascending list below lo and below hi, counted by the
     // whole wave at once: one memory latency per 256 entries instead of a
     // chain of dependent loads.
-    auto count_below = [&](const int32_t *a, int32_t cnt, int32_t &c_lo, int32_t &c_hi) {
+    auto count_below = [&](const int32_t *a, int32_t cnt, int32_t lo, int32_t hi, int32_t &c_lo,
+                           int32_t &c_hi) {
         int32_t n_lo = 0, n_hi = 0;
         for (int32_t b0 = 0; b0 < cnt; b0 += 256) {
             int32_t v[4];
@@ -316,16 +322,33 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                n_lo += __popcll(__ballot(v[u] < t_lo));
-                n_hi += __popcll(__ballot(v[u] < t_hi));
+                n_lo += __popcll(__ballot(v[u] < lo));
+                n_hi += __popcll(__ballot(v[u] < hi));
             }
         }
         c_lo = n_lo;
         c_hi = n_hi;
     };
     const int32_t cnt_p = p.rev_p_cnt[bt];
+    const int64_t mstride = p.stride >> 5;
+    const uint32_t *mrow = p.mbits + (b * p.Sq) * mstride + (key0 >> 5);
+    const int shift = (int)(key0 & 16);
+    int32_t t_lo = (int32_t)(seg * p.seg_tiles);
+    int32_t t_hi = (int32_t)((seg + 1) * p.seg_tiles);
+    if (p.merge > 1) {
+        const int64_t s0 = seg - seg % p.merge;
+        const bool split = p.kv_split[(bg * ((p.nseg + p.merge - 1) / p.merge) + s0 / p.merge) * ngroups + kg] != 0;
+        if (!split) {
+            if (seg != s0) {
+                if (lane == 0) *flag = 0;
+                return;
+            }
+            t_lo = (int32_t)(s0 * p.seg_tiles);
+            t_hi = (int32_t)((s0 + p.merge) * p.seg_tiles);
+        }
+    }
     int32_t p_lo, p_hi;
-    count_below(idx_p, cnt_p, p_lo, p_hi);
+    count_below(idx_p, cnt_p, t_lo, t_hi, p_lo, p_hi);
     const int64_t nwin = 2 * (int64_t)(p_hi - p_lo);  // 64-row windows
     if (lane == 0) *flag = nwin > 0 ? 1 : 0;
     if (nwin == 0) return;
@@ -436,9 +459,6 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
     // reverse list of partial tiles, the upper 64 rows of a tile first): all items of a
     // segment sweep its rows at about the same rate, so the rows they read
     // stay in the caches.
-    const int64_t mstride = p.stride >> 5;
-    const uint32_t *mrow = p.mbits + (b * p.Sq) * mstride + (key0 >> 5);
-    const int shift = (int)(key0 & 16);
     const uint64_t above = (lane == 63) ? 0ull : (~0ull << (lane + 1));
     // The segment's tiles, read once: lane j holds entry p_lo + j (segments of
     // more than 64 tiles read the list in memory).
@@ -576,6 +596,59 @@ __device__ __forceinline__ void dkdv_item(const Problem &p, lds_char *slots, int
     }
 }
 
+// Whether each (batch and KV head, segment group, 16-key group) is split into
+// its segments: the rows of the group's partial tiles that select one of the
+// 16 keys, counted until the count passes kSplitHits. One wave per entry.
+__global__ __launch_bounds__(64) void k_dkdv_split(Problem p)
+{
+    const int lane = threadIdx.x;
+    const int64_t ngroups = p.stride >> 4;
+    const int64_t nmg = (p.nseg + p.merge - 1) / p.merge;
+    const int64_t item = blockIdx.x;
+    if (item >= p.B * p.Hkv * nmg * ngroups) return;
+    const int64_t kg = item % ngroups;
+    const int64_t mg = (item / ngroups) % nmg;
+    const int64_t bg = item / (ngroups * nmg);
+    const int64_t b = bg / p.Hkv;
+    const int64_t key0 = kg * 16;
+    uint8_t *out = p.kv_split + item;
+    if (key0 >= p.Skv) {
+        if (lane == 0) *out = 0;
+        return;
+    }
+    const int64_t bt = b * p.nKT + (key0 >> 7);
+    const int32_t *idx_p = p.rev_p_idx + bt * p.nQT;
+    const int32_t cnt = p.rev_p_cnt[bt];
+    const int32_t g_lo = (int32_t)(mg * p.merge * p.seg_tiles);
+    const int32_t g_hi = (int32_t)((mg + 1) * p.merge * p.seg_tiles);
+    int32_t e_lo = 0, e_hi = 0;
+    for (int32_t b0 = 0; b0 < cnt; b0 += 64) {
+        const int32_t x = b0 + lane;
+        const int32_t v = x < cnt ? idx_p[x] : INT32_MAX;
+        e_lo += __popcll(__ballot(v < g_lo));
+        e_hi += __popcll(__ballot(v < g_hi));
+    }
+    const int64_t mstride = p.stride >> 5;
+    const uint32_t *mrow = p.mbits + (b * p.Sq) * mstride + (key0 >> 5);
+    const int shift = (int)(key0 & 16);
+    int32_t hits = 0;
+    for (int32_t e0 = e_lo; e0 < e_hi && hits <= kSplitHits; e0 += 8) {
+        uint32_t m[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int32_t e = e0 + (u >> 1);
+            m[u] = 0u;
+            if (e < e_hi) {
+                const int64_t qi = (int64_t)idx_p[e] * kTile + 64 * (u & 1) + lane;
+                if (qi < p.Sq) m[u] = (mrow[qi * mstride] >> shift) & 0xffffu;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) hits += __popcll(__ballot(m[u] != 0u));
+    }
+    if (lane == 0) *out = hits > kSplitHits ? 1 : 0;
+}
+
 __global__ __launch_bounds__(64) void k_dkdv(Problem p)
 {
     __shared__ __attribute__((aligned(16))) char slots[kRingRows * kSlot];
@@ -656,6 +729,12 @@ hipError_t launch_dq(const Problem &p, hipStream_t s)
 
 hipError_t launch_dkdv(const Problem &p, hipStream_t s)
 {
+    if (p.merge > 1) {
+        const int64_t entries = p.B * p.Hkv * ((p.nseg + p.merge - 1) / p.merge) * (p.stride >> 4);
+        hipLaunchKernelGGL(k_dkdv_split, dim3((unsigned)entries), dim3(64), 0, s, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const int64_t items = p.nseg * p.B * p.Hkv * (p.stride >> 4);
     hipLaunchKernelGGL(k_dkdv, dim3((unsigned)items), dim3(64), 0, s, p);
     return hipGetLastError();

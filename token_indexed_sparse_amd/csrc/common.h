@@ -12,8 +12,13 @@ constexpr int kD = 256;     // head dimension (QSA page, "Support and execution"
 constexpr int kGroup = 12;  // query heads per KV head
 constexpr int kTile = 128;  // query and key tile edge of the membership table
 // dK/dV work segments: kSegTilesMin query tiles, doubled while the FP32
-// partial sums of all segments would exceed kPartialBudget bytes.
-constexpr int kSegTilesMin = 8;
+// partial sums of all segments would exceed kPartialBudget bytes. Segments
+// are grouped kMergeTiles tiles at a time: one work item takes a whole group
+// unless its rows hit the item's 16 keys more than kSplitHits times, and then
+// each segment of the group is an item of its own.
+constexpr int kSegTilesMin = 2;
+constexpr int kMergeTiles = 8;
+constexpr int kSplitHits = 256;
 constexpr int64_t kPartialBudget = int64_t(4) << 30;
 constexpr int kMaxSkvLog2 = 19;
 
@@ -67,9 +72,13 @@ struct Problem {
     // and per (B*Hkv, slot, 16-key group) whether a partial was written
     float *kv_part;
     uint8_t *kv_flag;
+    // per (B*Hkv, segment group, 16-key group): whether the group's segments
+    // are separate work items (see kMergeTiles)
+    uint8_t *kv_split;
     int64_t nseg;
     int64_t nslot;      // nseg + 1 partial-sum slots per (batch, KV head)
     int64_t seg_tiles;  // query tiles per segment
+    int64_t merge;      // segments per group (kMergeTiles / seg_tiles, at least 1)
     // Hand-off from the gathered to the dense dQ: unscaled FP32 sums
     // [B, Sq, Hq, 256] of the rows whose tile row has full tiles.
     float *dq_part;
