@@ -30,7 +30,7 @@ int64_t seg_tiles_for(const qsa_dims *d)
     int64_t seg = kSegTilesMin;
     for (;;) {
         const int64_t nseg = (nQT + seg - 1) / seg;
-        const int64_t bytes = d->B * d->Hkv * (nseg + 1) * stride * 2 * kD * 4;
+        const int64_t bytes = d->B * d->Hkv * (nseg + dense_parts(nQT)) * stride * 2 * kD * 4;
         if (bytes <= kPartialBudget || seg >= nQT) return seg;
         seg *= 2;
     }
@@ -131,11 +131,12 @@ Layout layout(const qsa_dims *d, unsigned parts)
     const int64_t nseg = (nQT + seg - 1) / seg;
     // The dK/dV partial sums and the dQ hand-over each have a region: the
     // backward runs its dQ passes beside the dK/dV passes.
-    const size_t kv_bytes = (size_t)(d->B * d->Hkv * (nseg + 1) * stride) * 2 * kD * 4;
+    const int64_t nslot = nseg + dense_parts(nQT);
+    const size_t kv_bytes = (size_t)(d->B * d->Hkv * nslot * stride) * 2 * kD * 4;
     const size_t dq_bytes = (size_t)(rows * d->Hq) * kD * 4;
     L.kv_part = take(parts & kBwd, kv_bytes);
     L.dq_part = take(parts & kBwd, dq_bytes);
-    L.kv_flag = take(parts & kBwd, (size_t)(d->B * d->Hkv * (nseg + 1) * (stride / 16)));
+    L.kv_flag = take(parts & kBwd, (size_t)(d->B * d->Hkv * nslot * (stride / 16)));
     const int64_t merge = seg < kMergeTiles ? kMergeTiles / seg : 1;
     L.kv_split = take(parts & kBwd, (size_t)(d->B * d->Hkv * ((nseg + merge - 1) / merge) * (stride / 16)));
     L.walk = take(parts & kWalk, 16 * 4);
@@ -235,7 +236,7 @@ void fill_common(Problem &p, const qsa_dims *d, const void *routes, float scale)
     p.stride = p.nKT * kTile;
     p.seg_tiles = seg_tiles_for(d);
     p.nseg = (p.nQT + p.seg_tiles - 1) / p.seg_tiles;
-    p.nslot = p.nseg + 1;
+    p.nslot = p.nseg + dense_parts(p.nQT);
     p.merge = p.seg_tiles < kMergeTiles ? kMergeTiles / p.seg_tiles : 1;
     p.scale = scale;
     p.routes = routes;

@@ -43,8 +43,8 @@
 //    high + low parts, so that sums over thousands of query heads keep
 //    FP32-level error.
 //  * k_dkdv_reduce: the FP32 partial sums of the segments and then of the
-//    dense full-tile pass are added in that fixed order (deterministic, no
-//    atomics) and written as bf16 dK, dV.
+//    dense full-tile pass's parts are added in that fixed order
+//    (deterministic, no atomics) and written as bf16 dK, dV.
 //    Splitting the long causal key columns into segments keeps every SIMD
 //    busy to the end: the first key groups are selected by almost every later
 //    row and would otherwise dominate the run time.

@@ -20,6 +20,13 @@ constexpr int kSegTilesMin = 2;
 constexpr int kMergeTiles = 8;
 constexpr int kSplitHits = 256;
 constexpr int64_t kPartialBudget = int64_t(4) << 30;
+// The dense dK/dV pass takes a key tile's full query tiles kDenseSplit at a
+// time, each run into a partial-sum slot of its own after the segments'.
+constexpr int kDenseSplit = 48;
+__host__ __device__ constexpr int64_t dense_parts(int64_t nQT)
+{
+    return (nQT + kDenseSplit - 1) / kDenseSplit;
+}
 constexpr int kMaxSkvLog2 = 19;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -67,8 +74,9 @@ struct Problem {
     // backward
     float *delta;
     uint16_t *dq, *dk, *dv;
-    // dK/dV partial sums: [B*Hkv][nseg + 1][stride][dK 256 | dV 256] FP32, one
-    // slot per query segment of the gathered pass plus one for the full tiles,
+    // dK/dV partial sums: [B*Hkv][nslot][stride][dK 256 | dV 256] FP32, one
+    // slot per query segment of the gathered pass, then one per part of the
+    // full tiles (dense_parts),
     // and per (B*Hkv, slot, 16-key group) whether a partial was written
     float *kv_part;
     uint8_t *kv_flag;
@@ -76,7 +84,7 @@ struct Problem {
     // are separate work items (see kMergeTiles)
     uint8_t *kv_split;
     int64_t nseg;
-    int64_t nslot;      // nseg + 1 partial-sum slots per (batch, KV head)
+    int64_t nslot;      // nseg + dense_parts(nQT) partial-sum slots per (batch, KV head)
     int64_t seg_tiles;  // query tiles per segment
     int64_t merge;      // segments per group (kMergeTiles / seg_tiles, at least 1)
     // Hand-off from the gathered to the dense dQ: unscaled FP32 sums
@@ -412,6 +420,18 @@ __device__ __forceinline__ void hold_after(uint4 &x)
     u32x4 v = __builtin_bit_cast(u32x4, x);
     asm volatile("" : "+v"(v));
     x = __builtin_bit_cast(uint4, v);
+}
+
+// The same dispatch, for work whose cost varies along the logical range (the
+// full tiles of causal documents grow towards each document's end): groups of
+// `unit` consecutive logical blocks stay on one XCD (they share their operands
+// in its L2) and consecutive groups go to consecutive XCDs, so every XCD takes
+// its share of the heavy and the light parts. The grid must be a multiple of
+// 8 * unit blocks; the logical blocks past the work are to be skipped.
+__device__ __forceinline__ int64_t xcd_group_block(int64_t b, int64_t unit)
+{
+    const int64_t x = b & 7, y = b >> 3;
+    return ((y / unit) * 8 + x) * unit + (y % unit);
 }
 
 __device__ __forceinline__ int64_t xcd_logical_block(int64_t b, int64_t n)
