@@ -446,10 +446,10 @@ __global__ __launch_bounds__(256) void k_partial_keys(Problem p)
 }
 
 
-// A row's ascending key list and count from its bit-packed membership, -1
-// tail to the row width W; with skip_full, without the keys of the full
-// tiles of the row's tile row (the partial-tile list of the gathered
-// passes), else all keys. One wave per row: lane l takes words l, l + 64,
+// A row's ascending key list and count from its bit-packed membership; with
+// skip_full, without the keys of the full tiles of the row's tile row (the
+// partial-tile list of the gathered passes, valid up to its count), else all
+// keys with a -1 tail to the row width W. One wave per row: lane l takes words l, l + 64,
 // ... four blocks of 64 words at a time (their loads in flight together);
 // a word's keys go to positions from a wave prefix sum of the popcounts.
 __global__ __launch_bounds__(256) void k_row_lists(Problem p, int32_t *out_keys,
@@ -511,7 +511,12 @@ __global__ __launch_bounds__(256) void k_row_lists(Problem p, int32_t *out_keys,
             base += __shfl(inc, 63);
         }
     }
-    for (int64_t s2 = base + lane; s2 < p.W; s2 += 64) out[s2] = -1;
+    // The full lists (for inspection) end in -1 up to W; the readers of the
+    // partial-tile lists stop at the count, so those get no tail (a
+    // document-causal plan of 32768 tokens has W = 32768: its tails were
+    // 4.3 GB of stores).
+    if (!skip_full)
+        for (int64_t s2 = base + lane; s2 < p.W; s2 += 64) out[s2] = -1;
     if (lane == 0) out_cnt[row] = base;
 }
 
