@@ -717,19 +717,20 @@ __device__ __forceinline__ void dkdv_dense_item(const Problem &p, lds_char *buf)
         for (int x = 0; x < 2; ++x) {
             f32x4 sa = {0.f, 0.f, 0.f, 0.f}, pd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {  // four column steps at a time
-                uint4 qa[4], ga[4];
+            for (int hh = 0; hh < 4; ++hh) {  // two column steps at a time
+                uint4 qa[2], ga[2];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int t8 = 4 * hh + u;
+                for (int u = 0; u < 2; ++u) {
+                    const int t8 = 2 * hh + u;
                     const int o = col * 1024 + 512 * x + (((4 * t8 + quad) ^ amask) << 4);
                     qa[u] = lds_read16(qs + o);
                     ga[u] = lds_read16(gs + o);
                 }
+                __builtin_amdgcn_sched_barrier(0);  // the step's four reads in flight
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    sa = mfma_16x16x32(as_bf16x8(qa[u]), kf[4 * hh + u], sa);
-                    pd = mfma_16x16x32(as_bf16x8(ga[u]), vf[4 * hh + u], pd);
+                for (int u = 0; u < 2; ++u) {
+                    sa = mfma_16x16x32(as_bf16x8(qa[u]), kf[2 * hh + u], sa);
+                    pd = mfma_16x16x32(as_bf16x8(ga[u]), vf[2 * hh + u], pd);
                 }
             }
             const f32x4 ls = *reinterpret_cast<const lds_f32x4 *>(qs + kKvStats + (16 * x + 4 * quad) * 4);
