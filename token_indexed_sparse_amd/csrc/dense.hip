@@ -495,16 +495,18 @@ __device__ __forceinline__ void dq_dense_item(const Problem &p, lds_char *buf)
                 kt[1][j] = lds_read_tr(ks + o + 512);
             }
             __builtin_amdgcn_sched_barrier(0);  // all sixteen reads in flight
+            // the high parts of the half's eight column blocks, then the low
+            // parts: no product waits on the one just before it
+#pragma unroll
+            for (int lo = 0; lo < 2; ++lo)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int db = 8 * h + j;
                 const bf16x8 ka =
                     as_bf16x8(make_uint4(kt[0][j].x, kt[0][j].y, kt[1][j].x, kt[1][j].y));
 #pragma unroll
-                for (int x = 0; x < kVecBlocks; ++x) {
-                    acc[x][db] = mfma_16x16x32(ka, ds_hi[x], acc[x][db]);
-                    acc[x][db] = mfma_16x16x32(ka, ds_lo[x], acc[x][db]);
-                }
+                for (int x = 0; x < kVecBlocks; ++x)
+                    acc[x][db] = mfma_16x16x32(ka, lo ? ds_lo[x] : ds_hi[x], acc[x][db]);
             }
         }
     };
@@ -713,33 +715,35 @@ __device__ __forceinline__ void dkdv_dense_item(const Problem &p, lds_char *buf)
         const lds_char *gs = qs + kHalf;
         typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
         float pn[2][4], dn[2][4];
+        // The two 16-vector blocks side by side: four independent product
+        // chains per column step, the step's four reads in flight.
+        f32x4 sa[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4 pd[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8) {
+            uint4 qa[2], ga[2];
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int o = col * 1024 + 512 * x + (((4 * t8 + quad) ^ amask) << 4);
+                qa[x] = lds_read16(qs + o);
+                ga[x] = lds_read16(gs + o);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                sa[x] = mfma_16x16x32(as_bf16x8(qa[x]), kf[t8], sa[x]);
+                pd[x] = mfma_16x16x32(as_bf16x8(ga[x]), vf[t8], pd[x]);
+            }
+        }
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-            f32x4 sa = {0.f, 0.f, 0.f, 0.f}, pd = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int hh = 0; hh < 4; ++hh) {  // two column steps at a time
-                uint4 qa[2], ga[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int t8 = 2 * hh + u;
-                    const int o = col * 1024 + 512 * x + (((4 * t8 + quad) ^ amask) << 4);
-                    qa[u] = lds_read16(qs + o);
-                    ga[u] = lds_read16(gs + o);
-                }
-                __builtin_amdgcn_sched_barrier(0);  // the step's four reads in flight
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    sa = mfma_16x16x32(as_bf16x8(qa[u]), kf[2 * hh + u], sa);
-                    pd = mfma_16x16x32(as_bf16x8(ga[u]), vf[2 * hh + u], pd);
-                }
-            }
             const f32x4 ls = *reinterpret_cast<const lds_f32x4 *>(qs + kKvStats + (16 * x + 4 * quad) * 4);
             const f32x4 dl = *reinterpret_cast<const lds_f32x4 *>(qs + kKvStats + 128 + (16 * x + 4 * quad) * 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float pr = __builtin_amdgcn_exp2f(sa[e] * c - ls[e] * 1.4426950408889634f);
+                const float pr = __builtin_amdgcn_exp2f(sa[x][e] * c - ls[e] * 1.4426950408889634f);
                 pn[x][e] = pr;
-                dn[x][e] = pr * (pd[e] - dl[e]);
+                dn[x][e] = pr * (pd[x][e] - dl[e]);
             }
         }
         uint32_t ph[4], pl[4], dh[4], dlo[4];
